@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the HiSparse path on one MI355X.
+
+One step = RESOLVE (hit detection, LRU replacement, metadata update, miss
+fetch over the host link) plus sparse MLA decode attention for every layer
+of every request, i.e. one ``hisparse_step`` call.  Default workload: 32
+requests x 131072-token context, 4 sparse layers sharing one top-2048
+selection, 128 heads, 4096 hot slots per (request, layer), 64-token tail
+page resident, seeded synthetic drift trace (retain 0.85).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, published
+ROW_BYTES = 1152
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def host_link_probe(torch, H, dev, nbytes=256 << 20, reps=5):
+    """Measured host->device bandwidth: DMA copy and zero-copy kernel read."""
+    stream = torch.cuda.current_stream(dev)
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    host.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(host, non_blocking=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(host, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    dma = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    out = {"dma_h2d_GBs": round(dma, 2)}
+    for coherent in (0, 1):
+        h, d = H.hisparse_host_alloc(nbytes, coherent)
+        try:
+            ctypes_fill(h, nbytes)
+            H.hisparse_stream_copy(dst.data_ptr(), d, nbytes, stream.cuda_stream)
+            e0.record(stream)
+            for _ in range(reps):
+                H.hisparse_stream_copy(dst.data_ptr(), d, nbytes, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            zc = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        finally:
+            H.hisparse_host_free(h)
+        out["zero_copy_read_GBs_" + ("coherent" if coherent else "noncoherent")] = round(zc, 2)
+    # device-to-device copy with the same kernel (HBM reference)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    H.hisparse_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream.cuda_stream)
+    e0.record(stream)
+    for _ in range(reps):
+        H.hisparse_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    out["d2d_copy_GBs"] = round(2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    return out
+
+
+def ctypes_fill(addr: int, nbytes: int) -> None:
+    import ctypes
+
+    ctypes.memset(addr, 1, nbytes)
+
+
+def cpu_baseline(w, trace, budget_s=20.0):
+    """The CPU oracle, untuned, on a bounded sample of the same workload."""
+    from oracle.step import OracleDecoder
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    reqs = [0, 1]
+    dec = OracleDecoder(w, requests=reqs)
+    t0 = time.time()
+    steps = 0
+    for t in range(trace.shape[0]):
+        dec.step(t, trace[t])
+        steps += 1
+        if time.time() - t0 > budget_s:
+            break
+    el = time.time() - t0
+    tokens = len(reqs) * steps
+    return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"requests {reqs} x all {w.num_layers} layers x steps 0..{steps - 1} "
+                      f"(resolve + fp64 attention), {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=14)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="r32_ctx128k_l4")
+    ap.add_argument("--host-coherent", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: every (request, layer) is independent and this build "
+              "measures one GPU's share; multi-GPU runs are not part of it.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from host_offloaded_kv_amd import hisparse as H
+    from tracegen import named_workload
+    from tracegen.populate import populate, queries
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    H.load()
+    dev = torch.device("cuda:0")
+    w = named_workload(args.workload)
+    n_steps = args.warmup + args.steps
+    L, R, K, Hh, B = w.num_layers, w.num_requests, w.top_k, w.num_heads, w.hot_slots
+
+    log(f"workload {w.name}: R={R} L={L} g={w.index_share} ctx={w.ctx_len[0]} H={Hh} K={K} B={B}")
+    t0 = time.time()
+    trace = w.trace(n_steps)
+    log(f"trace generated ({n_steps} steps) in {time.time() - t0:.1f}s")
+    cfg = w.config_dict()
+    cfg["host_coherent"] = args.host_coherent
+    t0 = time.time()
+    hs = H.HiSparse(cfg, dev)
+    log(f"pool created ({sum(w.ctx_len) * L * ROW_BYTES / 1e9:.2f} GB pinned) in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    populate(hs, w)
+    log(f"host pool filled and residency uploaded in {time.time() - t0:.1f}s")
+
+    d_steps = torch.arange(n_steps, dtype=torch.int32, device=dev)
+    d_topk = torch.from_numpy(trace).to(dev)  # [T][G][R][K]
+    q_all = np.stack([queries(w, t) for t in range(n_steps)])
+    d_q = torch.from_numpy(q_all.view(np.int16)).to(dev)  # [T][L][R][H][576]
+    d_rows = torch.empty((n_steps, L, R, K), dtype=torch.int32, device=dev)
+    d_counts = torch.empty((n_steps, L, R, 3), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, Hh, 512), dtype=torch.float32, device=dev)
+    d_lse = torch.empty((L, R, Hh), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize(dev)
+    log("inputs staged in HBM")
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        H.hisparse_step(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(), d_q[t].data_ptr(), w.scale,
+                        d_rows[t].data_ptr(), d_counts[t].data_ptr(), d_out.data_ptr(), d_lse.data_ptr(),
+                        stream.cuda_stream)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize(dev)
+    log(f"{args.warmup} warmup steps done")
+    H.hisparse_profile_enable(hs.pool, True)
+    H.hisparse_profile_read(hs.pool)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    wall0 = time.perf_counter()
+    for t in range(args.warmup, n_steps):
+        step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    prof = H.hisparse_profile_read(hs.pool)
+    H.hisparse_profile_enable(hs.pool, False)
+    flags = hs.check_errors()
+    if flags:
+        log(f"device error flags {flags:#x}")
+        return 1
+    log(f"timed {args.steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.1f} ms)")
+
+    counts = d_counts[args.warmup:].cpu().numpy().astype(np.int64)  # [K][L][R][3]
+    valid = counts.sum(axis=3)  # valid selections per (step, l, r)
+    misses = counts[..., 2]
+    ms_step = ms_total / args.steps
+    tokens_per_s = R * args.steps / (ms_total * 1e-3)
+
+    # algorithmic bytes per step
+    host_bytes = misses.sum(axis=(1, 2)) * ROW_BYTES  # per step
+    attn_bytes = (valid.sum(axis=(1, 2)) * ROW_BYTES
+                  + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4))
+    attn_flops = valid.sum(axis=(1, 2)) * 2 * Hh * (576 + 512)
+    meta_bytes = L * R * (2 * 3 * B * 4 + 2 * K * 4 + 12) + misses.sum(axis=(1, 2)) * 8
+    hbm_step_bytes = attn_bytes + host_bytes + meta_bytes  # hot-row writes counted once in host_bytes
+
+    groups = w.groups
+    launches_per_step = {"resolve_meta": groups, "fetch_rows": groups, "sparse_mla_decode": groups,
+                         "combine_splits": groups}
+    kern = {}
+    for name, (n, tot_ms) in prof.items():
+        avg_ms = tot_ms / n
+        per_launch_steps = args.steps * launches_per_step[name]
+        if name == "fetch_rows":
+            alg = host_bytes.sum() / per_launch_steps
+            bound, peak, unit = "host_link", PCIE_PEAK_GBS, "GB/s"
+        elif name == "sparse_mla_decode":
+            alg = attn_bytes.sum() / per_launch_steps
+            bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        elif name == "resolve_meta":
+            alg = meta_bytes.sum() / per_launch_steps
+            bound, peak, unit = "alu", None, "GB/s"
+        else:
+            alg = 2 * L * R * Hh * 514 * 4 / groups
+            bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        ach = alg / (avg_ms * 1e-3) / 1e9
+        kern[name] = {"launches": n, "avg_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg),
+                      "achieved": round(ach, 2), "bound": bound, "peak": peak, "unit": unit,
+                      "frac": round(ach / peak, 4) if peak else None,
+                      "share_of_step": round(tot_ms / ms_total, 4)}
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    d = kern[dom]
+    roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
+                "frac": d["frac"], "traffic": None, "kernel": dom, "avg_us": d["avg_us"]}
+
+    probe = None
+    if not args.no_probe:
+        log("host-link probe")
+        probe = host_link_probe(torch, H, dev)
+        log(f"host-link probe: {probe}")
+    measured_link = max(v for k, v in probe.items() if k != "d2d_copy_GBs") if probe else None
+    if "fetch_rows" in kern and measured_link:
+        kern["fetch_rows"]["frac_of_measured_link"] = round(kern["fetch_rows"]["achieved"] / measured_link, 4)
+
+    cpu = None
+    hs.close()
+    del hs
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        cpu = cpu_baseline(w, trace)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": "decode tokens/s (resolve + sparse MLA) at 128K ctx; achieved HBM & host GB/s",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": R, "ctx": int(w.ctx_len[0]), "layers": L,
+                   "index_share": w.index_share, "heads": Hh, "top_k": K, "hot_slots": B,
+                   "seed": w.seed, "host_coherent": args.host_coherent},
+        "roofline": roofline,
+        "kernels": kern,
+        "step": {"us": round(ms_step * 1e3, 2),
+                 "hbm_GBs": round(float(hbm_step_bytes.mean()) / (ms_step * 1e-3) / 1e9, 2),
+                 "host_GBs": round(float(host_bytes.mean()) / (ms_step * 1e-3) / 1e9, 2),
+                 "miss_rate": round(float(misses.sum() / max(valid.sum(), 1)), 4),
+                 "attn_gflop": round(float(attn_flops.mean()) / 1e9, 2)},
+        "host_link": probe,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

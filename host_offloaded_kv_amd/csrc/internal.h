@@ -1,0 +1,144 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "hisparse.h"
+
+namespace hs {
+
+constexpr int kLatent = 576;         // bf16 values per KV row
+constexpr int kVDim = 512;           // value width (the "nope" part)
+constexpr int kRowBytes = kLatent * 2;
+constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per row (72)
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxHotSlots = 8192;
+constexpr int kMaxHeads = 256;
+
+// Per-launch description of the fan-out copy of missed rows.
+struct FetchArgs {
+  const int32_t* miss_count;   // [n_pairs]
+  const int2* fetch;           // [n_pairs][K] (position, slot)
+  const uint64_t* host_rows;   // [L*R] device-visible address of pool rows of (l, r)
+  uint16_t* const* kv;         // [L] device pointers of the KV tensors (device array)
+  int32_t layer_begin;
+  int32_t n_pairs;             // n_layers * R
+  int32_t num_requests;
+  int32_t top_k;
+  int32_t hot_slots;
+  int64_t resident_rows;
+};
+
+struct ResolveArgs {
+  const int32_t* step;     // device scalar t
+  const int32_t* topk;     // [R][K]
+  int32_t* rows;           // [n_layers][R][K]
+  int32_t* counts;         // [n_layers][R][3]
+  int32_t* owner;          // [L][R][B]
+  int32_t* stamp;          // [L][R][B]
+  int32_t* lru;            // [L][R][B] slots in ascending (stamp, slot)
+  int32_t* last_t;         // [L][R]
+  int32_t* miss_count;     // [n_layers][R] (pair order of this call)
+  int2* fetch;             // [n_layers][R][K]
+  const int32_t* bt;       // concatenated block tables
+  const int32_t* bt_off;   // [R]
+  const int32_t* ctx;      // [R]
+  uint32_t* err;
+  int32_t layer_begin;
+  int32_t n_layers;
+  int32_t num_requests;
+  int32_t top_k;
+  int32_t hot_slots;
+  int32_t hash_bits;       // slot hash has 1 << hash_bits entries (>= 2B)
+  int32_t page_shift;
+  int64_t resident_rows;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;       // [n_layers][R][H][576]
+  const int32_t* rows;     // [n_layers][R][K]
+  uint16_t* const* kv;     // [L] device array of KV tensor pointers
+  float* out;              // [n_layers][R][H][512]
+  float* lse;              // [n_layers][R][H]
+  float* partial;          // [n_layers][R][splits][H][514] when splits > 1
+  uint32_t* err;
+  int32_t layer_begin;
+  int32_t n_layers;
+  int32_t num_requests;
+  int32_t num_heads;
+  int32_t top_k;
+  int32_t splits;
+  int64_t kv_rows;         // rows per KV tensor
+  float scale_log2;        // scale * log2(e)
+};
+
+// Workspace carving, computed identically for sizing and for creation.
+struct Layout {
+  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, host_rows, kv_ptrs, err,
+      partial, total;
+  int64_t bt_entries;
+  int32_t splits_max;      // largest split count any decode launch uses
+  int32_t layers_batched;  // layers decoded by one launch in hisparse_step
+};
+
+}  // namespace hs
+
+namespace hs {
+enum KernelId { kKMeta = 0, kKFetch = 1, kKDecode = 2, kKCombine = 3, kKCount = 4 };
+constexpr int kProfCap = 8192;
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  std::vector<int> kid;
+  int n = 0;
+  bool overflow = false;
+};
+}  // namespace hs
+
+struct hisparse_pool {
+  hisparse_config cfg;
+  hs::Profiler prof;
+  std::vector<int64_t> ctx;
+  std::vector<int32_t> n_pages;
+  int device = 0;
+  hs::Layout lay;
+  char* ws = nullptr;
+  std::vector<void*> host_alloc;        // one pinned allocation per request
+  std::vector<uint16_t*> host_rows;     // [L*R] host addresses (index l*R + r)
+  std::vector<uint64_t> host_rows_dev;  // [L*R] device-visible addresses
+  std::vector<uint16_t*> kv;            // [L]
+  int64_t kv_rows = 0;
+  int hash_bits = 0;
+  size_t resolve_lds = 0;
+  // device views into the workspace
+  int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d;
+  int2* fetch;
+  uint64_t* host_rows_d;
+  uint16_t** kv_d;
+  uint32_t* err;
+  float* partial;
+};
+
+namespace hs {
+void set_error(const std::string& msg);
+hisparse_status hip_fail(hipError_t e, const char* what);
+
+// profiling marks around a launch (no-ops unless enabled)
+void prof_begin(hisparse_pool* p, int kid, hipStream_t s);
+void prof_end(hisparse_pool* p, hipStream_t s);
+
+// resolve.hip
+size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits);
+hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s);
+hipError_t launch_resolve(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);
+hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& a, hipStream_t s);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// decode.hip
+int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
+hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s);
+}  // namespace hs

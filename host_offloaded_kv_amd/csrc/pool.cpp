@@ -1,0 +1,608 @@
+// Host side of the C ABI: configuration checks, the pinned host pool,
+// workspace carving, block tables, and the enqueue entry points.
+//
+// The pool layout follows the HiSparse summary article (section 02): the
+// authoritative full KV of every request and sparse layer sits in pinned
+// host DRAM, and the device keeps B slots per (request, layer).  Mixed
+// residency (vLLM Hybrid HiSparse blog, "工作原理") adds a per-request block
+// table whose resident entries are read in place and never evicted.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace hs {
+hipError_t set_resolve_lds_limit(size_t bytes);
+
+namespace {
+thread_local std::string g_last_error;
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int ilog2_exact(int v) {
+  int b = 0;
+  while ((1 << b) < v) ++b;
+  return (1 << b) == v ? b : -1;
+}
+
+hisparse_status check_config(const hisparse_config* c) {
+  if (!c) {
+    set_error("config is NULL");
+    return HISPARSE_EINVAL;
+  }
+  if (c->num_requests < 1 || c->num_layers < 1 || c->index_share < 1 || c->num_layers % c->index_share) {
+    set_error("need num_requests >= 1, num_layers >= 1, index_share >= 1 and num_layers % index_share == 0");
+    return HISPARSE_EINVAL;
+  }
+  if (c->latent_dim != kLatent || c->v_dim != kVDim) {
+    set_error("latent_dim must be 576 and v_dim 512");
+    return HISPARSE_EINVAL;
+  }
+  if (c->top_k < 1 || c->top_k > kMaxTopK) {
+    set_error("top_k must be in [1, 4096]");
+    return HISPARSE_EINVAL;
+  }
+  if (c->hot_slots < c->top_k || c->hot_slots > kMaxHotSlots) {
+    set_error("hot_slots must satisfy top_k <= hot_slots <= 8192");
+    return HISPARSE_EINVAL;
+  }
+  if (c->page_size < 1 || ilog2_exact(c->page_size) < 0 || c->page_size > (1 << 20)) {
+    set_error("page_size must be a power of two");
+    return HISPARSE_EINVAL;
+  }
+  if (c->num_heads < 16 || c->num_heads % 16 || c->num_heads > kMaxHeads) {
+    set_error("num_heads must be a multiple of 16 in [16, 256]");
+    return HISPARSE_EINVAL;
+  }
+  if (c->resident_rows_per_layer < 0 || c->resident_rows_per_layer % c->page_size) {
+    set_error("resident_rows_per_layer must be a non-negative multiple of page_size");
+    return HISPARSE_EINVAL;
+  }
+  if (!c->ctx_len) {
+    set_error("ctx_len is NULL");
+    return HISPARSE_EINVAL;
+  }
+  for (int r = 0; r < c->num_requests; ++r) {
+    if (c->ctx_len[r] < 1 || c->ctx_len[r] > (int64_t{1} << 30)) {
+      set_error("ctx_len[" + std::to_string(r) + "] must be in [1, 2^30]");
+      return HISPARSE_EINVAL;
+    }
+  }
+  const int64_t rows = c->resident_rows_per_layer + (int64_t)c->num_requests * c->hot_slots;
+  if (rows >= (int64_t{1} << 31)) {
+    set_error("KV tensor rows per layer must stay below 2^31");
+    return HISPARSE_EINVAL;
+  }
+  if ((int64_t)c->num_layers * c->num_requests > 8192) {
+    set_error("num_layers * num_requests must be <= 8192");
+    return HISPARSE_EINVAL;
+  }
+  return HISPARSE_OK;
+}
+
+Layout make_layout(const hisparse_config* c) {
+  Layout L{};
+  const size_t R = c->num_requests, NL = c->num_layers, B = c->hot_slots, K = c->top_k;
+  int64_t bt_entries = 0;
+  for (size_t r = 0; r < R; ++r) bt_entries += (c->ctx_len[r] + c->page_size - 1) / c->page_size;
+  L.bt_entries = bt_entries;
+  L.layers_batched = c->index_share;
+  const int s1 = decode_splits(1, c->num_requests, c->num_heads, c->top_k);
+  const int sg = decode_splits(c->index_share, c->num_requests, c->num_heads, c->top_k);
+  L.splits_max = s1 > sg ? s1 : sg;
+  size_t part_1 = s1 > 1 ? (size_t)s1 * R * c->num_heads * (kVDim + 2) : 0;
+  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * c->num_heads * (kVDim + 2) : 0;
+  size_t off = 0;
+  L.owner = off; off = align256(off + NL * R * B * 4);
+  L.stamp = off; off = align256(off + NL * R * B * 4);
+  L.lru = off; off = align256(off + NL * R * B * 4);
+  L.last_t = off; off = align256(off + NL * R * 4);
+  L.miss_count = off; off = align256(off + NL * R * 4);
+  L.fetch = off; off = align256(off + NL * R * K * 8);
+  L.bt = off; off = align256(off + (size_t)bt_entries * 4);
+  L.bt_off = off; off = align256(off + R * 4);
+  L.ctx = off; off = align256(off + R * 4);
+  L.host_rows = off; off = align256(off + NL * R * 8);
+  L.kv_ptrs = off; off = align256(off + NL * 8);
+  L.err = off; off = align256(off + 4);
+  L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
+  L.total = off;
+  return L;
+}
+
+hisparse_status check_ptr(const void* p, size_t align, const char* what) {
+  if (!p) {
+    set_error(std::string(what) + " is NULL");
+    return HISPARSE_EINVAL;
+  }
+  if ((uintptr_t)p % align) {
+    set_error(std::string(what) + " is not " + std::to_string(align) + "-byte aligned");
+    return HISPARSE_EINVAL;
+  }
+  return HISPARSE_OK;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+hisparse_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return HISPARSE_EHIP;
+}
+
+void prof_begin(hisparse_pool* p, int kid, hipStream_t s) {
+  Profiler& pr = p->prof;
+  if (!pr.on) return;
+  if (pr.n >= kProfCap) {
+    pr.overflow = true;
+    return;
+  }
+  pr.kid[pr.n] = kid;
+  (void)hipEventRecord(pr.ev[2 * pr.n], s);
+}
+
+void prof_end(hisparse_pool* p, hipStream_t s) {
+  Profiler& pr = p->prof;
+  if (!pr.on || pr.n >= kProfCap) return;
+  (void)hipEventRecord(pr.ev[2 * pr.n + 1], s);
+  ++pr.n;
+}
+
+}  // namespace hs
+
+using namespace hs;
+
+extern "C" {
+
+const char* hisparse_last_error(void) { return g_last_error.c_str(); }
+
+hisparse_status hisparse_workspace_bytes(const hisparse_config* cfg, size_t* bytes) {
+  hisparse_status st = check_config(cfg);
+  if (st) return st;
+  if (!bytes) {
+    set_error("bytes is NULL");
+    return HISPARSE_EINVAL;
+  }
+  *bytes = make_layout(cfg).total;
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_kv_rows_per_layer(const hisparse_config* cfg, int64_t* rows) {
+  hisparse_status st = check_config(cfg);
+  if (st) return st;
+  if (!rows) {
+    set_error("rows is NULL");
+    return HISPARSE_EINVAL;
+  }
+  *rows = cfg->resident_rows_per_layer + (int64_t)cfg->num_requests * cfg->hot_slots;
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspace, size_t ws_bytes,
+                                     void* const* d_kv, void* stream, hisparse_pool** out) {
+  hisparse_status st = check_config(cfg);
+  if (st) return st;
+  if (!out) {
+    set_error("out is NULL");
+    return HISPARSE_EINVAL;
+  }
+  *out = nullptr;
+  if ((st = check_ptr(d_workspace, 256, "d_workspace"))) return st;
+  if (!d_kv) {
+    set_error("d_kv is NULL");
+    return HISPARSE_EINVAL;
+  }
+  for (int l = 0; l < cfg->num_layers; ++l)
+    if ((st = check_ptr(d_kv[l], 16, "d_kv[l]"))) return st;
+  const Layout lay = make_layout(cfg);
+  if (ws_bytes < lay.total) {
+    set_error("workspace too small: need " + std::to_string(lay.total) + " bytes");
+    return HISPARSE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+
+  hisparse_pool* p = new (std::nothrow) hisparse_pool();
+  if (!p) {
+    set_error("out of host memory");
+    return HISPARSE_ENOMEM;
+  }
+  p->cfg = *cfg;
+  const int R = cfg->num_requests, NL = cfg->num_layers;
+  p->ctx.assign(cfg->ctx_len, cfg->ctx_len + R);
+  p->cfg.ctx_len = p->ctx.data();
+  p->lay = lay;
+  p->ws = (char*)d_workspace;
+  p->kv.resize(NL);
+  for (int l = 0; l < NL; ++l) p->kv[l] = (uint16_t*)d_kv[l];
+  p->kv_rows = cfg->resident_rows_per_layer + (int64_t)R * cfg->hot_slots;
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  int hb = 1;
+  while ((1 << hb) < 2 * cfg->hot_slots) ++hb;
+  p->hash_bits = hb;
+  p->resolve_lds = resolve_lds_bytes(cfg->top_k, cfg->hot_slots, hb);
+  int max_lds = 0;
+  e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  if ((size_t)max_lds < p->resolve_lds) {
+    set_error("resolve needs " + std::to_string(p->resolve_lds) + " bytes of LDS, device allows " +
+              std::to_string(max_lds));
+    delete p;
+    return HISPARSE_EDEVICE;
+  }
+  if (p->resolve_lds > 65536) {
+    e = set_resolve_lds_limit(p->resolve_lds);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "hipFuncSetAttribute(resolve LDS)");
+    }
+  }
+
+  // Pinned, device-mapped host pool: one allocation per request holding
+  // its L layers back to back.
+  const unsigned flags = hipHostMallocMapped | (cfg->host_coherent ? hipHostMallocCoherent : hipHostMallocNonCoherent);
+  p->host_alloc.assign(R, nullptr);
+  p->host_rows.assign((size_t)NL * R, nullptr);
+  p->host_rows_dev.assign((size_t)NL * R, 0);
+  for (int r = 0; r < R; ++r) {
+    const size_t per_layer = (size_t)p->ctx[r] * kRowBytes;
+    void* h = nullptr;
+    e = hipHostMalloc(&h, per_layer * NL, flags);
+    if (e != hipSuccess || !h) {
+      (void)hipGetLastError();
+      set_error("hipHostMalloc of " + std::to_string(per_layer * NL) + " bytes failed for request " +
+                std::to_string(r));
+      hisparse_destroy_pool(p);
+      return HISPARSE_ENOMEM;
+    }
+    p->host_alloc[r] = h;
+    void* dptr = nullptr;
+    e = hipHostGetDevicePointer(&dptr, h, 0);
+    if (e != hipSuccess) {
+      hisparse_destroy_pool(p);
+      return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    for (int l = 0; l < NL; ++l) {
+      p->host_rows[(size_t)l * R + r] = (uint16_t*)((char*)h + per_layer * l);
+      p->host_rows_dev[(size_t)l * R + r] = (uint64_t)((char*)dptr + per_layer * l);
+    }
+  }
+
+  // Carve the workspace.
+  char* w = p->ws;
+  p->owner = (int32_t*)(w + lay.owner);
+  p->stamp = (int32_t*)(w + lay.stamp);
+  p->lru = (int32_t*)(w + lay.lru);
+  p->last_t = (int32_t*)(w + lay.last_t);
+  p->miss_count = (int32_t*)(w + lay.miss_count);
+  p->fetch = (int2*)(w + lay.fetch);
+  p->bt = (int32_t*)(w + lay.bt);
+  p->bt_off = (int32_t*)(w + lay.bt_off);
+  p->ctx_d = (int32_t*)(w + lay.ctx);
+  p->host_rows_d = (uint64_t*)(w + lay.host_rows);
+  p->kv_d = (uint16_t**)(w + lay.kv_ptrs);
+  p->err = (uint32_t*)(w + lay.err);
+  p->partial = (float*)(w + lay.partial);
+
+  std::vector<int32_t> bt_off(R), ctx32(R);
+  p->n_pages.resize(R);
+  int64_t acc = 0;
+  for (int r = 0; r < R; ++r) {
+    bt_off[r] = (int32_t)acc;
+    p->n_pages[r] = (int32_t)((p->ctx[r] + cfg->page_size - 1) / cfg->page_size);
+    acc += p->n_pages[r];
+    ctx32[r] = (int32_t)p->ctx[r];
+  }
+  std::vector<uint64_t> kvp(NL);
+  for (int l = 0; l < NL; ++l) kvp[l] = (uint64_t)p->kv[l];
+  if ((e = hipMemcpyAsync(p->bt_off, bt_off.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(p->ctx_d, ctx32.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(p->host_rows_d, p->host_rows_dev.data(), (size_t)NL * R * 8, hipMemcpyHostToDevice, s)) !=
+          hipSuccess ||
+      (e = hipMemcpyAsync(p->kv_d, kvp.data(), (size_t)NL * 8, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = launch_workspace_init(p, s)) != hipSuccess || (e = hipStreamSynchronize(s)) != hipSuccess) {
+    hisparse_destroy_pool(p);
+    return hip_fail(e, "workspace initialisation");
+  }
+  *out = p;
+  return HISPARSE_OK;
+}
+
+void hisparse_destroy_pool(hisparse_pool* p) {
+  if (!p) return;
+  (void)hipDeviceSynchronize();
+  for (hipEvent_t e : p->prof.ev) (void)hipEventDestroy(e);
+  for (void* h : p->host_alloc)
+    if (h) (void)hipHostFree(h);
+  delete p;
+}
+
+uint16_t* hisparse_host_rows(hisparse_pool* p, int32_t r, int32_t l) {
+  if (!p || r < 0 || r >= p->cfg.num_requests || l < 0 || l >= p->cfg.num_layers) {
+    set_error("hisparse_host_rows: bad argument");
+    return nullptr;
+  }
+  return p->host_rows[(size_t)l * p->cfg.num_requests + r];
+}
+
+hisparse_status hisparse_set_block_table(hisparse_pool* p, int32_t r, const int32_t* host_bt, int32_t n_pages,
+                                         void* stream) {
+  if (!p || !host_bt || r < 0 || r >= p->cfg.num_requests) {
+    set_error("hisparse_set_block_table: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  if (n_pages != p->n_pages[r]) {
+    set_error("hisparse_set_block_table: n_pages must be ceil(ctx_r / page_size) = " +
+              std::to_string(p->n_pages[r]));
+    return HISPARSE_EINVAL;
+  }
+  const int64_t nblocks = p->cfg.resident_rows_per_layer / p->cfg.page_size;
+  for (int i = 0; i < n_pages; ++i) {
+    if (host_bt[i] < -1 || host_bt[i] >= nblocks) {
+      set_error("hisparse_set_block_table: block id out of range at page " + std::to_string(i));
+      return HISPARSE_EINVAL;
+    }
+  }
+  int32_t off = 0;
+  for (int i = 0; i < r; ++i) off += p->n_pages[i];
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(p->bt + off, host_bt, (size_t)n_pages * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_set_block_table");
+}
+
+namespace {
+hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const int32_t* d_step,
+                                const int32_t* d_topk, int32_t* d_rows, int32_t* d_counts, hipStream_t s) {
+  ResolveArgs a;
+  a.step = d_step;
+  a.topk = d_topk;
+  a.rows = d_rows;
+  a.counts = d_counts;
+  a.owner = p->owner;
+  a.stamp = p->stamp;
+  a.lru = p->lru;
+  a.last_t = p->last_t;
+  a.miss_count = p->miss_count + (size_t)layer_begin * p->cfg.num_requests;
+  a.fetch = p->fetch + (size_t)layer_begin * p->cfg.num_requests * p->cfg.top_k;
+  a.bt = p->bt;
+  a.bt_off = p->bt_off;
+  a.ctx = p->ctx_d;
+  a.err = p->err;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.num_requests = p->cfg.num_requests;
+  a.top_k = p->cfg.top_k;
+  a.hot_slots = p->cfg.hot_slots;
+  a.hash_bits = p->hash_bits;
+  int ps = 0;
+  while ((1 << ps) < p->cfg.page_size) ++ps;
+  a.page_shift = ps;
+  a.resident_rows = p->cfg.resident_rows_per_layer;
+  hipError_t e = launch_resolve(p, a, s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "resolve launch");
+}
+
+hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const uint16_t* d_q,
+                               const int32_t* d_rows, float scale, float* d_out, float* d_lse, hipStream_t s) {
+  DecodeArgs a;
+  a.q = d_q;
+  a.rows = d_rows;
+  a.kv = p->kv_d;
+  a.out = d_out;
+  a.lse = d_lse;
+  a.partial = p->partial;
+  a.err = p->err;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.num_requests = p->cfg.num_requests;
+  a.num_heads = p->cfg.num_heads;
+  a.top_k = p->cfg.top_k;
+  a.splits = decode_splits(n_layers, p->cfg.num_requests, p->cfg.num_heads, p->cfg.top_k);
+  a.kv_rows = p->kv_rows;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = launch_decode(p, a, s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "decode launch");
+}
+}  // namespace
+
+hisparse_status hisparse_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const int32_t* d_step,
+                                 const int32_t* d_topk, int32_t* d_rows, int32_t* d_counts, void* stream) {
+  if (!p || !d_step || !d_topk || !d_rows || !d_counts) {
+    set_error("hisparse_resolve: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  const int g = p->cfg.index_share;
+  if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > p->cfg.num_layers ||
+      layer_begin / g != (layer_begin + n_layers - 1) / g) {
+    set_error("hisparse_resolve: layers must lie inside one index-share group");
+    return HISPARSE_EINVAL;
+  }
+  return enqueue_resolve(p, layer_begin, n_layers, d_step, d_topk, d_rows, d_counts, (hipStream_t)stream);
+}
+
+hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, const uint16_t* d_q,
+                                           const int32_t* d_rows, float scale, float* d_out, float* d_lse,
+                                           void* stream) {
+  if (!p || !d_q || !d_rows || !d_out || !d_lse) {
+    set_error("hisparse_sparse_mla_decode: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  if (layer < 0 || layer >= p->cfg.num_layers) {
+    set_error("hisparse_sparse_mla_decode: layer out of range");
+    return HISPARSE_EINVAL;
+  }
+  if ((uintptr_t)d_q % 16) {
+    set_error("hisparse_sparse_mla_decode: d_q must be 16-byte aligned");
+    return HISPARSE_EINVAL;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("hisparse_sparse_mla_decode: scale must be finite");
+    return HISPARSE_EINVAL;
+  }
+  return enqueue_decode(p, layer, 1, d_q, d_rows, scale, d_out, d_lse, (hipStream_t)stream);
+}
+
+hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,
+                              float scale, int32_t* d_rows, int32_t* d_counts, float* d_out, float* d_lse,
+                              void* stream) {
+  if (!p || !d_step || !d_topk || !d_q || !d_rows || !d_counts || !d_out || !d_lse) {
+    set_error("hisparse_step: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  if ((uintptr_t)d_q % 16 || !std::isfinite(scale)) {
+    set_error("hisparse_step: d_q must be 16-byte aligned and scale finite");
+    return HISPARSE_EINVAL;
+  }
+  const auto& c = p->cfg;
+  const size_t R = c.num_requests, K = c.top_k, H = c.num_heads;
+  hipStream_t s = (hipStream_t)stream;
+  for (int g = 0; g < c.num_layers / c.index_share; ++g) {
+    const int l0 = g * c.index_share;
+    hisparse_status st = enqueue_resolve(p, l0, c.index_share, d_step, d_topk + (size_t)g * R * K,
+                                         d_rows + (size_t)l0 * R * K, d_counts + (size_t)l0 * R * 3, s);
+    if (st) return st;
+    st = enqueue_decode(p, l0, c.index_share, d_q + (size_t)l0 * R * H * kLatent, d_rows + (size_t)l0 * R * K, scale,
+                        d_out + (size_t)l0 * R * H * kVDim, d_lse + (size_t)l0 * R * H, s);
+    if (st) return st;
+  }
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_export_state(hisparse_pool* p, int32_t r, int32_t l, int32_t* host_owner,
+                                      int32_t* host_stamp, void* stream) {
+  if (!p || !host_owner || !host_stamp || r < 0 || r >= p->cfg.num_requests || l < 0 || l >= p->cfg.num_layers) {
+    set_error("hisparse_export_state: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  const size_t B = p->cfg.hot_slots;
+  const size_t pair = (size_t)l * p->cfg.num_requests + r;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(host_owner, p->owner + pair * B, B * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_stamp, p->stamp + pair * B, B * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_export_state");
+}
+
+hisparse_status hisparse_check_errors(hisparse_pool* p, void* stream, uint32_t* flags) {
+  if (!p || !flags) {
+    set_error("hisparse_check_errors: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, p->err, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemsetAsync(p->err, 0, 4, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hisparse_check_errors");
+  *flags = v;
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_profile_enable(hisparse_pool* p, int32_t enable) {
+  if (!p) {
+    set_error("hisparse_profile_enable: pool is NULL");
+    return HISPARSE_EINVAL;
+  }
+  Profiler& pr = p->prof;
+  if (enable && pr.ev.empty()) {
+    pr.ev.resize(2 * kProfCap);
+    pr.kid.resize(kProfCap);
+    for (auto& e : pr.ev) {
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    }
+  }
+  pr.on = enable != 0;
+  pr.n = 0;
+  pr.overflow = false;
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_profile_read(hisparse_pool* p, hisparse_kernel_time* out, int32_t max, int32_t* n) {
+  static const char* names[kKCount] = {"resolve_meta", "fetch_rows", "sparse_mla_decode", "combine_splits"};
+  if (!p || !out || !n || max < 0) {
+    set_error("hisparse_profile_read: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  Profiler& pr = p->prof;
+  double total[kKCount] = {0, 0, 0, 0};
+  int cnt[kKCount] = {0, 0, 0, 0};
+  for (int i = 0; i < pr.n; ++i) {
+    hipError_t e = hipEventSynchronize(pr.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.ev[2 * i], pr.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    total[pr.kid[i]] += ms;
+    cnt[pr.kid[i]] += 1;
+  }
+  const bool overflow = pr.overflow;
+  pr.n = 0;
+  pr.overflow = false;
+  int k = 0;
+  for (int i = 0; i < kKCount; ++i) {
+    if (!cnt[i]) continue;
+    if (k < max) out[k] = hisparse_kernel_time{names[i], cnt[i], total[i]};
+    ++k;
+  }
+  *n = k < max ? k : max;
+  if (overflow) {
+    set_error("hisparse_profile_read: more than 8192 launches since the last read; later ones were not timed");
+    return HISPARSE_ESTATE;
+  }
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_host_alloc(size_t bytes, int32_t coherent, void** host, void** dev) {
+  if (!host || !dev || bytes == 0) {
+    set_error("hisparse_host_alloc: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  const unsigned flags = hipHostMallocMapped | (coherent ? hipHostMallocCoherent : hipHostMallocNonCoherent);
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, flags);
+  if (e != hipSuccess || !h) {
+    (void)hipGetLastError();
+    set_error("hipHostMalloc failed");
+    return HISPARSE_ENOMEM;
+  }
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return hip_fail(e, "hipHostGetDevicePointer");
+  }
+  *host = h;
+  *dev = d;
+  return HISPARSE_OK;
+}
+
+void hisparse_host_free(void* host) {
+  if (host) (void)hipHostFree(host);
+}
+
+hisparse_status hisparse_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16 || (uintptr_t)dst % 16 || (uintptr_t)src % 16) {
+    set_error("hisparse_stream_copy: pointers and size must be 16-byte multiples");
+    return HISPARSE_EINVAL;
+  }
+  if (bytes == 0) return HISPARSE_OK;
+  hipError_t e = launch_stream_copy(dst, src, bytes, (hipStream_t)stream);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_stream_copy");
+}
+
+}  // extern "C"

@@ -1,0 +1,491 @@
+// RESOLVE for gfx950: hit detection, LRU replacement, metadata update and
+// the host fetch of every miss.
+//
+// The operation follows the HiSparse summary article ("显存占用直降30倍！…
+// HiSparse夯爆了", section 02: a fused RESOLVE per sparse layer over a B-slot
+// device buffer with a position->slot page table and LRU metadata, rows
+// fetched from pinned host memory on a miss) and the vLLM Hybrid HiSparse
+// blog (section "工作原理": resident tokens read in place, hot tokens read
+// with their LRU entry refreshed, a miss copies a single row into an LRU
+// slot, nothing on the decode path waits for the CPU).
+//
+// Design on CDNA4:
+//  * resolve_meta: one 64-lane wavefront per (request, layer).  The slot
+//    owner, stamp and LRU-order arrays and the position->slot page table (an
+//    open-addressing hash rebuilt from the owner array on every call) live
+//    in LDS.  Misses are compacted with wavefront ballots in ascending
+//    position order; victims are the first unpinned slots of a persistent
+//    array that lists all slots in ascending (stamp, slot) order, so victim
+//    choice is a single ballot scan with no sort.  After the fills the order
+//    array is rebuilt as [untouched slots with stamp < t, in old order] ++
+//    [slots with stamp == t, by slot index], which keeps it sorted.
+//  * fetch_rows: a fan-out copy over the whole GPU.  Each workgroup scans
+//    the per-(request, layer) miss counts in LDS, then the grid walks a flat
+//    index of 16-byte chunks over every missed row (72 chunks per 1152-byte
+//    row), so a wavefront's loads cover 1 KiB of contiguous host memory.
+//    Loads are zero-copy reads of the pinned, device-mapped pool over the
+//    host link.
+#include "internal.h"
+
+#include <climits>
+
+namespace hs {
+namespace {
+
+__device__ __forceinline__ uint32_t hash_pos(int32_t p, int bits) {
+  return ((uint32_t)p * 0x9E3779B1u) >> (32 - bits);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+int ceil_log2(int64_t v) {
+  int b = 0;
+  while ((int64_t{1} << b) < v) ++b;
+  return b;
+}
+
+struct LdsMap {
+  size_t owner, stamp, lru, sel, mpos, mj, vic, flag, region, total;
+  int seen_bits;
+};
+
+__host__ __device__ inline LdsMap lds_map(int K, int B, int hash_bits, int seen_bits) {
+  LdsMap m;
+  m.owner = 0;
+  m.stamp = m.owner + 4 * (size_t)B;
+  m.lru = m.stamp + 4 * (size_t)B;
+  m.sel = m.lru + 4 * (size_t)B;
+  m.mpos = m.sel + 4 * (size_t)K;
+  m.mj = m.mpos + 4 * (size_t)K;
+  m.vic = m.mj + 4 * (size_t)K;
+  m.flag = m.vic + 4 * (size_t)K;
+  m.region = (m.flag + (size_t)B + 15) & ~(size_t)15;
+  size_t hash_bytes = (size_t)4 << hash_bits;
+  size_t seen_bytes = (size_t)8 << seen_bits;  // also holds the miss sort (<= K entries)
+  m.total = m.region + (hash_bytes > seen_bytes ? hash_bytes : seen_bytes);
+  m.seen_bits = seen_bits;
+  return m;
+}
+
+__global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
+  const LdsMap M = lds_map(K, B, a.hash_bits, seen_bits);
+  int32_t* owner_s = (int32_t*)(smem + M.owner);
+  int32_t* stamp_s = (int32_t*)(smem + M.stamp);
+  int32_t* lru_s = (int32_t*)(smem + M.lru);
+  int32_t* sel_s = (int32_t*)(smem + M.sel);
+  int32_t* mpos_s = (int32_t*)(smem + M.mpos);
+  int32_t* mj_s = (int32_t*)(smem + M.mj);
+  int32_t* vic_s = (int32_t*)(smem + M.vic);
+  unsigned char* flag_s = smem + M.flag;
+  int32_t* hash_s = (int32_t*)(smem + M.region);
+  unsigned long long* kv64_s = (unsigned long long*)(smem + M.region);
+
+  const int lane = threadIdx.x;
+  const uint64_t lt = lanemask_lt();
+  const int li = blockIdx.x / R;
+  const int r = blockIdx.x - li * R;
+  const int l = a.layer_begin + li;
+  const size_t pair = (size_t)l * R + r;    // state index
+  const size_t cpair = (size_t)li * R + r;  // output index of this call
+  int32_t* rows_out = a.rows + cpair * K;
+  const int32_t* topk = a.topk + (size_t)r * K;
+  const int t = *a.step;
+  const int ctx = a.ctx[r];
+  const int64_t hot_base = a.resident_rows + (int64_t)r * B;
+  const int page_shift = a.page_shift;
+  const int page_mask = (1 << page_shift) - 1;
+
+  const int last = a.last_t[pair];
+  if (t < 0 || t < last) {
+    for (int j = lane; j < K; j += 64) rows_out[j] = -1;
+    if (lane == 0) {
+      a.counts[cpair * 3 + 0] = 0;
+      a.counts[cpair * 3 + 1] = 0;
+      a.counts[cpair * 3 + 2] = 0;
+      a.miss_count[cpair] = 0;
+      atomicOr(a.err, HISPARSE_ERR_STEP);
+    }
+    return;
+  }
+  if (lane == 0) a.last_t[pair] = t;
+
+  int32_t* owner_g = a.owner + pair * B;
+  int32_t* stamp_g = a.stamp + pair * B;
+  int32_t* lru_g = a.lru + pair * B;
+  for (int s = lane; s < B; s += 64) {
+    owner_s[s] = owner_g[s];
+    stamp_s[s] = stamp_g[s];
+    lru_s[s] = lru_g[s];
+    flag_s[s] = 0;
+  }
+
+  // Selection: validate the range; note whether it is strictly ascending
+  // with padding only at the end (then it has no repeats and its misses
+  // come out already in ascending order).
+  uint32_t errbits = 0;
+  for (int j = lane; j < K; j += 64) {
+    int p = topk[j];
+    if (p < -1 || p >= ctx) {
+      errbits |= HISPARSE_ERR_RANGE;
+      p = -1;
+    }
+    sel_s[j] = p;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int j = lane; j + 1 < K; j += 64) {
+    const int a0 = sel_s[j], a1 = sel_s[j + 1];
+    const int k0 = a0 < 0 ? INT_MAX : a0, k1 = a1 < 0 ? INT_MAX : a1;
+    if (!(k0 < k1 || (k0 == INT_MAX && k1 == INT_MAX))) bad = true;
+  }
+  const bool fast = __ballot(bad) == 0ull;
+
+  if (!fast) {
+    // Repeated positions: keep the earliest entry (smallest j) of each.
+    const int ES = 1 << seen_bits;
+    for (int i = lane; i < ES; i += 64) kv64_s[i] = ~0ull;
+    __syncthreads();
+    for (int j = lane; j < K; j += 64) {
+      const int p = sel_s[j];
+      if (p < 0) continue;
+      const unsigned long long ent = ((unsigned long long)(uint32_t)p << 32) | (uint32_t)j;
+      uint32_t h = hash_pos(p, seen_bits);
+      while (true) {
+        const unsigned long long old = atomicCAS(&kv64_s[h], ~0ull, ent);
+        if (old == ~0ull) break;
+        if ((uint32_t)(old >> 32) == (uint32_t)p) {
+          atomicMin(&kv64_s[h], ent);
+          break;
+        }
+        h = (h + 1) & (ES - 1);
+      }
+    }
+    __syncthreads();
+    for (int j = lane; j < K; j += 64) {
+      const int p = sel_s[j];
+      if (p < 0) continue;
+      uint32_t h = hash_pos(p, seen_bits);
+      while ((uint32_t)(kv64_s[h] >> 32) != (uint32_t)p) h = (h + 1) & (ES - 1);
+      if ((uint32_t)kv64_s[h] != (uint32_t)j) {
+        sel_s[j] = -1;
+        errbits |= HISPARSE_ERR_DUP;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Page table: position -> slot, rebuilt from the owner array.
+  const int HS = 1 << a.hash_bits;
+  for (int i = lane; i < HS; i += 64) hash_s[i] = -1;
+  __syncthreads();
+  for (int s = lane; s < B; s += 64) {
+    const int p = owner_s[s];
+    if (p < 0) continue;
+    uint32_t h = hash_pos(p, a.hash_bits);
+    while (atomicCAS(&hash_s[h], -1, s) != -1) h = (h + 1) & (HS - 1);
+  }
+  __syncthreads();
+
+  // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
+  const int32_t* bt = a.bt + a.bt_off[r];
+  int n_res = 0, n_hit = 0, m = 0;
+  for (int j0 = 0; j0 < K; j0 += 64) {
+    const int j = j0 + lane;
+    bool miss = false;
+    int p = -1;
+    if (j < K) {
+      p = sel_s[j];
+      int row = -1;
+      if (p >= 0) {
+        const int blk = bt[p >> page_shift];
+        if (blk >= 0) {
+          row = (blk << page_shift) + (p & page_mask);
+          ++n_res;
+        } else {
+          uint32_t h = hash_pos(p, a.hash_bits);
+          int s;
+          while ((s = hash_s[h]) >= 0 && owner_s[s] != p) h = (h + 1) & (HS - 1);
+          if (s >= 0) {
+            stamp_s[s] = t;
+            flag_s[s] = 1;
+            row = (int)(hot_base + s);
+            ++n_hit;
+          } else {
+            miss = true;
+          }
+        }
+      }
+      if (!miss) rows_out[j] = row;
+    }
+    const uint64_t bm = __ballot(miss);
+    if (miss) {
+      const int idx = m + __popcll(bm & lt);
+      mpos_s[idx] = p;
+      mj_s[idx] = j;
+    }
+    m += __popcll(bm);
+  }
+  __syncthreads();
+
+  if (!fast && m > 1) {
+    // Ascending position order of the misses: bitonic sort of (pos, j).
+    int mp = 1;
+    while (mp < m) mp <<= 1;
+    for (int i = lane; i < mp; i += 64)
+      kv64_s[i] = i < m ? (((unsigned long long)(uint32_t)mpos_s[i] << 32) | (uint32_t)mj_s[i]) : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= mp; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = lane; i < mp; i += 64) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const unsigned long long x = kv64_s[i], y = kv64_s[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              kv64_s[i] = y;
+              kv64_s[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = lane; i < m; i += 64) {
+      mpos_s[i] = (int)(kv64_s[i] >> 32);
+      mj_s[i] = (int)(uint32_t)kv64_s[i];
+    }
+    __syncthreads();
+  }
+
+  // Victims: the first m unpinned slots in (stamp, slot) order.
+  int found = 0;
+  for (int i0 = 0; i0 < B && found < m; i0 += 64) {
+    const int i = i0 + lane;
+    const int s = i < B ? lru_s[i] : 0;
+    const bool cand = i < B && flag_s[s] == 0;
+    const uint64_t bm = __ballot(cand);
+    if (cand) {
+      const int rank = found + __popcll(bm & lt);
+      if (rank < m) vic_s[rank] = s;
+    }
+    found += __popcll(bm);
+  }
+  __syncthreads();
+
+  // Fill: i-th smallest missing position -> i-th victim.
+  int2* fetch = a.fetch + cpair * K;
+  for (int i = lane; i < m; i += 64) {
+    const int v = vic_s[i], p = mpos_s[i], j = mj_s[i];
+    owner_s[v] = p;
+    stamp_s[v] = t;
+    flag_s[v] = 1;
+    rows_out[j] = (int)(hot_base + v);
+    fetch[i] = make_int2(p, v);
+  }
+  __syncthreads();
+
+  // New order: untouched slots older than t (old order), then every slot
+  // stamped t, by slot index.
+  int nA = 0;
+  for (int i0 = 0; i0 < B; i0 += 64) {
+    const int i = i0 + lane;
+    const int s = i < B ? lru_s[i] : 0;
+    const bool keep = i < B && stamp_s[s] < t;
+    const uint64_t bm = __ballot(keep);
+    if (keep) lru_g[nA + __popcll(bm & lt)] = s;
+    nA += __popcll(bm);
+  }
+  int nB = 0;
+  for (int s0 = 0; s0 < B; s0 += 64) {
+    const int s = s0 + lane;
+    const bool inB = s < B && stamp_s[s] == t;
+    const uint64_t bm = __ballot(inB);
+    if (inB) lru_g[nA + nB + __popcll(bm & lt)] = s;
+    nB += __popcll(bm);
+  }
+  for (int s = lane; s < B; s += 64) {
+    owner_g[s] = owner_s[s];
+    stamp_g[s] = stamp_s[s];
+  }
+
+  n_res = wave_sum(n_res);
+  n_hit = wave_sum(n_hit);
+  if (errbits) atomicOr(a.err, errbits);
+  if (lane == 0) {
+    a.counts[cpair * 3 + 0] = n_res;
+    a.counts[cpair * 3 + 1] = n_hit;
+    a.counts[cpair * 3 + 2] = m;
+    a.miss_count[cpair] = m;
+  }
+}
+
+constexpr int kFetchThreads = 256;
+constexpr int kFetchUnroll = 4;
+constexpr int kFetchMaxPairs = 8192;
+
+__global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const int32_t* ctx) {
+  __shared__ int32_t pre_s[kFetchMaxPairs + 1];
+  __shared__ int32_t part_s[kFetchThreads];
+  const int n = a.n_pairs, tid = threadIdx.x;
+  const int per = (n + kFetchThreads - 1) / kFetchThreads;
+  int sum = 0;
+  for (int i = tid * per; i < n && i < (tid + 1) * per; ++i) sum += a.miss_count[i];
+  part_s[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < kFetchThreads; ++i) {
+      const int v = part_s[i];
+      part_s[i] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  int acc = part_s[tid];
+  for (int i = tid * per; i < n && i < (tid + 1) * per; ++i) {
+    pre_s[i] = acc;
+    acc += a.miss_count[i];
+  }
+  if (tid == kFetchThreads - 1) pre_s[n] = acc;
+  __syncthreads();
+  const int64_t total_chunks = (int64_t)pre_s[n] * kRowChunks;
+  const int R = a.num_requests;
+
+  for (int64_t base = (int64_t)blockIdx.x * kFetchThreads * kFetchUnroll; base < total_chunks;
+       base += (int64_t)gridDim.x * kFetchThreads * kFetchUnroll) {
+    u32x4 v[kFetchUnroll];
+    u32x4* dst[kFetchUnroll];
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t q = base + (int64_t)u * kFetchThreads + tid;
+      dst[u] = nullptr;
+      if (q < total_chunks) {
+        const int gi = (int)(q / kRowChunks);
+        const int c = (int)(q - (int64_t)gi * kRowChunks);
+        int lo = 0, hi = n;  // largest pair with pre_s[pair] <= gi
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre_s[mid] <= gi) lo = mid; else hi = mid;
+        }
+        const int pr = lo;
+        const int i = gi - pre_s[pr];
+        const int2 e = a.fetch[(size_t)pr * a.top_k + i];
+        const int li = pr / R;
+        const int r = pr - li * R;
+        const int l = a.layer_begin + li;
+        if ((unsigned)e.y < (unsigned)a.hot_slots && e.x >= 0 && e.x < ctx[r]) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const char*>(a.host_rows[(size_t)l * R + r]) + (size_t)e.x * kRowBytes) + c;
+          const int64_t row = a.resident_rows + (int64_t)r * a.hot_slots + e.y;
+          dst[u] = reinterpret_cast<u32x4*>(a.kv[l] + row * kLatent) + c;
+          v[u] = __builtin_nontemporal_load(src);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u)
+      if (dst[u]) *dst[u] = v[u];
+  }
+}
+
+__global__ void iota_lru(int32_t* lru, int64_t n_pairs, int B) {
+  const int64_t total = n_pairs * B;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x)
+    lru[i] = (int32_t)(i % B);
+}
+
+__global__ __launch_bounds__(256) void copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * kFetchUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kFetchUnroll; base < n; base += stride) {
+    u32x4 v[kFetchUnroll];
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t q = base + (int64_t)u * 256 + threadIdx.x;
+      if (q < n) v[u] = __builtin_nontemporal_load(src + q);
+    }
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t q = base + (int64_t)u * 256 + threadIdx.x;
+      if (q < n) dst[q] = v[u];
+    }
+  }
+}
+
+}  // namespace
+
+size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits) {
+  return lds_map(top_k, hot_slots, hash_bits, ceil_log2(2 * (int64_t)top_k)).total;
+}
+
+hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
+  const auto& c = p->cfg;
+  const int64_t pairs = (int64_t)c.num_layers * c.num_requests;
+  hipError_t e;
+  if ((e = hipMemsetAsync(p->owner, 0xFF, pairs * c.hot_slots * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->stamp, 0xFF, pairs * c.hot_slots * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->last_t, 0xFF, pairs * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->bt, 0xFF, p->lay.bt_entries * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->miss_count, 0, pairs * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->err, 0, 4, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(iota_lru, dim3(1024), dim3(256), 0, s, p->lru, pairs, c.hot_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_resolve(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
+  const int seen_bits = ceil_log2(2 * (int64_t)a.top_k);
+  const size_t lds = lds_map(a.top_k, a.hot_slots, a.hash_bits, seen_bits).total;
+  prof_begin(p, kKMeta, s);
+  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(64), lds, s, a, seen_bits);
+  hipError_t e = hipGetLastError();
+  prof_end(p, s);
+  if (e != hipSuccess) return e;
+  FetchArgs f;
+  f.miss_count = a.miss_count;
+  f.fetch = a.fetch;
+  f.host_rows = p->host_rows_d;
+  f.kv = p->kv_d;
+  f.layer_begin = a.layer_begin;
+  f.n_pairs = a.n_layers * a.num_requests;
+  f.num_requests = a.num_requests;
+  f.top_k = a.top_k;
+  f.hot_slots = a.hot_slots;
+  f.resident_rows = a.resident_rows;
+  return launch_fetch(p, f, s);
+}
+
+hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& f, hipStream_t s) {
+  if (f.n_pairs > kFetchMaxPairs) return hipErrorInvalidValue;
+  prof_begin(p, kKFetch, s);
+  hipLaunchKernelGGL(fetch_rows, dim3(1024), dim3(kFetchThreads), 0, s, f, p->ctx_d);
+  hipError_t e = hipGetLastError();
+  prof_end(p, s);
+  return e;
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  int64_t blocks = (n + 256 * kFetchUnroll - 1) / (256 * kFetchUnroll);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(copy16, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)dst, (const u32x4*)src, n);
+  return hipGetLastError();
+}
+
+hipError_t set_resolve_lds_limit(size_t bytes) {
+  return hipFuncSetAttribute((const void*)resolve_meta, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace hs

@@ -1,0 +1,208 @@
+/*
+ * hisparse.h -- C ABI of the MI355X (gfx950) HiSparse decode path.
+ *
+ * What the library computes (sources: the HiSparse summary article
+ * "显存占用直降30倍！大模型稀疏注意力解码KV缓存方案HiSparse夯爆了", section 02,
+ * and the vLLM blog "GLM 5.3 优化（一）：vLLM 的 Hybrid HiSparse 混合稀疏卸载",
+ * section "工作原理"):
+ *
+ *   The full latent KV of every request and sparse layer lives in a pinned,
+ *   device-mapped host pool.  On the device each (request, layer) owns a
+ *   fixed buffer of B "hot" rows; a per-request block table marks 64-token
+ *   pages that are GPU-resident (read in place, never evicted).  Every
+ *   decode step the indexer names K logical positions per request; RESOLVE
+ *   turns each into a row id of the layer's KV tensor:
+ *     - position on a resident page  -> block * page_size + offset
+ *     - position already in the hot buffer (hit) -> hot row, LRU refreshed
+ *     - otherwise (miss) -> an LRU victim slot, whose row is fetched from
+ *       the host pool by GPU loads over the host link.
+ *   Sparse MLA decode attention then runs over the resolved rows.
+ *
+ * Row ids index one KV tensor per layer: rows [0, resident_rows_per_layer)
+ * hold resident pages (block b = rows [b*page_size, (b+1)*page_size)), and
+ * rows [resident_rows_per_layer + r*B, ... + B) are the hot rows of request
+ * r.  A KV row is latent_dim = 576 bf16 values (512 "nope" + 64 rope); the
+ * value vector is its first v_dim = 512 values.
+ *
+ * Replacement rule (exact; the pages say only that LRU metadata drives
+ * replacement and that the current selection must be served): every slot
+ * starts empty (owner -1, stamp -1); a call at step t stamps every slot it
+ * touches with t; slots hit or filled by a call cannot be evicted by the
+ * same call; victims are the untouched slots with the smallest (stamp,
+ * slot); the i-th smallest missing position fills the i-th victim.
+ *
+ * Conventions
+ *   - Status: every function returns HISPARSE_OK (0) or a negative code;
+ *     hisparse_last_error() gives a message for the calling thread's last
+ *     failure.  No exception crosses the ABI.
+ *   - Ownership: the caller owns every device buffer (workspace, KV tensors,
+ *     inputs, outputs) and the stream; the library owns the pinned host pool
+ *     and the opaque pool handle.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  resolve,
+ *     decode and step only enqueue kernels (no host synchronisation, no
+ *     allocation) and read the step index from device memory, so they can be
+ *     captured in a HIP graph.  Calls on one stream run in order; a pool is
+ *     not thread-safe.
+ *   - Host-checkable errors (bad sizes, null pointers, B < K, ...) return
+ *     HISPARSE_EINVAL and enqueue nothing.  Errors only the device can see
+ *     set bits in a device flag word, read (and cleared) by
+ *     hisparse_check_errors; the offending entry is treated as padding.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hisparse_status;
+#define HISPARSE_OK 0
+#define HISPARSE_EINVAL (-1) /* invalid argument or configuration */
+#define HISPARSE_ENOMEM (-2) /* pinned host allocation failed */
+#define HISPARSE_EHIP (-3)   /* a HIP runtime call failed */
+#define HISPARSE_EDEVICE (-4) /* device does not support the launch (LDS, arch) */
+#define HISPARSE_ESTATE (-5)  /* call not valid in the pool's state */
+
+/* Device error flag bits (hisparse_check_errors). */
+#define HISPARSE_ERR_RANGE 1u /* a selected position outside [-1, ctx_r) */
+#define HISPARSE_ERR_DUP 2u   /* a position repeated within one selection (later copies dropped) */
+#define HISPARSE_ERR_STEP 4u  /* step index negative or below the last one seen by a (request, layer) */
+#define HISPARSE_ERR_ROW 8u   /* decode saw a row id outside the KV tensor (treated as padding) */
+
+typedef struct hisparse_pool hisparse_pool;
+
+typedef struct {
+  int32_t num_requests;  /* R >= 1 */
+  int32_t num_layers;    /* L >= 1 sparse layers */
+  int32_t index_share;   /* g: consecutive layers sharing one selection; L % g == 0 */
+  int32_t latent_dim;    /* must be 576 */
+  int32_t v_dim;         /* must be 512 */
+  int32_t top_k;         /* K: positions per selection, 1..4096 */
+  int32_t hot_slots;     /* B: hot rows per (request, layer), K <= B <= 8192 */
+  int32_t page_size;     /* tokens per page, a power of two (64) */
+  int32_t num_heads;     /* H: query heads, a multiple of 16, <= 256 */
+  int32_t host_coherent; /* 0: coarse-grained (non-coherent) pinned pool, 1: coherent */
+  int64_t resident_rows_per_layer; /* rows of each KV tensor reserved for resident pages (multiple of page_size) */
+  const int64_t* ctx_len; /* [R] host array, context length per request (>= 1); copied */
+} hisparse_config;
+
+/* Message describing the calling thread's last failure ("" if none). */
+const char* hisparse_last_error(void);
+
+/* Bytes of device workspace the caller must provide to hisparse_create_pool
+ * (metadata, block tables, miss lists, attention partials). */
+hisparse_status hisparse_workspace_bytes(const hisparse_config* cfg, size_t* bytes);
+
+/* Rows each layer's KV tensor must have: resident_rows_per_layer + R * B. */
+hisparse_status hisparse_kv_rows_per_layer(const hisparse_config* cfg, int64_t* rows);
+
+/* Create a pool on the current device.
+ *   d_workspace: device buffer of at least hisparse_workspace_bytes bytes,
+ *                256-byte aligned; owned by the caller, must outlive the pool.
+ *   d_kv:        host array of L device pointers; d_kv[l] is a bf16 tensor
+ *                [kv_rows_per_layer][576], 16-byte aligned, caller-owned.
+ *   stream:      used to initialise the workspace (synchronised before return).
+ * Allocates the pinned, device-mapped host pool: request r, layer l holds
+ * ctx_r rows of 576 bf16 (filled by the caller via hisparse_host_rows).
+ * Every slot starts empty and every page host-only.
+ * Errors: EINVAL (bad config, null or misaligned pointers, workspace too
+ * small), ENOMEM (pinned allocation failed), EHIP, EDEVICE. */
+hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspace, size_t ws_bytes,
+                                     void* const* d_kv, void* stream, hisparse_pool** out);
+
+/* Free the host pool and the handle (device buffers stay the caller's).
+ * Synchronises the device first.  NULL is ignored. */
+void hisparse_destroy_pool(hisparse_pool* pool);
+
+/* Host address of the pool rows of (request r, layer l): bf16 bits
+ * [ctx_r][576], row-major, for the caller to fill before resolving.
+ * NULL on a bad argument. */
+uint16_t* hisparse_host_rows(hisparse_pool* pool, int32_t r, int32_t l);
+
+/* Set the block table of request r: host_bt[page] is the resident block id
+ * of that page, or -1 (host-only placeholder); n_pages must equal
+ * ceil(ctx_r / page_size).  Block ids must satisfy
+ * (id + 1) * page_size <= resident_rows_per_layer.  The library never edits
+ * a block table, so resident pages (the tail included) are never evicted.
+ * The caller must keep resident rows equal to the host rows they mirror.
+ * Synchronous.  Errors: EINVAL. */
+hisparse_status hisparse_set_block_table(hisparse_pool* pool, int32_t r, const int32_t* host_bt,
+                                         int32_t n_pages, void* stream);
+
+/* RESOLVE layers [layer_begin, layer_begin + n_layers), which share one
+ * selection (they must lie in one index-share group).
+ *   d_step:   device int32 scalar, the step index t (>= 0, non-decreasing
+ *             per (request, layer)); read on the device.
+ *   d_topk:   device int32 [R][K] logical positions, -1 = padding, any order.
+ *   d_rows:   device int32 [n_layers][R][K] out: row id per entry (-1 for padding).
+ *   d_counts: device int32 [n_layers][R][3] out: (resident, hit, miss).
+ * Enqueues the metadata kernel (one wavefront per (request, layer)) and the
+ * miss fetch (zero-copy 16-byte loads from the host pool into hot rows). */
+hisparse_status hisparse_resolve(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers,
+                                 const int32_t* d_step, const int32_t* d_topk, int32_t* d_rows,
+                                 int32_t* d_counts, void* stream);
+
+/* Sparse MLA decode attention of one layer over resolved rows.
+ *   d_q:    device bf16 [R][H][576]
+ *   d_rows: device int32 [R][K] row ids of this layer (-1 = skip)
+ *   scale:  softmax scale applied to q . x
+ *   d_out:  device fp32 [R][H][512] out: softmax(scale q X^T) X[:, :512]
+ *   d_lse:  device fp32 [R][H] out: log-sum-exp of the scaled scores
+ * A request with no valid row gets O = 0 and lse = -inf. */
+hisparse_status hisparse_sparse_mla_decode(hisparse_pool* pool, int32_t layer, const uint16_t* d_q,
+                                           const int32_t* d_rows, float scale, float* d_out,
+                                           float* d_lse, void* stream);
+
+/* One decode step over every layer: for each index-share group, RESOLVE all
+ * of its layers with the group's selection, then decode each layer.
+ *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],
+ *   d_counts [L][R][3], d_out [L][R][H][512], d_lse [L][R][H]. */
+hisparse_status hisparse_step(hisparse_pool* pool, const int32_t* d_step, const int32_t* d_topk,
+                              const uint16_t* d_q, float scale, int32_t* d_rows, int32_t* d_counts,
+                              float* d_out, float* d_lse, void* stream);
+
+/* Copy the LRU state of (request r, layer l) to host arrays of B int32:
+ * owner (logical position per slot, -1 empty) and stamp (step of last use,
+ * -1 never).  Synchronises the stream.  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_export_state(hisparse_pool* pool, int32_t r, int32_t l, int32_t* host_owner,
+                                      int32_t* host_stamp, void* stream);
+
+/* Read and clear the device error flags (HISPARSE_ERR_* bits).
+ * Synchronises the stream. */
+hisparse_status hisparse_check_errors(hisparse_pool* pool, void* stream, uint32_t* flags);
+
+/* ---- measurement helpers (not on the decode path) ---- */
+
+/* Per-kernel timing with HIP events recorded on the launch stream around
+ * every kernel the pool enqueues (resolve metadata, miss fetch, decode,
+ * split combine).  Off by default; while on, each launch adds two event
+ * records.  Up to 8192 launches are kept between reads. */
+typedef struct {
+  const char* name;   /* kernel name (static storage) */
+  int32_t launches;   /* launches timed since the last read */
+  double total_ms;    /* summed event-measured duration */
+} hisparse_kernel_time;
+
+hisparse_status hisparse_profile_enable(hisparse_pool* pool, int32_t enable);
+/* Synchronises on the recorded events, fills up to `max` entries (one per
+ * kernel that ran) and clears the record.  *n receives the entry count. */
+hisparse_status hisparse_profile_read(hisparse_pool* pool, hisparse_kernel_time* out, int32_t max, int32_t* n);
+
+/* Pinned, device-mapped host buffer with the pool's flags; *host and *dev
+ * receive the host address and the device-visible address. */
+hisparse_status hisparse_host_alloc(size_t bytes, int32_t coherent, void** host, void** dev);
+void hisparse_host_free(void* host);
+
+/* Copy `bytes` (a multiple of 16) from src to dst with the same 16-byte
+ * vector-load kernel the miss fetch uses; src may be a device-mapped host
+ * address (zero-copy read over the host link) or device memory. */
+hisparse_status hisparse_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

@@ -1,0 +1,82 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+configurations on the host (no GPU needed: no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from host_offloaded_kv_amd import hisparse as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "hisparse.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hisparse_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = H.load()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(H.EXPORTED) == names
+
+
+def _cfg(**kw):
+    base = dict(num_requests=2, num_layers=4, index_share=4, top_k=2048, hot_slots=4096, num_heads=128,
+                resident_rows_per_layer=128, ctx_len=[131072, 5000])
+    base.update(kw)
+    return H.make_config(base)
+
+
+def test_sizes():
+    c, keep = _cfg()
+    assert H.hisparse_kv_rows_per_layer(c) == 128 + 2 * 4096
+    ws = H.hisparse_workspace_bytes(c)
+    # owner + stamp + order arrays alone are 3 * L * R * B * 4 bytes
+    assert ws >= 3 * 4 * 2 * 4096 * 4
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hot_slots=1000),            # B < K
+    dict(top_k=0),
+    dict(top_k=5000, hot_slots=8000),
+    dict(hot_slots=9000),
+    dict(index_share=3),             # L % g != 0
+    dict(num_heads=24),              # not a multiple of 16
+    dict(page_size=48),              # not a power of two
+    dict(resident_rows_per_layer=100),
+    dict(ctx_len=[0, 5]),
+    dict(latent_dim=512),
+])
+def test_bad_configs_rejected(bad):
+    c, keep = _cfg(**bad)
+    with pytest.raises(H.HiSparseError) as ei:
+        H.hisparse_workspace_bytes(c)
+    assert ei.value.status == H.HISPARSE_EINVAL
+    assert H.hisparse_last_error()
+
+
+def test_null_arguments_rejected():
+    lib = H.load()
+    assert lib.hisparse_workspace_bytes(None, None) == H.HISPARSE_EINVAL
+    assert lib.hisparse_resolve(None, 0, 1, None, None, None, None, None) == H.HISPARSE_EINVAL
+    assert lib.hisparse_step(None, None, None, None, 1.0, None, None, None, None, None) == H.HISPARSE_EINVAL
+    assert lib.hisparse_host_rows(None, 0, 0) is None
+    assert lib.hisparse_stream_copy(None, None, 16, None) == H.HISPARSE_EINVAL
+    c, keep = _cfg()
+    out = ctypes.c_void_p()
+    assert lib.hisparse_create_pool(ctypes.byref(c), None, 0, None, None, ctypes.byref(out)) == H.HISPARSE_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(H, "_lib", None)
+    monkeypatch.setattr(H, "LIB_PATH", os.path.join(ROOT, "does_not_exist.so"))
+    with pytest.raises(RuntimeError):
+        H.load()
