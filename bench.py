@@ -114,6 +114,9 @@ def main() -> int:
     ap.add_argument("--host-coherent", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run 3 device-to-device copies of this size with the library's copy kernel "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -243,6 +246,15 @@ def main() -> int:
     measured_link = max(v for k, v in probe.items() if k != "d2d_copy_GBs") if probe else None
     if "fetch_rows" in kern and measured_link:
         kern["fetch_rows"]["frac_of_measured_link"] = round(kern["fetch_rows"]["achieved"] / measured_link, 4)
+
+    if args.calib_copy_mib:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            H.hisparse_stream_copy(dst.data_ptr(), src.data_ptr(), nb, stream.cuda_stream)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     cpu = None
     hs.close()

@@ -11,9 +11,21 @@
 // same as attention over the full KV with the same selection.
 //
 // Work split: a workgroup handles (layer, request, group of up to 64 heads,
-// K split); 32-row tiles are gathered into LDS with direct-to-LDS loads
-// (double-buffered), QK^T and PV run on 16x16x32 bf16 MFMA with fp32
-// accumulation, and split partials are merged by a second kernel.
+// K split) with 8 wavefronts, two per SIMD, specialised by role:
+//  * score waves 0-3: wave w owns heads 16w .. 16w+15 of the group; it keeps
+//    their Q in registers, computes the 32x16 score block of each 32-row
+//    tile on 16x16x32 bf16 MFMA, applies the softmax (all rows of its heads
+//    are in the wave, so no cross-wave reduction is needed) and writes the
+//    bf16 probabilities P to LDS;
+//  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
+//    every head of the group (fp32 accumulators in AGPRs); it multiplies the
+//    transposed tile (read with ds_read_b64_tr_b16) by P, and it also loads
+//    the tiles: global loads into registers one tile ahead, stored to LDS
+//    after use.
+// The value waves run one tile behind the score waves, so each tile costs a
+// single workgroup barrier and the two waves sharing a SIMD overlap each
+// other's LDS and softmax latency with MFMA work.  Split partials are merged
+// by a second kernel.
 #include "internal.h"
 
 #include <cmath>
@@ -22,14 +34,15 @@ namespace hs {
 namespace {
 
 constexpr int kT = 32;                        // rows per tile
-constexpr int kPitchChunks = kRowChunks + 2;  // LDS row pitch: 72 data + 2 pad chunks (1184 bytes)
+constexpr int kPitchChunks = kRowChunks + 1;  // LDS row pitch: 72 data + 1 pad chunk (1168 bytes)
 constexpr int kPitch = kPitchChunks * 16;
-constexpr int kTileBytes = kT * kPitch;       // 37888 = 37 KiB
-constexpr int kTileBlocks = kTileBytes / 1024; // 1 KiB direct-to-LDS blocks per tile
-constexpr int kThreads = 256;                 // 4 wavefronts
+constexpr int kTileBytes = kT * kPitch;       // 37376
+constexpr int kNBuf = 3;                      // tiles in LDS: scored, multiplied, being stored
+constexpr int kThreads = 512;                 // 8 wavefronts
 constexpr int kPPitch = kT + 8;               // bf16 per P row (80 bytes)
-constexpr int kPartW = kVDim + 2;             // partial record: o[512], m, l
-constexpr float kMaxGrowLog2 = 64.f;          // P = 2^(s - m) may reach 2^64 before a restart
+constexpr float kMaxGrowLog2 = 64.f;          // P = 2^(s - m) may reach 2^64 before a second pass
+constexpr int kStage = kRowChunks / 8;        // 9 chunks per loading thread per tile
+static_assert(kT * 8 == 256 && kRowChunks % 8 == 0, "8 loader threads per row, 256 loaders per tile");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -37,6 +50,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef const __attribute__((address_space(1))) u32x4 gu32x4;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
@@ -54,37 +68,48 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
   return r;
 }
 
-// Issue the direct-to-LDS loads of one tile.  The tile is kT rows of
-// kPitch bytes; block b (1 KiB) is written by one wavefront instruction,
-// lane l landing at byte 16 (64 b + l).  Slot s = 64 b + l is chunk
-// s % kPitchChunks of row s / kPitchChunks; the two pad chunks of a row
-// re-read its first chunk (an L1 hit) and are never used.
-__device__ __forceinline__ void issue_tile(const uint16_t* kv, unsigned char* xs, const int* rowid, int w, int lane) {
-  for (int blk = w; blk < kTileBlocks; blk += 4) {
-    const int slot = blk * 64 + lane;
-    const int j = slot / kPitchChunks;
-    int c = slot - j * kPitchChunks;
-    c = c < kRowChunks ? c : 0;
-    const int rid = rowid[j];
-    const uint16_t* src = kv + (size_t)(rid < 0 ? 0 : rid) * kLatent + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_u8*)(xs + blk * 1024), 16, 0, 0);
-  }
+// Tile loads go through VGPRs: each loading thread fetches 9 16-byte chunks
+// of a tile with ordinary global loads one tile ahead, and writes them to
+// LDS after the current tile's work.  On MI355X this sustains ~7.3 TB/s for a random
+// 1152-byte row gather, where direct-to-LDS loads stayed under 3 TB/s.  The
+// loads use global-address-space pointers: flat loads would also count
+// against the LDS wait counter and be drained by every lds_barrier().
+// Loader thread t (0..255) owns row t / 8 of the tile and its chunks
+// t % 8 + 8 k, k = 0..8: eight threads cover 128 contiguous bytes of a row
+// per k, and every address is one base plus an immediate k * 128.
+__device__ __forceinline__ void load_tile(u32x4* st, const uint16_t* kv, const int* rowid, int t) {
+  const int rid = rowid[t >> 3];
+  gu32x4* src = (gu32x4*)(kv + (size_t)(rid < 0 ? 0 : rid) * kLatent + (t & 7) * 8);
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) st[k] = src[8 * k];
 }
+
+__device__ __forceinline__ void store_tile(const u32x4* st, unsigned char* xs, int t) {
+  u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) dst[8 * k] = st[k];
+}
+
+// Workgroup barrier for LDS traffic only: unlike __syncthreads() it does
+// not wait for outstanding global loads, so tile loads stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // D += A * B on a 16x16x32 bf16 MFMA (fp32 accumulate), compiler-scheduled.
 __device__ __forceinline__ void mfma16(f32x4& d, const u32x4& a, const u32x4& b) {
   d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
 }
 
-// The PV accumulators are pinned to AGPRs with inline asm ("a" constraint):
-// with the builtin the register allocator keeps them in VGPRs next to the
-// 144-register Q operand and copies them through AGPRs around every MFMA.
-// The compiler does not see these as MFMAs, so the two hazards they can
-// meet are covered by hand:
+// The value accumulators are pinned to AGPRs with inline asm ("a"
+// constraint); with the builtin the register allocator moves them between
+// register files around the MFMAs.  The compiler does not see these as
+// MFMAs, so the hazards they can meet are covered by hand:
 //  * an operand written by a VALU instruction just before: two wait states
 //    in front of the first MFMA that reads a freshly assembled operand;
 //  * reading the accumulators afterwards (v_accvgpr_read): agpr_drain()
-//    inserts 24 wait states, more than an 8-pass MFMA needs.
+//    inserts 128 wait states after the last MFMA;
+//  * the accumulators must never be copied by the compiler inside the loop
+//    (checked in the generated code), since such a copy would read an AGPR
+//    that an MFMA may still be writing.
 // Back-to-back MFMAs that chain through srcC need no wait states.
 __device__ __forceinline__ void mfma16_agpr(f32x4& d, const u32x4& a, const u32x4& b) {
   asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
@@ -96,24 +121,40 @@ __device__ __forceinline__ void zero_agpr(f32x4& d) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(d) : "v"(z));
 }
-__device__ __forceinline__ void agpr_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// Score MFMAs: A (tile rows) in VGPRs, B (Q) in AGPRs, scores in VGPRs.
+// The first k-step starts from srcC = 0.  score_drain() must separate the
+// last one from any VALU read of the scores (the compiler does not see
+// these as MFMAs either).
+__device__ __forceinline__ void mfma_score_first(f32x4& d, const u32x4& a, const f32x4& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_score(f32x4& d, const u32x4& a, const f32x4& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// The drains name the registers they protect as read-write operands, so no
+// later read of those registers can be scheduled above the wait states.
+__device__ __forceinline__ void score_drain(f32x4& s0, f32x4& s1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1)::"memory");
+}
+template <int N>
+__device__ __forceinline__ void agpr_drain(f32x4 (&acc)[N]) {
+  asm volatile(
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; i += 2) asm volatile("" : "+a"(acc[i]), "+a"(acc[i + 1]));
+}
 
-// One workgroup = (layer, request, group of HG heads, K split).  Wave w:
-//  * QK^T: rows 16*(w%2) .. +15 of the tile against heads
-//    (w/2)*SH .. +SH-1 of the group (SH = max(16, HG/2)), Q in registers;
-//  * PV: output columns 128 w .. 128 w + 127 for all HG heads.
 template <int HG>
-__global__ __launch_bounds__(kThreads, 1) void decode_mfma(DecodeArgs a, int nhg) {
-  constexpr int SH = HG / 2 < 16 ? 16 : HG / 2;  // heads per wave in QK^T
-  constexpr int NBW = SH / 16;                    // 16-head blocks per wave in QK^T
-  constexpr int NBP = HG / 16;                    // 16-head blocks in PV
-  __shared__ __align__(16) unsigned char xs[2][kTileBytes];
-  __shared__ __align__(16) uint16_t ps[HG][kPPitch];
-  __shared__ float mred[2][HG];
-  __shared__ float lred[2][HG];
+__global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
+  constexpr int NBP = HG / 16;  // 16-head blocks
+  __shared__ __align__(16) unsigned char xs[kNBuf][kTileBytes];
+  __shared__ __align__(16) uint16_t ps[2][HG][kPPitch];
+  __shared__ int rowid_all[kMaxTopK];
+  __shared__ float lred[HG];
+  __shared__ float lexact_s[HG];
   __shared__ float mfin_s[HG];
-  __shared__ int rowid_s[2][kT];
-  __shared__ int restart_s;
+  __shared__ int overflow_s;
 
   const int H = a.num_heads, R = a.num_requests, K = a.top_k;
   // XCD-aware order: consecutive logical blocks (the head groups and splits
@@ -128,9 +169,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma(DecodeArgs a, int nhg
   const uint16_t* kv = a.kv[l];
   const int32_t* rows = a.rows + (size_t)pair * K;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
-  const int rb = w & 1, hw = w >> 1;
-  const bool s_active = hw * SH < HG;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, i16 = lane & 15;
+  const bool score_wave = w < 4;
+  const bool s_active = score_wave && 16 * w < HG;  // score wave with heads to own
+  const int cw = w - 4;                             // value wave: column block
+  const int lt = tid - 256;                         // value wave: loader thread index
 
   int per = (K + a.splits - 1) / a.splits;
   per = (per + kT - 1) / kT * kT;
@@ -138,186 +183,192 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma(DecodeArgs a, int nhg
   const int k1 = min(K, k0 + per);
   const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
 
-  // Q of this wave's QK^T heads, in the MFMA B-operand layout:
-  // lane (g, i16) holds dims 32 s + 8 g .. +7 of head (block nb, i16).
-  u32x4 qreg[NBW][kLatent / 32];
+  // One AGPR-resident array serves both roles, so the compiler allocates
+  // it once: a value wave accumulates O^T in acc[mb * NBP + nb]; a score
+  // wave keeps the Q of its 16 heads in acc[0 .. 18) as MFMA B operands
+  // (lane (g, i16) holding dims 32 s + 8 g .. +7 of head 16 w + i16).
+  constexpr int kAcc = 8 * NBP > kLatent / 32 ? 8 * NBP : kLatent / 32;
+  f32x4 acc[kAcc];
+  u32x4 st[kStage];  // value wave: one tile of staged loads
+  float m_run = -INFINITY, m_seen = -INFINITY, l_run = 0.f, l_exact = 0.f;
   if (s_active) {
+    const int head = hg * HG + 16 * w + i16;
+    gu32x4* qp = (gu32x4*)(a.q + ((size_t)pair * H + head) * kLatent + 8 * g);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int head = hg * HG + hw * SH + nb * 16 + i16;
-      const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)pair * H + head) * kLatent + 8 * g);
+    for (int s = 0; s < kLatent / 32; ++s) acc[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
+    asm volatile("s_nop 4" ::: "memory");  // AGPR writes -> MFMA reads
 #pragma unroll
-      for (int s = 0; s < kLatent / 32; ++s) qreg[nb][s] = qp[4 * s];
-    }
+    for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+a"(acc[s]), "+a"(acc[s + 1]));
   }
-  float m_run[NBW], l_run[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
-  }
-  f32x4 o[8][NBP];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBP; ++nb) zero_agpr(o[mb][nb]);
 
-  if (tid < kT) {
-    rowid_s[0][tid] = load_row_id(a, rows, k0 + tid, k1);
-    rowid_s[1][tid] = load_row_id(a, rows, k0 + kT + tid, k1);
-  }
+  // Row ids of the whole K range, validated once.
+  for (int k = tid; k < n_tiles * kT; k += kThreads) rowid_all[k] = load_row_id(a, rows, k0 + k, k1);
+  if (tid == 0) overflow_s = 0;
   __syncthreads();
-  if (n_tiles > 0) issue_tile(kv, xs[0], rowid_s[0], w, lane);
 
   // Softmax with a fixed reference max per head: the first valid tile sets
-  // m, and P = 2^(s*scale*log2e - m) accumulates unnormalised.  If a later
-  // tile exceeds m by more than 2^64, every wave restarts from tile 0 with
-  // the larger m (exact either way; never taken unless scores jump that
-  // far), so the O accumulators never need rescaling inside the loop.
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) restart_s = 0;
-    if (it + 1 < n_tiles) issue_tile(kv, xs[buf ^ 1], rowid_s[buf ^ 1], w, lane);
-    const unsigned char* xb = xs[buf];
-
-    // ---- QK^T and the tile max -------------------------------------------
-    f32x4 sacc[NBW];
-    bool valid[4];
-    if (s_active) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
-      const unsigned char* xrow = xb + (16 * rb + i16) * kPitch + 16 * g;
-#pragma unroll
-      for (int s = 0; s < kLatent / 32; ++s) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) mfma16(sacc[nb], av, qreg[nb][s]);
-        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) valid[v] = rowid_s[buf][16 * rb + 4 * g + v] >= 0;
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          sacc[nb][v] = valid[v] ? sacc[nb][v] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sacc[nb][v]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (g == 0) mred[rb][hw * SH + nb * 16 + i16] = mx;
-      }
-    }
-    __syncthreads();
-    // ---- softmax against the reference max, P to LDS -----------------------
-    if (s_active) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const int hs = hw * SH + nb * 16 + i16;
-        const float mt = fmaxf(mred[0][hs], mred[1][hs]);
-        if (m_run[nb] == -INFINITY) {
-          m_run[nb] = mt;  // first valid rows of this head: O and l are still zero
-        } else if (mt > m_run[nb] + kMaxGrowLog2) {
-          m_run[nb] = mt;
-          restart_s = 1;
-        }
-        const float m = m_run[nb];
-        float p[4], sum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[v] = valid[v] ? __builtin_amdgcn_exp2f(sacc[nb][v] - m) : 0.f;
-          sum += p[v];
-        }
-        l_run[nb] += sum;
-        u32x2 pk = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-        *reinterpret_cast<u32x2*>(&ps[hs][16 * rb + 4 * g]) = pk;
-      }
-    }
-    __syncthreads();
-    if (__builtin_expect(restart_s != 0, 0)) {
-      // Rare path: drop everything accumulated and start over from tile 0.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // m, and P = 2^(s*scale*log2e - m) accumulates unnormalised, so the O
+  // accumulators are never rescaled inside the loop.  If a later tile
+  // exceeds m by more than 2^64 (never for ordinary scores), the whole range
+  // is recomputed once with m = the true maximum, which no tile can exceed.
+  // Both passes give the exact softmax.
+  for (int pass = 0; pass < 2; ++pass) {
+    if (!score_wave) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NBP; ++nb) zero_agpr(o[mb][nb]);
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) l_run[nb] = 0.f;
-      __syncthreads();
-      if (tid < kT) {
-        rowid_s[0][tid] = load_row_id(a, rows, k0 + tid, k1);
-        rowid_s[1][tid] = load_row_id(a, rows, k0 + kT + tid, k1);
+        for (int nb = 0; nb < NBP; ++nb) zero_agpr(acc[mb * NBP + nb]);
+      if (n_tiles > 0) {
+        load_tile(st, kv, rowid_all, lt);
+        store_tile(st, xs[0], lt);
       }
-      __syncthreads();
-      issue_tile(kv, xs[0], rowid_s[0], w, lane);
-      it = -1;
-      continue;
+      if (n_tiles > 1) load_tile(st, kv, rowid_all + kT, lt);
     }
-    if (tid < kT) rowid_s[buf][tid] = load_row_id(a, rows, k0 + (it + 2) * kT + tid, k1);
-    // ---- PV: O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T[32 x HG] ---
-    u32x4 bp[NBP];
+    l_run = 0.f;
+    l_exact = 0.f;
+    lds_barrier();
+
+    // Iteration it: score tile it, multiply tile it-1.
+    for (int it = 0; it <= n_tiles; ++it) {
+      if (score_wave) {
+        if (s_active && it < n_tiles) {
+          const unsigned char* xb = xs[it % kNBuf];
+          const int* rowid_t = rowid_all + it * kT;
+          f32x4 sacc[2];
+          // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
+          const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
 #pragma unroll
-    for (int nb = 0; nb < NBP; ++nb) bp[nb] = *reinterpret_cast<const u32x4*>(&ps[nb * 16 + i16][8 * g]);
-    // Transposed A operand: lane i16 of each 16-lane group supplies row
-    // j0 + i16/4, columns c0 + 4 (i16 % 4) .. +3, and receives column
-    // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).
-    const lds_u8* xl = (const lds_u8*)xb + (8 * g + (i16 >> 2)) * kPitch + (128 * w + 4 * (i16 & 3)) * 2;
+          for (int s = 0; s < kLatent / 32; ++s) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
+            if (s == 0) {
+              mfma_score_first(sacc[0], a0, acc[0]);
+              mfma_score_first(sacc[1], a1, acc[0]);
+            } else {
+              mfma_score(sacc[0], a0, acc[s]);
+              mfma_score(sacc[1], a1, acc[s]);
+            }
+            if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
+          }
+          score_drain(sacc[0], sacc[1]);
+          // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
+          bool valid[2][4];
+          float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
-      const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      mfma16_agpr_after_valu(o[mb][0], av, bp[0]);
+          for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nb = 1; nb < NBP; ++nb) mfma16_agpr(o[mb][nb], av, bp[nb]);
-      if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < 4; ++v) {
+              valid[rb][v] = rowid_t[16 * rb + 4 * g + v] >= 0;
+              sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * a.scale_log2 : -INFINITY;
+              mx = fmaxf(mx, sacc[rb][v]);
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          m_seen = fmaxf(m_seen, mx);
+          if (m_run == -INFINITY) {
+            m_run = mx;  // first valid rows of this head: O and l are still zero
+          } else if (mx > m_run + kMaxGrowLog2) {
+            overflow_s = 1;  // this pass is discarded; P may overflow below
+          }
+          uint16_t* prow = &ps[it & 1][16 * w + i16][0];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            float p[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
+            l_exact += (p[0] + p[1]) + (p[2] + p[3]);
+            const u32x2 pk = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+            *reinterpret_cast<u32x2*>(prow + 16 * rb + 4 * g) = pk;
+            // O is normalised by the sum of the bf16-rounded weights that PV
+            // multiplies (an exact convex combination of the value rows);
+            // lse uses the sum of the unrounded weights.
+            l_run += (__uint_as_float(pk[0] << 16) + __uint_as_float(pk[0] & 0xFFFF0000u)) +
+                     (__uint_as_float(pk[1] << 16) + __uint_as_float(pk[1] & 0xFFFF0000u));
+          }
+        }
+      } else if (it >= 1) {
+        // ---- O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T[32 x HG] ----
+        const int tp = it - 1;
+        const unsigned char* xb = xs[tp % kNBuf];
+        u32x4 bp[NBP];
+#pragma unroll
+        for (int nb = 0; nb < NBP; ++nb) bp[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][16 * nb + i16][8 * g]);
+        // Transposed A operand: lane i16 of each 16-lane group supplies row
+        // j0 + i16/4, columns c0 + 4 (i16 % 4) .. +3, and receives column
+        // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).
+        const lds_u8* xl = (const lds_u8*)xb + (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          const s16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
+          const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          mfma16_agpr_after_valu(acc[mb * NBP], av, bp[0]);
+#pragma unroll
+          for (int nb = 1; nb < NBP; ++nb) mfma16_agpr(acc[mb * NBP + nb], av, bp[nb]);
+          if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!score_wave && it + 1 < n_tiles) {
+        // Tile it+1: registers -> its LDS slot (last read two iterations ago),
+        // then start loading tile it+2.
+        store_tile(st, xs[(it + 1) % kNBuf], lt);
+        if (it + 2 < n_tiles) load_tile(st, kv, rowid_all + (it + 2) * kT, lt);
+      }
+      lds_barrier();
     }
+    if (!overflow_s) break;
+    m_run = m_seen;
+    lds_barrier();
   }
 
-  agpr_drain();
-  // ---- epilogue: combine the row-half sums, normalise, write --------------
+  // ---- epilogue: normaliser per head, then O / l and lse ------------------
   if (s_active) {
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      float ls = l_run[nb];
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      const int hs = hw * SH + nb * 16 + i16;
-      if (g == 0) {
-        lred[rb][hs] = ls;
-        if (rb == 0) mfin_s[hs] = m_run[nb];
-      }
+    float ls = l_run, le = l_exact;
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    le += __shfl_xor(le, 16, 64);
+    le += __shfl_xor(le, 32, 64);
+    if (g == 0) {
+      lred[16 * w + i16] = ls;
+      lexact_s[16 * w + i16] = le;
+      mfin_s[16 * w + i16] = m_run;
     }
   }
   __syncthreads();
+  if (score_wave) return;
+  agpr_drain(acc);
   const size_t head0 = (size_t)pair * H + hg * HG;
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
     const int h = nb * 16 + i16;
-    const float lsum = lred[0][h] + lred[1][h];
+    const float lsum = lred[h];
+    const float lex = lexact_s[h];
     const float m = mfin_s[h];
     if (a.splits == 1) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      float* out = a.out + (head0 + h) * kVDim + 128 * w + 4 * g;
+      float* out = a.out + (head0 + h) * kVDim + 128 * cw + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(out + 16 * mb) = o[mb][nb] * inv;
-      if (w == 0 && g == 0) a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
+      for (int mb = 0; mb < 8; ++mb) {
+        *reinterpret_cast<f32x4*>(out + 16 * mb) = acc[mb * NBP + nb] * inv;
+        __builtin_amdgcn_sched_barrier(0);  // few accumulators in VGPRs at a time
+      }
+      if (cw == 0 && g == 0)
+        a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lex)) * 0.69314718055994531f : -INFINITY;
     } else {
       float* part = a.partial + (((size_t)pair * a.splits + split) * H + hg * HG + h) * kPartW;
-      float* po = part + 128 * w + 4 * g;
+      float* po = part + 128 * cw + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) po[16 * mb + v] = o[mb][nb][v];
+        for (int v = 0; v < 4; ++v) po[16 * mb + v] = acc[mb * NBP + nb][v];
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (w == 0 && g == 0) {
+      if (cw == 0 && g == 0) {
         part[kVDim] = m;
         part[kVDim + 1] = lsum;
+        part[kVDim + 2] = lex;
       }
     }
   }
@@ -339,11 +390,15 @@ __global__ __launch_bounds__(256) void combine_splits(DecodeArgs a) {
     if (threadIdx.x == 0) a.lse[ph] = -INFINITY;
     return;
   }
-  float L = 0.f;
+  float L = 0.f, LE = 0.f;
   for (int s = 0; s < a.splits; ++s) {
     const float* part = a.partial + ((pair * a.splits + s) * H + head) * kPartW;
     const float ls = part[kVDim + 1];
-    if (ls > 0.f) L += ls * exp2f(part[kVDim] - mmax);
+    if (ls > 0.f) {
+      const float f = exp2f(part[kVDim] - mmax);
+      L += ls * f;
+      LE += part[kVDim + 2] * f;
+    }
   }
   const float inv = 1.f / L;
   for (int c = threadIdx.x; c < kVDim; c += 256) {
@@ -355,7 +410,7 @@ __global__ __launch_bounds__(256) void combine_splits(DecodeArgs a) {
     }
     out[c] = acc * inv;
   }
-  if (threadIdx.x == 0) a.lse[ph] = (mmax + log2f(L)) * 0.69314718055994531f;
+  if (threadIdx.x == 0) a.lse[ph] = (mmax + log2f(LE)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -377,11 +432,11 @@ hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s) {
   const int grid = a.n_layers * a.num_requests * nhg * a.splits;
   prof_begin(p, kKDecode, s);
   if (hgs == 64)
-    hipLaunchKernelGGL(decode_mfma<64>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
+    hipLaunchKernelGGL(decode_ws<64>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
   else if (hgs == 32)
-    hipLaunchKernelGGL(decode_mfma<32>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
+    hipLaunchKernelGGL(decode_ws<32>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
   else
-    hipLaunchKernelGGL(decode_mfma<16>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
+    hipLaunchKernelGGL(decode_ws<16>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   if (e != hipSuccess || a.splits == 1) return e;

@@ -15,6 +15,7 @@ constexpr int kLatent = 576;         // bf16 values per KV row
 constexpr int kVDim = 512;           // value width (the "nope" part)
 constexpr int kRowBytes = kLatent * 2;
 constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per row (72)
+constexpr int kPartW = kVDim + 4;           // split partial: o[512], m, l (rounded weights), l (exact), pad
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHotSlots = 8192;
 constexpr int kMaxHeads = 256;
@@ -64,7 +65,7 @@ struct DecodeArgs {
   uint16_t* const* kv;     // [L] device array of KV tensor pointers
   float* out;              // [n_layers][R][H][512]
   float* lse;              // [n_layers][R][H]
-  float* partial;          // [n_layers][R][splits][H][514] when splits > 1
+  float* partial;          // [n_layers][R][splits][H][kPartW] when splits > 1
   uint32_t* err;
   int32_t layer_begin;
   int32_t n_layers;

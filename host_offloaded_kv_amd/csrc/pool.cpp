@@ -95,8 +95,8 @@ Layout make_layout(const hisparse_config* c) {
   const int s1 = decode_splits(1, c->num_requests, c->num_heads, c->top_k);
   const int sg = decode_splits(c->index_share, c->num_requests, c->num_heads, c->top_k);
   L.splits_max = s1 > sg ? s1 : sg;
-  size_t part_1 = s1 > 1 ? (size_t)s1 * R * c->num_heads * (kVDim + 2) : 0;
-  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * c->num_heads * (kVDim + 2) : 0;
+  size_t part_1 = s1 > 1 ? (size_t)s1 * R * c->num_heads * kPartW : 0;
+  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * c->num_heads * kPartW : 0;
   size_t off = 0;
   L.owner = off; off = align256(off + NL * R * B * 4);
   L.stamp = off; off = align256(off + NL * R * B * 4);

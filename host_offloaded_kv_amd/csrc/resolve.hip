@@ -48,6 +48,20 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy n int32 from global memory into LDS with direct-to-LDS dword loads
+// (no VGPR round trip, all in flight at once); lanes past n are masked off.
+// The caller waits with s_waitcnt vmcnt(0) and a barrier.
+__device__ __forceinline__ void g2l_i32(int32_t* lds, const int32_t* g, int n, int lane) {
+  for (int c = 0; c < n; c += 64)
+    if (c + lane < n) __builtin_amdgcn_global_load_lds(g + c + lane, (lds_void*)(lds + c), 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 int ceil_log2(int64_t v) {
   int b = 0;
@@ -56,7 +70,7 @@ int ceil_log2(int64_t v) {
 }
 
 struct LdsMap {
-  size_t owner, stamp, lru, sel, mpos, mj, vic, flag, region, total;
+  size_t owner, stamp, lru, sel, mpos, mj, vic, btv, flag, region, total;
   int seen_bits;
 };
 
@@ -69,7 +83,8 @@ __host__ __device__ inline LdsMap lds_map(int K, int B, int hash_bits, int seen_
   m.mpos = m.sel + 4 * (size_t)K;
   m.mj = m.mpos + 4 * (size_t)K;
   m.vic = m.mj + 4 * (size_t)K;
-  m.flag = m.vic + 4 * (size_t)K;
+  m.btv = m.vic + 4 * (size_t)K;
+  m.flag = m.btv + 4 * (size_t)K;
   m.region = (m.flag + (size_t)B + 15) & ~(size_t)15;
   size_t hash_bytes = (size_t)4 << hash_bits;
   size_t seen_bytes = (size_t)8 << seen_bits;  // also holds the miss sort (<= K entries)
@@ -89,6 +104,7 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   int32_t* mpos_s = (int32_t*)(smem + M.mpos);
   int32_t* mj_s = (int32_t*)(smem + M.mj);
   int32_t* vic_s = (int32_t*)(smem + M.vic);
+  int32_t* btv_s = (int32_t*)(smem + M.btv);
   unsigned char* flag_s = smem + M.flag;
   int32_t* hash_s = (int32_t*)(smem + M.region);
   unsigned long long* kv64_s = (unsigned long long*)(smem + M.region);
@@ -125,26 +141,35 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   int32_t* owner_g = a.owner + pair * B;
   int32_t* stamp_g = a.stamp + pair * B;
   int32_t* lru_g = a.lru + pair * B;
-  for (int s = lane; s < B; s += 64) {
-    owner_s[s] = owner_g[s];
-    stamp_s[s] = stamp_g[s];
-    lru_s[s] = lru_g[s];
-    flag_s[s] = 0;
-  }
+  // State and selection arrive together through direct-to-LDS loads.
+  g2l_i32(owner_s, owner_g, B, lane);
+  g2l_i32(stamp_s, stamp_g, B, lane);
+  g2l_i32(lru_s, lru_g, B, lane);
+  g2l_i32(sel_s, topk, K, lane);
+  for (int s = lane; s < B; s += 64) flag_s[s] = 0;
+  wait_vmem_and_sync();
 
   // Selection: validate the range; note whether it is strictly ascending
   // with padding only at the end (then it has no repeats and its misses
   // come out already in ascending order).
   uint32_t errbits = 0;
   for (int j = lane; j < K; j += 64) {
-    int p = topk[j];
+    const int p = sel_s[j];
     if (p < -1 || p >= ctx) {
       errbits |= HISPARSE_ERR_RANGE;
-      p = -1;
+      sel_s[j] = -1;
     }
-    sel_s[j] = p;
   }
   __syncthreads();
+  // Block-table entry of every selected page, gathered straight into LDS.
+  const int32_t* bt = a.bt + a.bt_off[r];
+  for (int c = 0; c < K; c += 64) {
+    const int j = c + lane;
+    if (j < K) {
+      const int p = sel_s[j];
+      __builtin_amdgcn_global_load_lds(bt + (p >= 0 ? (p >> page_shift) : 0), (lds_void*)(btv_s + c), 4, 0, 0);
+    }
+  }
   bool bad = false;
   for (int j = lane; j + 1 < K; j += 64) {
     const int a0 = sel_s[j], a1 = sel_s[j + 1];
@@ -191,16 +216,31 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   const int HS = 1 << a.hash_bits;
   for (int i = lane; i < HS; i += 64) hash_s[i] = -1;
   __syncthreads();
-  for (int s = lane; s < B; s += 64) {
-    const int p = owner_s[s];
-    if (p < 0) continue;
-    uint32_t h = hash_pos(p, a.hash_bits);
-    while (atomicCAS(&hash_s[h], -1, s) != -1) h = (h + 1) & (HS - 1);
+  for (int s0 = 0; s0 < B; s0 += 256) {
+    // four inserts per lane in flight at once
+    int sl[4];
+    uint32_t h[4];
+    bool pend[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sl[u] = s0 + 64 * u + lane;
+      const int p = sl[u] < B ? owner_s[sl[u]] : -1;
+      pend[u] = p >= 0;
+      h[u] = pend[u] ? hash_pos(p, a.hash_bits) : 0u;
+    }
+    while (pend[0] || pend[1] || pend[2] || pend[3]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pend[u]) {
+          if (atomicCAS(&hash_s[h[u]], -1, sl[u]) == -1) pend[u] = false;
+          else h[u] = (h[u] + 1) & (HS - 1);
+        }
+      }
+    }
   }
-  __syncthreads();
+  wait_vmem_and_sync();  // also completes the block-table gather
 
   // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
-  const int32_t* bt = a.bt + a.bt_off[r];
   int n_res = 0, n_hit = 0, m = 0;
   for (int j0 = 0; j0 < K; j0 += 64) {
     const int j = j0 + lane;
@@ -210,7 +250,7 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
       p = sel_s[j];
       int row = -1;
       if (p >= 0) {
-        const int blk = bt[p >> page_shift];
+        const int blk = btv_s[j];
         if (blk >= 0) {
           row = (blk << page_shift) + (p & page_mask);
           ++n_res;
