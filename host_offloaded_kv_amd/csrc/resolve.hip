@@ -10,15 +10,16 @@
 // slot, nothing on the decode path waits for the CPU).
 //
 // Design on CDNA4:
-//  * resolve_meta: one 64-lane wavefront per (request, layer).  The slot
-//    owner, stamp and LRU-order arrays and the position->slot page table (an
-//    open-addressing hash rebuilt from the owner array on every call) live
-//    in LDS.  Misses are compacted with wavefront ballots in ascending
-//    position order; victims are the first unpinned slots of a persistent
-//    array that lists all slots in ascending (stamp, slot) order, so victim
-//    choice is a single ballot scan with no sort.  After the fills the order
-//    array is rebuilt as [untouched slots with stamp < t, in old order] ++
-//    [slots with stamp == t, by slot index], which keeps it sorted.
+//  * resolve_meta: one 4-wavefront workgroup per (request, layer).  The
+//    slot owner, stamp and LRU-order arrays and the position->slot page
+//    table (an open-addressing hash rebuilt from the owner array on every
+//    call) live in LDS.  Misses are compacted with wavefront ballots in
+//    ascending position order; victims are the first unpinned slots of a
+//    persistent array that lists all slots in ascending (stamp, slot) order,
+//    so victim choice is a ballot scan with no sort.  After the fills the
+//    order array is rebuilt as [untouched slots with stamp < t, in old
+//    order] ++ [slots with stamp == t, by slot index], which keeps it
+//    sorted.  Only the owner and stamp entries that change are written back.
 //  * fetch_rows: a fan-out copy over the whole GPU.  Each workgroup scans
 //    the per-(request, layer) miss counts in LDS, then the grid walks a flat
 //    index of 16-byte chunks over every missed row (72 chunks per 1152-byte
@@ -50,14 +51,6 @@ __device__ __forceinline__ int wave_sum(int v) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copy n int32 from global memory into LDS with direct-to-LDS dword loads
-// (no VGPR round trip, all in flight at once); lanes past n are masked off.
-// The caller waits with s_waitcnt vmcnt(0) and a barrier.
-__device__ __forceinline__ void g2l_i32(int32_t* lds, const int32_t* g, int n, int lane) {
-  for (int c = 0; c < n; c += 64)
-    if (c + lane < n) __builtin_amdgcn_global_load_lds(g + c + lane, (lds_void*)(lds + c), 4, 0, 0);
-}
-
 __device__ __forceinline__ void wait_vmem_and_sync() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -69,10 +62,14 @@ int ceil_log2(int64_t v) {
   return b;
 }
 
+constexpr int kMetaThreads = 256;  // 4 wavefronts per (request, layer)
+constexpr int kMetaWaves = kMetaThreads / 64;
+
 struct LdsMap {
-  size_t owner, stamp, lru, sel, mpos, mj, vic, btv, flag, region, total;
-  int seen_bits;
+  size_t owner, stamp, lru, sel, mpos, mj, vic, btv, flag, missf, region, total;
 };
+
+__host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 __host__ __device__ inline LdsMap lds_map(int K, int B, int hash_bits, int seen_bits) {
   LdsMap m;
@@ -84,17 +81,45 @@ __host__ __device__ inline LdsMap lds_map(int K, int B, int hash_bits, int seen_
   m.mj = m.mpos + 4 * (size_t)K;
   m.vic = m.mj + 4 * (size_t)K;
   m.btv = m.vic + 4 * (size_t)K;
-  m.flag = m.btv + 4 * (size_t)K;
-  m.region = (m.flag + (size_t)B + 15) & ~(size_t)15;
-  size_t hash_bytes = (size_t)4 << hash_bits;
-  size_t seen_bytes = (size_t)8 << seen_bits;  // also holds the miss sort (<= K entries)
+  m.flag = round16(m.btv + 4 * (size_t)K);
+  m.missf = m.flag + round16((size_t)B);
+  m.region = m.missf + round16((size_t)K);
+  const size_t hash_bytes = (size_t)4 << hash_bits;
+  const size_t seen_bytes = (size_t)8 << seen_bits;  // also holds the miss sort (<= K entries)
   m.total = m.region + (hash_bytes > seen_bytes ? hash_bytes : seen_bytes);
-  m.seen_bits = seen_bits;
   return m;
 }
 
-__global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits) {
+// Direct-to-LDS copy of n int32 by one workgroup: wave w issues chunks
+// w, w+4, ... of 64 dwords; lanes past n are masked off.
+__device__ __forceinline__ void g2l_block(int32_t* lds, const int32_t* g, int n, int wid, int lane) {
+  for (int c = wid * 64; c < n; c += kMetaThreads)
+    if (c + lane < n) __builtin_amdgcn_global_load_lds(g + c + lane, (lds_void*)(lds + c), 4, 0, 0);
+}
+
+// Exclusive prefix over the per-wave counts in cnt[0..kMetaWaves).
+__device__ __forceinline__ int wave_base(const int* cnt, int wid, int* total) {
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kMetaWaves; ++w2) {
+    const int c = cnt[w2];
+    base += w2 < wid ? c : 0;
+    tot += c;
+  }
+  *total = tot;
+  return base;
+}
+
+// One workgroup (4 wavefronts) per (request, layer).  Element-wise passes
+// are split over all 256 threads; the order-preserving compactions (the
+// miss list in ascending position, the victims in (stamp, slot) order, the
+// rebuilt order array) give each wave a contiguous quarter of the input,
+// count with ballots, exchange the four counts through LDS and then write
+// at base + ballot prefix.
+__global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int seen_bits) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int cnt_s[2][kMetaWaves];
+  __shared__ int red_s[2][kMetaWaves];
   const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
   const LdsMap M = lds_map(K, B, a.hash_bits, seen_bits);
   int32_t* owner_s = (int32_t*)(smem + M.owner);
@@ -106,10 +131,13 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   int32_t* vic_s = (int32_t*)(smem + M.vic);
   int32_t* btv_s = (int32_t*)(smem + M.btv);
   unsigned char* flag_s = smem + M.flag;
+  unsigned char* missf_s = smem + M.missf;
   int32_t* hash_s = (int32_t*)(smem + M.region);
   unsigned long long* kv64_s = (unsigned long long*)(smem + M.region);
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const uint64_t lt = lanemask_lt();
   const int li = blockIdx.x / R;
   const int r = blockIdx.x - li * R;
@@ -124,10 +152,9 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   const int page_shift = a.page_shift;
   const int page_mask = (1 << page_shift) - 1;
 
-  const int last = a.last_t[pair];
-  if (t < 0 || t < last) {
-    for (int j = lane; j < K; j += 64) rows_out[j] = -1;
-    if (lane == 0) {
+  if (t < 0 || t < a.last_t[pair]) {
+    for (int j = tid; j < K; j += kMetaThreads) rows_out[j] = -1;
+    if (tid == 0) {
       a.counts[cpair * 3 + 0] = 0;
       a.counts[cpair * 3 + 1] = 0;
       a.counts[cpair * 3 + 2] = 0;
@@ -136,24 +163,23 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
     }
     return;
   }
-  if (lane == 0) a.last_t[pair] = t;
 
   int32_t* owner_g = a.owner + pair * B;
   int32_t* stamp_g = a.stamp + pair * B;
   int32_t* lru_g = a.lru + pair * B;
   // State and selection arrive together through direct-to-LDS loads.
-  g2l_i32(owner_s, owner_g, B, lane);
-  g2l_i32(stamp_s, stamp_g, B, lane);
-  g2l_i32(lru_s, lru_g, B, lane);
-  g2l_i32(sel_s, topk, K, lane);
-  for (int s = lane; s < B; s += 64) flag_s[s] = 0;
+  g2l_block(owner_s, owner_g, B, wid, lane);
+  g2l_block(stamp_s, stamp_g, B, wid, lane);
+  g2l_block(lru_s, lru_g, B, wid, lane);
+  g2l_block(sel_s, topk, K, wid, lane);
+  for (int i = tid; i < (int)(round16(B) / 4); i += kMetaThreads) ((uint32_t*)flag_s)[i] = 0u;
   wait_vmem_and_sync();
 
   // Selection: validate the range; note whether it is strictly ascending
   // with padding only at the end (then it has no repeats and its misses
   // come out already in ascending order).
   uint32_t errbits = 0;
-  for (int j = lane; j < K; j += 64) {
+  for (int j = tid; j < K; j += kMetaThreads) {
     const int p = sel_s[j];
     if (p < -1 || p >= ctx) {
       errbits |= HISPARSE_ERR_RANGE;
@@ -161,29 +187,29 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
     }
   }
   __syncthreads();
+  bool bad = false;
+  for (int j = tid; j + 1 < K; j += kMetaThreads) {
+    const int a0 = sel_s[j], a1 = sel_s[j + 1];
+    const int k0 = a0 < 0 ? INT_MAX : a0, k1 = a1 < 0 ? INT_MAX : a1;
+    if (!(k0 < k1 || (k0 == INT_MAX && k1 == INT_MAX))) bad = true;
+  }
+  const bool fast = __syncthreads_or(bad) == 0;
   // Block-table entry of every selected page, gathered straight into LDS.
   const int32_t* bt = a.bt + a.bt_off[r];
-  for (int c = 0; c < K; c += 64) {
+  for (int c = wid * 64; c < K; c += kMetaThreads) {
     const int j = c + lane;
     if (j < K) {
       const int p = sel_s[j];
       __builtin_amdgcn_global_load_lds(bt + (p >= 0 ? (p >> page_shift) : 0), (lds_void*)(btv_s + c), 4, 0, 0);
     }
   }
-  bool bad = false;
-  for (int j = lane; j + 1 < K; j += 64) {
-    const int a0 = sel_s[j], a1 = sel_s[j + 1];
-    const int k0 = a0 < 0 ? INT_MAX : a0, k1 = a1 < 0 ? INT_MAX : a1;
-    if (!(k0 < k1 || (k0 == INT_MAX && k1 == INT_MAX))) bad = true;
-  }
-  const bool fast = __ballot(bad) == 0ull;
 
   if (!fast) {
     // Repeated positions: keep the earliest entry (smallest j) of each.
     const int ES = 1 << seen_bits;
-    for (int i = lane; i < ES; i += 64) kv64_s[i] = ~0ull;
+    for (int i = tid; i < ES; i += kMetaThreads) kv64_s[i] = ~0ull;
     __syncthreads();
-    for (int j = lane; j < K; j += 64) {
+    for (int j = tid; j < K; j += kMetaThreads) {
       const int p = sel_s[j];
       if (p < 0) continue;
       const unsigned long long ent = ((unsigned long long)(uint32_t)p << 32) | (uint32_t)j;
@@ -199,7 +225,7 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
       }
     }
     __syncthreads();
-    for (int j = lane; j < K; j += 64) {
+    for (int j = tid; j < K; j += kMetaThreads) {
       const int p = sel_s[j];
       if (p < 0) continue;
       uint32_t h = hash_pos(p, seen_bits);
@@ -214,16 +240,16 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
 
   // Page table: position -> slot, rebuilt from the owner array.
   const int HS = 1 << a.hash_bits;
-  for (int i = lane; i < HS; i += 64) hash_s[i] = -1;
+  for (int i = tid; i < HS; i += kMetaThreads) hash_s[i] = -1;
   __syncthreads();
-  for (int s0 = 0; s0 < B; s0 += 256) {
-    // four inserts per lane in flight at once
+  for (int s0 = 0; s0 < B; s0 += 4 * kMetaThreads) {
+    // four inserts per thread in flight at once
     int sl[4];
     uint32_t h[4];
     bool pend[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      sl[u] = s0 + 64 * u + lane;
+      sl[u] = s0 + kMetaThreads * u + tid;
       const int p = sl[u] < B ? owner_s[sl[u]] : -1;
       pend[u] = p >= 0;
       h[u] = pend[u] ? hash_pos(p, a.hash_bits) : 0u;
@@ -241,13 +267,15 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
   wait_vmem_and_sync();  // also completes the block-table gather
 
   // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
-  int n_res = 0, n_hit = 0, m = 0;
-  for (int j0 = 0; j0 < K; j0 += 64) {
+  // Wave w takes entries [w Kq, (w+1) Kq), so wave order is input order.
+  const int Kq = (K + kMetaThreads - 1) / kMetaThreads * 64;
+  const int jb = wid * Kq, je = min(K, jb + Kq);
+  int n_res = 0, n_hit = 0, mloc = 0;
+  for (int j0 = jb; j0 < je; j0 += 64) {
     const int j = j0 + lane;
     bool miss = false;
-    int p = -1;
-    if (j < K) {
-      p = sel_s[j];
+    if (j < je) {
+      const int p = sel_s[j];
       int row = -1;
       if (p >= 0) {
         const int blk = btv_s[j];
@@ -260,6 +288,7 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
           while ((s = hash_s[h]) >= 0 && owner_s[s] != p) h = (h + 1) & (HS - 1);
           if (s >= 0) {
             stamp_s[s] = t;
+            stamp_g[s] = t;
             flag_s[s] = 1;
             row = (int)(hot_base + s);
             ++n_hit;
@@ -269,14 +298,26 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
         }
       }
       if (!miss) rows_out[j] = row;
+      missf_s[j] = miss ? 1 : 0;
     }
-    const uint64_t bm = __ballot(miss);
-    if (miss) {
-      const int idx = m + __popcll(bm & lt);
-      mpos_s[idx] = p;
-      mj_s[idx] = j;
+    mloc += __popcll(__ballot(miss));
+  }
+  if (lane == 0) cnt_s[0][wid] = mloc;
+  __syncthreads();
+  int m;
+  {
+    int run = wave_base(cnt_s[0], wid, &m);
+    for (int j0 = jb; j0 < je; j0 += 64) {
+      const int j = j0 + lane;
+      const bool miss = j < je && missf_s[j];
+      const uint64_t bm = __ballot(miss);
+      if (miss) {
+        const int idx = run + __popcll(bm & lt);
+        mpos_s[idx] = sel_s[j];
+        mj_s[idx] = j;
+      }
+      run += __popcll(bm);
     }
-    m += __popcll(bm);
   }
   __syncthreads();
 
@@ -284,12 +325,12 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
     // Ascending position order of the misses: bitonic sort of (pos, j).
     int mp = 1;
     while (mp < m) mp <<= 1;
-    for (int i = lane; i < mp; i += 64)
+    for (int i = tid; i < mp; i += kMetaThreads)
       kv64_s[i] = i < m ? (((unsigned long long)(uint32_t)mpos_s[i] << 32) | (uint32_t)mj_s[i]) : ~0ull;
     __syncthreads();
     for (int k = 2; k <= mp; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = lane; i < mp; i += 64) {
+        for (int i = tid; i < mp; i += kMetaThreads) {
           const int ixj = i ^ jj;
           if (ixj > i) {
             const unsigned long long x = kv64_s[i], y = kv64_s[ixj];
@@ -303,72 +344,112 @@ __global__ __launch_bounds__(64) void resolve_meta(ResolveArgs a, int seen_bits)
         __syncthreads();
       }
     }
-    for (int i = lane; i < m; i += 64) {
+    for (int i = tid; i < m; i += kMetaThreads) {
       mpos_s[i] = (int)(kv64_s[i] >> 32);
       mj_s[i] = (int)(uint32_t)kv64_s[i];
     }
     __syncthreads();
   }
 
-  // Victims: the first m unpinned slots in (stamp, slot) order.
-  int found = 0;
-  for (int i0 = 0; i0 < B && found < m; i0 += 64) {
-    const int i = i0 + lane;
-    const int s = i < B ? lru_s[i] : 0;
-    const bool cand = i < B && flag_s[s] == 0;
-    const uint64_t bm = __ballot(cand);
-    if (cand) {
-      const int rank = found + __popcll(bm & lt);
-      if (rank < m) vic_s[rank] = s;
+  // Victims: the first m unpinned slots of the (stamp, slot) order array.
+  // Wave w scans entries [w Bq, (w+1) Bq) of the array.
+  const int Bq = (B + kMetaThreads - 1) / kMetaThreads * 64;
+  const int ib = wid * Bq, ie = min(B, ib + Bq);
+  {
+    int uloc = 0;
+    for (int i0 = ib; i0 < ie; i0 += 64) {
+      const int i = i0 + lane;
+      const bool cand = i < ie && flag_s[lru_s[i]] == 0;
+      uloc += __popcll(__ballot(cand));
     }
-    found += __popcll(bm);
+    if (lane == 0) cnt_s[1][wid] = uloc;
+  }
+  __syncthreads();
+  {
+    int unpinned;
+    int run = wave_base(cnt_s[1], wid, &unpinned);
+    for (int i0 = ib; i0 < ie && run < m; i0 += 64) {
+      const int i = i0 + lane;
+      const int s = i < ie ? lru_s[i] : 0;
+      const bool cand = i < ie && flag_s[s] == 0;
+      const uint64_t bm = __ballot(cand);
+      if (cand) {
+        const int rank = run + __popcll(bm & lt);
+        if (rank < m) vic_s[rank] = s;
+      }
+      run += __popcll(bm);
+    }
   }
   __syncthreads();
 
   // Fill: i-th smallest missing position -> i-th victim.
   int2* fetch = a.fetch + cpair * K;
-  for (int i = lane; i < m; i += 64) {
+  for (int i = tid; i < m; i += kMetaThreads) {
     const int v = vic_s[i], p = mpos_s[i], j = mj_s[i];
     owner_s[v] = p;
     stamp_s[v] = t;
     flag_s[v] = 1;
+    owner_g[v] = p;
+    stamp_g[v] = t;
     rows_out[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
   __syncthreads();
 
   // New order: untouched slots older than t (old order), then every slot
-  // stamped t, by slot index.
-  int nA = 0;
-  for (int i0 = 0; i0 < B; i0 += 64) {
-    const int i = i0 + lane;
-    const int s = i < B ? lru_s[i] : 0;
-    const bool keep = i < B && stamp_s[s] < t;
-    const uint64_t bm = __ballot(keep);
-    if (keep) lru_g[nA + __popcll(bm & lt)] = s;
-    nA += __popcll(bm);
+  // stamped t, by slot index.  Both parts are counted in one pass.
+  {
+    int ca = 0, cb = 0;
+    for (int i0 = ib; i0 < ie; i0 += 64) {
+      const int i = i0 + lane;
+      const bool keep = i < ie && stamp_s[lru_s[i]] < t;
+      const bool inB = i < ie && stamp_s[i] == t;
+      ca += __popcll(__ballot(keep));
+      cb += __popcll(__ballot(inB));
+    }
+    if (lane == 0) {
+      cnt_s[0][wid] = ca;
+      cnt_s[1][wid] = cb;
+    }
   }
-  int nB = 0;
-  for (int s0 = 0; s0 < B; s0 += 64) {
-    const int s = s0 + lane;
-    const bool inB = s < B && stamp_s[s] == t;
-    const uint64_t bm = __ballot(inB);
-    if (inB) lru_g[nA + nB + __popcll(bm & lt)] = s;
-    nB += __popcll(bm);
-  }
-  for (int s = lane; s < B; s += 64) {
-    owner_g[s] = owner_s[s];
-    stamp_g[s] = stamp_s[s];
+  __syncthreads();
+  {
+    int nA, nB;
+    int ra = wave_base(cnt_s[0], wid, &nA);
+    int rb = nA + wave_base(cnt_s[1], wid, &nB);
+    for (int i0 = ib; i0 < ie; i0 += 64) {
+      const int i = i0 + lane;
+      const int s = i < ie ? lru_s[i] : 0;
+      const bool keep = i < ie && stamp_s[s] < t;
+      const bool inB = i < ie && stamp_s[i] == t;
+      const uint64_t ba = __ballot(keep), bb = __ballot(inB);
+      if (keep) lru_g[ra + __popcll(ba & lt)] = s;
+      if (inB) lru_g[rb + __popcll(bb & lt)] = i;
+      ra += __popcll(ba);
+      rb += __popcll(bb);
+    }
   }
 
   n_res = wave_sum(n_res);
   n_hit = wave_sum(n_hit);
   if (errbits) atomicOr(a.err, errbits);
   if (lane == 0) {
-    a.counts[cpair * 3 + 0] = n_res;
-    a.counts[cpair * 3 + 1] = n_hit;
+    red_s[0][wid] = n_res;
+    red_s[1][wid] = n_hit;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tr = 0, th = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kMetaWaves; ++w2) {
+      tr += red_s[0][w2];
+      th += red_s[1][w2];
+    }
+    a.counts[cpair * 3 + 0] = tr;
+    a.counts[cpair * 3 + 1] = th;
     a.counts[cpair * 3 + 2] = m;
     a.miss_count[cpair] = m;
+    a.last_t[pair] = t;
   }
 }
 
@@ -488,7 +569,7 @@ hipError_t launch_resolve(hisparse_pool* p, const ResolveArgs& a, hipStream_t s)
   const int seen_bits = ceil_log2(2 * (int64_t)a.top_k);
   const size_t lds = lds_map(a.top_k, a.hot_slots, a.hash_bits, seen_bits).total;
   prof_begin(p, kKMeta, s);
-  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(64), lds, s, a, seen_bits);
+  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(kMetaThreads), lds, s, a, seen_bits);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   if (e != hipSuccess) return e;
