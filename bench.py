@@ -114,6 +114,11 @@ def main() -> int:
     ap.add_argument("--host-coherent", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--fetch-wg", type=int, default=0,
+                    help="workgroups of each per-layer miss fetch in the overlapped step (0 = library default)")
+    ap.add_argument("--no-sync-path", action="store_true",
+                    help="skip the replay of the same steps through the synchronous path")
+    ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph replay of the same steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -165,11 +170,39 @@ def main() -> int:
     log("inputs staged in HBM")
 
     stream = torch.cuda.current_stream(dev)
+    if args.fetch_wg:
+        hs.set_fetch_workgroups(0, args.fetch_wg)
 
-    def step(t):
+    def step(t, s=None):
         H.hisparse_step(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(), d_q[t].data_ptr(), w.scale,
                         d_rows[t].data_ptr(), d_counts[t].data_ptr(), d_out.data_ptr(), d_lse.data_ptr(),
-                        stream.cuda_stream)
+                        (s or stream).cuda_stream)
+
+    def sync_step(t):
+        # the same step through the synchronous path: resolve (metadata + one
+        # fetch of the whole group), then decode layer by layer, one stream
+        g = w.index_share
+        for gi in range(w.groups):
+            l0 = gi * g
+            H.hisparse_resolve(hs.pool, l0, g, d_steps[t:t + 1].data_ptr(), d_topk[t, gi].data_ptr(),
+                               d_rows[t, l0].data_ptr(), d_counts[t, l0].data_ptr(), stream.cuda_stream)
+            for l in range(l0, l0 + g):
+                H.hisparse_sparse_mla_decode(hs.pool, l, d_q[t, l].data_ptr(), d_rows[t, l].data_ptr(), w.scale,
+                                             d_out[l].data_ptr(), d_lse[l].data_ptr(), stream.cuda_stream)
+
+    def time_steps(fn):
+        """Replays steps 0..n_steps from the empty state; returns ms of the timed ones."""
+        hs.reset_state()
+        for t in range(args.warmup):
+            fn(t)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(args.warmup, n_steps):
+            fn(t)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1)
 
     for t in range(args.warmup):
         step(t)
@@ -209,34 +242,57 @@ def main() -> int:
     meta_bytes = L * R * (2 * 3 * B * 4 + 2 * K * 4 + 12) + misses.sum(axis=(1, 2)) * 8
     hbm_step_bytes = attn_bytes + host_bytes + meta_bytes  # hot-row writes counted once in host_bytes
 
-    groups = w.groups
-    launches_per_step = {"resolve_meta": groups, "fetch_rows": groups, "sparse_mla_decode": groups,
-                         "combine_splits": groups}
     kern = {}
     for name, (n, tot_ms) in prof.items():
+        # algorithmic bytes of the timed steps, spread evenly over the launches
         avg_ms = tot_ms / n
-        per_launch_steps = args.steps * launches_per_step[name]
         if name == "fetch_rows":
-            alg = host_bytes.sum() / per_launch_steps
+            alg = host_bytes.sum() / n
             bound, peak, unit = "host_link", PCIE_PEAK_GBS, "GB/s"
         elif name == "sparse_mla_decode":
-            alg = attn_bytes.sum() / per_launch_steps
+            alg = attn_bytes.sum() / n
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
         elif name == "resolve_meta":
-            alg = meta_bytes.sum() / per_launch_steps
+            alg = meta_bytes.sum() / n
             bound, peak, unit = "alu", None, "GB/s"
         else:
-            alg = 2 * L * R * Hh * 514 * 4 / groups
+            alg = args.steps * L * R * Hh * 4 * (2 * (512 + 4) + 512 + 1) / n
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
         ach = alg / (avg_ms * 1e-3) / 1e9
         kern[name] = {"launches": n, "avg_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg),
                       "achieved": round(ach, 2), "bound": bound, "peak": peak, "unit": unit,
                       "frac": round(ach / peak, 4) if peak else None,
-                      "share_of_step": round(tot_ms / ms_total, 4)}
+                      "busy_share_of_step": round(tot_ms / ms_total, 4)}
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kern[dom]
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
                 "frac": d["frac"], "traffic": None, "kernel": dom, "avg_us": d["avg_us"]}
+
+    graph_ms = None
+    if not args.no_graph:
+        log("captured-graph replay of the same steps")
+        side = torch.cuda.Stream(device=dev)
+        graphs = []
+        hs.reset_state()
+        side.wait_stream(stream)
+        for t in range(n_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(t, side)
+            graphs.append(g)
+        torch.cuda.synchronize(dev)
+        graph_ms = time_steps(lambda t: graphs[t].replay())
+        log(f"graph replay: {graph_ms / args.steps * 1e3:.1f} us/step")
+        del graphs
+    sync_ms = None
+    if not args.no_sync_path:
+        log("synchronous path (resolve, then per-layer decode, one stream)")
+        sync_ms = time_steps(sync_step)
+        log(f"synchronous path: {sync_ms / args.steps * 1e3:.1f} us/step")
+    flags = hs.check_errors()
+    if flags:
+        log(f"device error flags {flags:#x} after the replays")
+        return 1
 
     probe = None
     if not args.no_probe:
@@ -287,6 +343,10 @@ def main() -> int:
                  "host_GBs": round(float(host_bytes.mean()) / (ms_step * 1e-3) / 1e9, 2),
                  "miss_rate": round(float(misses.sum() / max(valid.sum(), 1)), 4),
                  "attn_gflop": round(float(attn_flops.mean()) / 1e9, 2)},
+        "layer_ahead": {"fetch_wg_per_layer": args.fetch_wg or None,
+                        "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None,
+                        "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
+                        "sync_path_tokens_per_s": round(R * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
         "host_link": probe,
         "cpu_baseline": cpu,
     }

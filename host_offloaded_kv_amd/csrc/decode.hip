@@ -16,16 +16,22 @@
 //    their Q in registers, computes the 32x16 score block of each 32-row
 //    tile on 16x16x32 bf16 MFMA, applies the softmax (all rows of its heads
 //    are in the wave, so no cross-wave reduction is needed) and writes the
-//    bf16 probabilities P to LDS;
+//    probabilities P to LDS as two bf16 planes, P = P_hi + P_lo;
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
 //    every head of the group (fp32 accumulators in AGPRs); it multiplies the
-//    transposed tile (read with ds_read_b64_tr_b16) by P, and it also loads
+//    transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo
+//    (one tile read, two MFMAs), and it also loads
 //    the tiles: global loads into registers one tile ahead, stored to LDS
 //    after use.
 // The value waves run one tile behind the score waves, so each tile costs a
 // single workgroup barrier and the two waves sharing a SIMD overlap each
 // other's LDS and softmax latency with MFMA work.  Split partials are merged
 // by a second kernel.
+//
+// Precision: a single bf16 P carries a relative rounding error up to 2^-8
+// per weight, which for near-uniform softmax weights shows up in O at the
+// 1e-3 level.  The hi/lo pair represents P to about 2^-16, so O keeps the
+// accuracy of fp32 accumulation over exact bf16 inputs.
 #include "internal.h"
 
 #include <cmath>
@@ -149,7 +155,7 @@ template <int HG>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   constexpr int NBP = HG / 16;  // 16-head blocks
   __shared__ __align__(16) unsigned char xs[kNBuf][kTileBytes];
-  __shared__ __align__(16) uint16_t ps[2][HG][kPPitch];
+  __shared__ __align__(16) uint16_t ps[2][2][HG][kPPitch];  // [tile parity][hi, lo][head][row]
   __shared__ int rowid_all[kMaxTopK];
   __shared__ float lred[HG];
   __shared__ float lexact_s[HG];
@@ -270,29 +276,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
           } else if (mx > m_run + kMaxGrowLog2) {
             overflow_s = 1;  // this pass is discarded; P may overflow below
           }
-          uint16_t* prow = &ps[it & 1][16 * w + i16][0];
+          uint16_t* prow_hi = &ps[it & 1][0][16 * w + i16][0];
+          uint16_t* prow_lo = &ps[it & 1][1][16 * w + i16][0];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            float p[4];
+            float p[4], r[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
             l_exact += (p[0] + p[1]) + (p[2] + p[3]);
-            const u32x2 pk = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-            *reinterpret_cast<u32x2*>(prow + 16 * rb + 4 * g) = pk;
-            // O is normalised by the sum of the bf16-rounded weights that PV
-            // multiplies (an exact convex combination of the value rows);
+            const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+            const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
+                                __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) r[v] = p[v] - h[v];  // exact in fp32
+            const u32x2 lo = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+            *reinterpret_cast<u32x2*>(prow_hi + 16 * rb + 4 * g) = hi;
+            *reinterpret_cast<u32x2*>(prow_lo + 16 * rb + 4 * g) = lo;
+            // O is normalised by the sum of the weights PV actually multiplies
+            // (P_hi + P_lo), so it is a convex combination of the value rows;
             // lse uses the sum of the unrounded weights.
-            l_run += (__uint_as_float(pk[0] << 16) + __uint_as_float(pk[0] & 0xFFFF0000u)) +
-                     (__uint_as_float(pk[1] << 16) + __uint_as_float(pk[1] & 0xFFFF0000u));
+            l_run += ((h[0] + __uint_as_float(lo[0] << 16)) + (h[1] + __uint_as_float(lo[0] & 0xFFFF0000u))) +
+                     ((h[2] + __uint_as_float(lo[1] << 16)) + (h[3] + __uint_as_float(lo[1] & 0xFFFF0000u)));
           }
         }
       } else if (it >= 1) {
         // ---- O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T[32 x HG] ----
         const int tp = it - 1;
         const unsigned char* xb = xs[tp % kNBuf];
-        u32x4 bp[NBP];
+        u32x4 bp[NBP], bq[NBP];  // P_hi, P_lo operands
 #pragma unroll
-        for (int nb = 0; nb < NBP; ++nb) bp[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][16 * nb + i16][8 * g]);
+        for (int nb = 0; nb < NBP; ++nb) {
+          bp[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][0][16 * nb + i16][8 * g]);
+          bq[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][1][16 * nb + i16][8 * g]);
+        }
         // Transposed A operand: lane i16 of each 16-lane group supplies row
         // j0 + i16/4, columns c0 + 4 (i16 % 4) .. +3, and receives column
         // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).
@@ -307,6 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
           mfma16_agpr_after_valu(acc[mb * NBP], av, bp[0]);
 #pragma unroll
           for (int nb = 1; nb < NBP; ++nb) mfma16_agpr(acc[mb * NBP + nb], av, bp[nb]);
+#pragma unroll
+          for (int nb = 0; nb < NBP; ++nb) mfma16_agpr(acc[mb * NBP + nb], av, bq[nb]);
           if (mb & 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -374,43 +392,49 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   }
 }
 
-__global__ __launch_bounds__(256) void combine_splits(DecodeArgs a) {
+// Merge the split partials of one (layer, request, head) per wavefront:
+// lane i owns output columns [4i, 4i+4) and [256+4i, 256+4i+4).
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) {
   const int H = a.num_heads;
-  const size_t ph = blockIdx.x;  // pair * H + head
+  const size_t ph = (size_t)blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);  // pair * H + head
+  const int lane = threadIdx.x & 63;
   const size_t pair = ph / H;
   const int head = (int)(ph % H);
+  const size_t sstride = (size_t)H * kPartW;  // floats between splits of one head
+  const float* part0 = a.partial + (pair * a.splits * H + head) * kPartW;
   float mmax = -INFINITY;
   for (int s = 0; s < a.splits; ++s) {
-    const float* part = a.partial + ((pair * a.splits + s) * H + head) * kPartW;
+    const float* part = part0 + s * sstride;
     if (part[kVDim + 1] > 0.f) mmax = fmaxf(mmax, part[kVDim]);
   }
-  float* out = a.out + ph * kVDim;
+  float4* out = reinterpret_cast<float4*>(a.out + ph * kVDim);
   if (mmax == -INFINITY) {
-    for (int c = threadIdx.x; c < kVDim; c += 256) out[c] = 0.f;
-    if (threadIdx.x == 0) a.lse[ph] = -INFINITY;
+    out[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    out[64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane == 0) a.lse[ph] = -INFINITY;
     return;
   }
   float L = 0.f, LE = 0.f;
+  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
   for (int s = 0; s < a.splits; ++s) {
-    const float* part = a.partial + ((pair * a.splits + s) * H + head) * kPartW;
+    const float* part = part0 + s * sstride;
     const float ls = part[kVDim + 1];
     if (ls > 0.f) {
       const float f = exp2f(part[kVDim] - mmax);
       L += ls * f;
       LE += part[kVDim + 2] * f;
+      const float4 x0 = reinterpret_cast<const float4*>(part)[lane];
+      const float4 x1 = reinterpret_cast<const float4*>(part)[64 + lane];
+      o0.x += x0.x * f; o0.y += x0.y * f; o0.z += x0.z * f; o0.w += x0.w * f;
+      o1.x += x1.x * f; o1.y += x1.y * f; o1.z += x1.z * f; o1.w += x1.w * f;
     }
   }
   const float inv = 1.f / L;
-  for (int c = threadIdx.x; c < kVDim; c += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* part = a.partial + ((pair * a.splits + s) * H + head) * kPartW;
-      const float ls = part[kVDim + 1];
-      if (ls > 0.f) acc += part[c] * exp2f(part[kVDim] - mmax);
-    }
-    out[c] = acc * inv;
-  }
-  if (threadIdx.x == 0) a.lse[ph] = (mmax + log2f(LE)) * 0.69314718055994531f;
+  out[lane] = make_float4(o0.x * inv, o0.y * inv, o0.z * inv, o0.w * inv);
+  out[64 + lane] = make_float4(o1.x * inv, o1.y * inv, o1.z * inv, o1.w * inv);
+  if (lane == 0) a.lse[ph] = (mmax + log2f(LE)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -441,7 +465,9 @@ hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s) {
   prof_end(p, s);
   if (e != hipSuccess || a.splits == 1) return e;
   prof_begin(p, kKCombine, s);
-  hipLaunchKernelGGL(combine_splits, dim3(a.n_layers * a.num_requests * a.num_heads), dim3(256), 0, s, a);
+  // num_heads is a multiple of 16, so the (pair, head) count divides by 4
+  hipLaunchKernelGGL(combine_splits, dim3(a.n_layers * a.num_requests * a.num_heads / (kCombineThreads / 64)),
+                     dim3(kCombineThreads), 0, s, a);
   e = hipGetLastError();
   prof_end(p, s);
   return e;

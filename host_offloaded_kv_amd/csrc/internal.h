@@ -19,6 +19,11 @@ constexpr int kPartW = kVDim + 4;           // split partial: o[512], m, l (roun
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHotSlots = 8192;
 constexpr int kMaxHeads = 256;
+// Workgroups of the miss fetch: a whole-group fetch (hisparse_resolve) owns
+// the GPU; a per-layer fetch of the overlapped step leaves most CUs to the
+// decode running beside it.
+constexpr int kDefaultGroupFetchWorkgroups = 256;
+constexpr int kDefaultLayerFetchWorkgroups = 32;
 
 // Per-launch description of the fan-out copy of missed rows.
 struct FetchArgs {
@@ -122,6 +127,13 @@ struct hisparse_pool {
   uint16_t** kv_d;
   uint32_t* err;
   float* partial;
+  // Overlapped step: per-layer miss fetches run on fetch_stream (default
+  // priority) while the caller's stream decodes earlier layers.
+  hipStream_t fetch_stream = nullptr;
+  hipEvent_t ev_meta = nullptr;
+  std::vector<hipEvent_t> ev_fetch;  // one per layer of an index-share group
+  int fetch_wg_all = hs::kDefaultGroupFetchWorkgroups;  // workgroups of a whole-group fetch
+  int fetch_wg_layer = 0;            // workgroups of a per-layer fetch (0: default)
 };
 
 namespace hs {
@@ -135,8 +147,9 @@ void prof_end(hisparse_pool* p, hipStream_t s);
 // resolve.hip
 size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits);
 hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s);
-hipError_t launch_resolve(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);
-hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& a, hipStream_t s);
+hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
+hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);
+hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& a, int grid, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 // decode.hip

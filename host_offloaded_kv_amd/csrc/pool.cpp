@@ -316,6 +316,19 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     hisparse_destroy_pool(p);
     return hip_fail(e, "workspace initialisation");
   }
+  // Side stream and events of the overlapped step (default priority).
+  p->ev_fetch.assign(cfg->index_share, nullptr);
+  if ((e = hipStreamCreateWithFlags(&p->fetch_stream, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&p->ev_meta, hipEventDisableTiming)) != hipSuccess) {
+    hisparse_destroy_pool(p);
+    return hip_fail(e, "stream/event creation");
+  }
+  for (auto& ev : p->ev_fetch) {
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+      hisparse_destroy_pool(p);
+      return hip_fail(e, "event creation");
+    }
+  }
   *out = p;
   return HISPARSE_OK;
 }
@@ -324,6 +337,10 @@ void hisparse_destroy_pool(hisparse_pool* p) {
   if (!p) return;
   (void)hipDeviceSynchronize();
   for (hipEvent_t e : p->prof.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->ev_fetch)
+    if (e) (void)hipEventDestroy(e);
+  if (p->ev_meta) (void)hipEventDestroy(p->ev_meta);
+  if (p->fetch_stream) (void)hipStreamDestroy(p->fetch_stream);
   for (void* h : p->host_alloc)
     if (h) (void)hipHostFree(h);
   delete p;
@@ -391,12 +408,38 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   while ((1 << ps) < p->cfg.page_size) ++ps;
   a.page_shift = ps;
   a.resident_rows = p->cfg.resident_rows_per_layer;
-  hipError_t e = launch_resolve(p, a, s);
-  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "resolve launch");
+  hipError_t e = launch_meta(p, a, s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "resolve metadata launch");
 }
 
+// Miss fetch of layers [layer, layer + n_layers): their miss lists (stored
+// per layer by the metadata kernel) are copied from the host pool.
+hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers, int grid, hipStream_t s) {
+  const int R = p->cfg.num_requests;
+  FetchArgs f;
+  f.miss_count = p->miss_count + (size_t)layer * R;
+  f.fetch = p->fetch + (size_t)layer * R * p->cfg.top_k;
+  f.host_rows = p->host_rows_d;
+  f.kv = p->kv_d;
+  f.layer_begin = layer;
+  f.n_pairs = n_layers * R;
+  f.num_requests = R;
+  f.top_k = p->cfg.top_k;
+  f.hot_slots = p->cfg.hot_slots;
+  f.resident_rows = p->cfg.resident_rows_per_layer;
+  hipError_t e = launch_fetch(p, f, grid, s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "miss fetch launch");
+}
+
+int layer_fetch_grid(const hisparse_pool* p) {
+  return p->fetch_wg_layer > 0 ? p->fetch_wg_layer : kDefaultLayerFetchWorkgroups;
+}
+
+// splits: key-range splits per (layer, request, head group); 0 picks the
+// count that fills the GPU (decode_splits).
 hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const uint16_t* d_q,
-                               const int32_t* d_rows, float scale, float* d_out, float* d_lse, hipStream_t s) {
+                               const int32_t* d_rows, float scale, float* d_out, float* d_lse, hipStream_t s,
+                               int splits = 0) {
   DecodeArgs a;
   a.q = d_q;
   a.rows = d_rows;
@@ -410,7 +453,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.num_requests = p->cfg.num_requests;
   a.num_heads = p->cfg.num_heads;
   a.top_k = p->cfg.top_k;
-  a.splits = decode_splits(n_layers, p->cfg.num_requests, p->cfg.num_heads, p->cfg.top_k);
+  a.splits = splits > 0 ? splits : decode_splits(n_layers, p->cfg.num_requests, p->cfg.num_heads, p->cfg.top_k);
   a.kv_rows = p->kv_rows;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = launch_decode(p, a, s);
@@ -430,7 +473,10 @@ hisparse_status hisparse_resolve(hisparse_pool* p, int32_t layer_begin, int32_t 
     set_error("hisparse_resolve: layers must lie inside one index-share group");
     return HISPARSE_EINVAL;
   }
-  return enqueue_resolve(p, layer_begin, n_layers, d_step, d_topk, d_rows, d_counts, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  hisparse_status st = enqueue_resolve(p, layer_begin, n_layers, d_step, d_topk, d_rows, d_counts, s);
+  if (st) return st;
+  return enqueue_fetch(p, layer_begin, n_layers, p->fetch_wg_all, s);
 }
 
 hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, const uint16_t* d_q,
@@ -468,16 +514,59 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
   }
   const auto& c = p->cfg;
   const size_t R = c.num_requests, K = c.top_k, H = c.num_heads;
+  const int G = c.index_share;
   hipStream_t s = (hipStream_t)stream;
-  for (int g = 0; g < c.num_layers / c.index_share; ++g) {
-    const int l0 = g * c.index_share;
-    hisparse_status st = enqueue_resolve(p, l0, c.index_share, d_step, d_topk + (size_t)g * R * K,
-                                         d_rows + (size_t)l0 * R * K, d_counts + (size_t)l0 * R * 3, s);
+  hipStream_t fs = p->fetch_stream;
+  const int grid = layer_fetch_grid(p);
+  hipError_t e;
+  for (int g = 0; g < c.num_layers / G; ++g) {
+    const int l0 = g * G;
+    // One metadata launch for the whole group (the layers share the
+    // selection), then per-layer fetches on the side stream, so that the
+    // decode of layer l0+i overlaps the fetches of layers l0+i+1 ...
+    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * K, d_rows + (size_t)l0 * R * K,
+                                         d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
-    st = enqueue_decode(p, l0, c.index_share, d_q + (size_t)l0 * R * H * kLatent, d_rows + (size_t)l0 * R * K, scale,
-                        d_out + (size_t)l0 * R * H * kVDim, d_lse + (size_t)l0 * R * H, s);
-    if (st) return st;
+    if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
+      return hip_fail(e, "hisparse_step: fork");
+    for (int i = 0; i < G; ++i) {
+      if ((st = enqueue_fetch(p, l0 + i, 1, grid, fs))) return st;
+      if ((e = hipEventRecord(p->ev_fetch[i], fs)) != hipSuccess) return hip_fail(e, "hisparse_step: fetch event");
+    }
+    for (int i = 0; i < G; ++i) {
+      const int l = l0 + i;
+      if ((e = hipStreamWaitEvent(s, p->ev_fetch[i], 0)) != hipSuccess) return hip_fail(e, "hisparse_step: join");
+      // A layer decoded while a later layer's fetch is still streaming only
+      // has to finish before that fetch does: it runs unsplit (fewer CUs, no
+      // partials).  The group's last layer is exposed and is split to fill
+      // the GPU.
+      st = enqueue_decode(p, l, 1, d_q + (size_t)l * R * H * kLatent, d_rows + (size_t)l * R * K, scale,
+                          d_out + (size_t)l * R * H * kVDim, d_lse + (size_t)l * R * H, s, i + 1 < G ? 1 : 0);
+      if (st) return st;
+    }
   }
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_reset_state(hisparse_pool* p, void* stream) {
+  if (!p) {
+    set_error("hisparse_reset_state: pool is NULL");
+    return HISPARSE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(p->fetch_stream);
+  if (e == hipSuccess) e = launch_state_reset(p, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_reset_state");
+}
+
+hisparse_status hisparse_set_fetch_workgroups(hisparse_pool* p, int32_t whole_group, int32_t per_layer) {
+  if (!p || whole_group < 0 || per_layer < 0 || whole_group > 65536 || per_layer > 65536) {
+    set_error("hisparse_set_fetch_workgroups: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  p->fetch_wg_all = whole_group > 0 ? whole_group : kDefaultGroupFetchWorkgroups;
+  p->fetch_wg_layer = per_layer;
   return HISPARSE_OK;
 }
 

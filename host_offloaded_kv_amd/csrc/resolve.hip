@@ -453,12 +453,15 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int 
   }
 }
 
-constexpr int kFetchThreads = 256;
+// 1024-thread workgroups (16 wavefronts) keep enough zero-copy loads in
+// flight that a few dozen CUs saturate the host link.
+constexpr int kFetchThreads = 1024;
 constexpr int kFetchUnroll = 4;
+constexpr int kCopyThreads = 256;
 constexpr int kFetchMaxPairs = 8192;
 
 __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const int32_t* ctx) {
-  __shared__ int32_t pre_s[kFetchMaxPairs + 1];
+  extern __shared__ int32_t pre_s[];  // [n_pairs + 1] exclusive prefix of the miss counts
   __shared__ int32_t part_s[kFetchThreads];
   const int n = a.n_pairs, tid = threadIdx.x;
   const int per = (n + kFetchThreads - 1) / kFetchThreads;
@@ -466,14 +469,16 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
   for (int i = tid * per; i < n && i < (tid + 1) * per; ++i) sum += a.miss_count[i];
   part_s[tid] = sum;
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < kFetchThreads; ++i) {
-      const int v = part_s[i];
-      part_s[i] = acc;
-      acc += v;
-    }
+  // exclusive scan of part_s (Hillis-Steele, in place through a register)
+  for (int off = 1; off < kFetchThreads; off <<= 1) {
+    const int add = tid >= off ? part_s[tid - off] : 0;
+    __syncthreads();
+    part_s[tid] += add;
+    __syncthreads();
   }
+  const int excl = part_s[tid] - sum;
+  __syncthreads();
+  part_s[tid] = excl;
   __syncthreads();
   int acc = part_s[tid];
   for (int i = tid * per; i < n && i < (tid + 1) * per; ++i) {
@@ -528,18 +533,19 @@ __global__ void iota_lru(int32_t* lru, int64_t n_pairs, int B) {
     lru[i] = (int32_t)(i % B);
 }
 
-__global__ __launch_bounds__(256) void copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 256 * kFetchUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * 256 * kFetchUnroll; base < n; base += stride) {
+__global__ __launch_bounds__(kCopyThreads) void copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                      int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kCopyThreads * kFetchUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kCopyThreads * kFetchUnroll; base < n; base += stride) {
     u32x4 v[kFetchUnroll];
 #pragma unroll
     for (int u = 0; u < kFetchUnroll; ++u) {
-      const int64_t q = base + (int64_t)u * 256 + threadIdx.x;
+      const int64_t q = base + (int64_t)u * kCopyThreads + threadIdx.x;
       if (q < n) v[u] = __builtin_nontemporal_load(src + q);
     }
 #pragma unroll
     for (int u = 0; u < kFetchUnroll; ++u) {
-      const int64_t q = base + (int64_t)u * 256 + threadIdx.x;
+      const int64_t q = base + (int64_t)u * kCopyThreads + threadIdx.x;
       if (q < n) dst[q] = v[u];
     }
   }
@@ -551,46 +557,39 @@ size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits) {
   return lds_map(top_k, hot_slots, hash_bits, ceil_log2(2 * (int64_t)top_k)).total;
 }
 
-hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
+hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   const auto& c = p->cfg;
   const int64_t pairs = (int64_t)c.num_layers * c.num_requests;
   hipError_t e;
   if ((e = hipMemsetAsync(p->owner, 0xFF, pairs * c.hot_slots * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->stamp, 0xFF, pairs * c.hot_slots * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->last_t, 0xFF, pairs * 4, s)) != hipSuccess) return e;
-  if ((e = hipMemsetAsync(p->bt, 0xFF, p->lay.bt_entries * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->miss_count, 0, pairs * 4, s)) != hipSuccess) return e;
-  if ((e = hipMemsetAsync(p->err, 0, 4, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(iota_lru, dim3(1024), dim3(256), 0, s, p->lru, pairs, c.hot_slots);
   return hipGetLastError();
 }
 
-hipError_t launch_resolve(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
+hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
+  hipError_t e;
+  if ((e = hipMemsetAsync(p->bt, 0xFF, p->lay.bt_entries * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->err, 0, 4, s)) != hipSuccess) return e;
+  return launch_state_reset(p, s);
+}
+
+hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
   const int seen_bits = ceil_log2(2 * (int64_t)a.top_k);
   const size_t lds = lds_map(a.top_k, a.hot_slots, a.hash_bits, seen_bits).total;
   prof_begin(p, kKMeta, s);
   hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(kMetaThreads), lds, s, a, seen_bits);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
-  if (e != hipSuccess) return e;
-  FetchArgs f;
-  f.miss_count = a.miss_count;
-  f.fetch = a.fetch;
-  f.host_rows = p->host_rows_d;
-  f.kv = p->kv_d;
-  f.layer_begin = a.layer_begin;
-  f.n_pairs = a.n_layers * a.num_requests;
-  f.num_requests = a.num_requests;
-  f.top_k = a.top_k;
-  f.hot_slots = a.hot_slots;
-  f.resident_rows = a.resident_rows;
-  return launch_fetch(p, f, s);
+  return e;
 }
 
-hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& f, hipStream_t s) {
-  if (f.n_pairs > kFetchMaxPairs) return hipErrorInvalidValue;
+hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& f, int grid, hipStream_t s) {
+  if (f.n_pairs < 1 || f.n_pairs > kFetchMaxPairs || grid < 1) return hipErrorInvalidValue;
   prof_begin(p, kKFetch, s);
-  hipLaunchKernelGGL(fetch_rows, dim3(1024), dim3(kFetchThreads), 0, s, f, p->ctx_d);
+  hipLaunchKernelGGL(fetch_rows, dim3(grid), dim3(kFetchThreads), (f.n_pairs + 1) * sizeof(int32_t), s, f, p->ctx_d);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   return e;
@@ -598,10 +597,10 @@ hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& f, hipStream_t s) {
 
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   const int64_t n = (int64_t)(bytes / 16);
-  int64_t blocks = (n + 256 * kFetchUnroll - 1) / (256 * kFetchUnroll);
+  int64_t blocks = (n + kCopyThreads * kFetchUnroll - 1) / (kCopyThreads * kFetchUnroll);
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(copy16, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)dst, (const u32x4*)src, n);
+  hipLaunchKernelGGL(copy16, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, (u32x4*)dst, (const u32x4*)src, n);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ EXPORTED = (
     "hisparse_last_error", "hisparse_workspace_bytes", "hisparse_kv_rows_per_layer",
     "hisparse_create_pool", "hisparse_destroy_pool", "hisparse_host_rows",
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
-    "hisparse_step", "hisparse_export_state", "hisparse_check_errors",
+    "hisparse_step", "hisparse_reset_state", "hisparse_set_fetch_workgroups",
+    "hisparse_export_state", "hisparse_check_errors",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
     "hisparse_profile_enable", "hisparse_profile_read",
 )
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
         "hisparse_resolve": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_sparse_mla_decode": (_I32, [_VP, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
+        "hisparse_reset_state": (_I32, [_VP, _VP]),
+        "hisparse_set_fetch_workgroups": (_I32, [_VP, _I32, _I32]),
         "hisparse_export_state": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
         "hisparse_check_errors": (_I32, [_VP, _VP, ctypes.POINTER(ctypes.c_uint32)]),
         "hisparse_host_alloc": (_I32, [ctypes.c_size_t, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP)]),
@@ -171,6 +174,14 @@ def hisparse_sparse_mla_decode(pool, layer, d_q, d_rows, scale, d_out, d_lse, st
 
 def hisparse_step(pool, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse, stream) -> None:
     _check(load().hisparse_step(pool, d_step, d_topk, d_q, float(scale), d_rows, d_counts, d_out, d_lse, stream))
+
+
+def hisparse_reset_state(pool: int, stream: int) -> None:
+    _check(load().hisparse_reset_state(pool, stream))
+
+
+def hisparse_set_fetch_workgroups(pool: int, whole_group: int, per_layer: int) -> None:
+    _check(load().hisparse_set_fetch_workgroups(pool, whole_group, per_layer))
 
 
 def hisparse_export_state(pool: int, r: int, l: int, hot_slots: int, stream: int):
@@ -266,6 +277,12 @@ class HiSparse:
     def step(self, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse) -> None:
         hisparse_step(self.pool, d_step.data_ptr(), d_topk.data_ptr(), d_q.data_ptr(), scale,
                       d_rows.data_ptr(), d_counts.data_ptr(), d_out.data_ptr(), d_lse.data_ptr(), self.stream)
+
+    def reset_state(self) -> None:
+        hisparse_reset_state(self.pool, self.stream)
+
+    def set_fetch_workgroups(self, whole_group: int = 0, per_layer: int = 0) -> None:
+        hisparse_set_fetch_workgroups(self.pool, whole_group, per_layer)
 
     def export_state(self, r: int, l: int):
         return hisparse_export_state(self.pool, r, l, self.cfg["hot_slots"], self.stream)

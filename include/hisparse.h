@@ -139,8 +139,9 @@ hisparse_status hisparse_set_block_table(hisparse_pool* pool, int32_t r, const i
  *   d_topk:   device int32 [R][K] logical positions, -1 = padding, any order.
  *   d_rows:   device int32 [n_layers][R][K] out: row id per entry (-1 for padding).
  *   d_counts: device int32 [n_layers][R][3] out: (resident, hit, miss).
- * Enqueues the metadata kernel (one wavefront per (request, layer)) and the
- * miss fetch (zero-copy 16-byte loads from the host pool into hot rows). */
+ * Enqueues the metadata kernel (one four-wavefront workgroup per (request,
+ * layer)) and one miss fetch over all n_layers (zero-copy 16-byte loads
+ * from the host pool into hot rows), both on `stream`. */
 hisparse_status hisparse_resolve(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers,
                                  const int32_t* d_step, const int32_t* d_topk, int32_t* d_rows,
                                  int32_t* d_counts, void* stream);
@@ -159,10 +160,37 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* pool, int32_t layer, c
 /* One decode step over every layer: for each index-share group, RESOLVE all
  * of its layers with the group's selection, then decode each layer.
  *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],
- *   d_counts [L][R][3], d_out [L][R][H][512], d_lse [L][R][H]. */
+ *   d_counts [L][R][3], d_out [L][R][H][512], d_lse [L][R][H].
+ * Layer-ahead fetch (the shared selection of an index-share group is known
+ * before the group's first layer is decoded; HiSparse summary article,
+ * sections 03-04, on prefetch): after the group's metadata kernel, the miss
+ * fetches run one layer at a time on a stream the pool owns, and the decode
+ * of layer l waits (by event) only for layer l's fetch, so it overlaps the
+ * fetches of the group's later layers (such a layer is decoded without
+ * key splits, on few CUs; the group's last layer is split to fill the
+ * GPU).  `stream` waits for every fetch
+ * before the call's last decode, so work enqueued on `stream` afterwards
+ * sees the whole step; under graph capture the side stream is forked from
+ * and joined back into `stream`.  Row ids, counts and the LRU state are
+ * identical to hisparse_resolve followed by hisparse_sparse_mla_decode per
+ * layer; O and lse agree to rounding (an unsplit layer sums its keys in
+ * another order). */
 hisparse_status hisparse_step(hisparse_pool* pool, const int32_t* d_step, const int32_t* d_topk,
                               const uint16_t* d_q, float scale, int32_t* d_rows, int32_t* d_counts,
                               float* d_out, float* d_lse, void* stream);
+
+/* Return every (request, layer) to the empty state (owner -1, stamp -1,
+ * no step seen); block tables and host rows are kept.  Waits for the
+ * pool's own stream, enqueues memory fills (not graph-capturable) and
+ * synchronises `stream`.  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_reset_state(hisparse_pool* pool, void* stream);
+
+/* Tuning: 1024-thread workgroups launched by the miss fetch.  whole_group
+ * is used by hisparse_resolve (0 = default 256); per_layer by the per-layer
+ * fetches of hisparse_step (0 = default 32), which leave the remaining CUs
+ * to the decode running beside them.  Counts above 65536 or negative:
+ * EINVAL. */
+hisparse_status hisparse_set_fetch_workgroups(hisparse_pool* pool, int32_t whole_group, int32_t per_layer);
 
 /* Copy the LRU state of (request r, layer l) to host arrays of B int32:
  * owner (logical position per slot, -1 empty) and stamp (step of last use,

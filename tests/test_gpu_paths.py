@@ -1,0 +1,184 @@
+"""GPU tests of the step orchestration: the layer-ahead (overlapped) step
+against the synchronous path and the oracle, fetch launch shapes, state
+reset, and replay of a captured step graph."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from tests.gpu_harness import LSE_TOL, O_TOL, check_attention, check_hot_bytes, check_state, log, make_pool
+from oracle.step import OracleDecoder
+from tracegen.populate import queries
+from tracegen.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _grouped_workload():
+    # two index-share groups of three layers, ragged contexts, tail pages resident
+    return make_workload("grouped_l6_g3", 11, 4, 6, 3, [20000, 9000, 33000, 4096], 32, 512, 1024, 6,
+                         0.7, 0.8, "tail")
+
+
+class _Buffers:
+    def __init__(self, w, dev):
+        import torch
+
+        L, R, K, H = w.num_layers, w.num_requests, w.top_k, w.num_heads
+        self.rows = torch.full((L, R, K), -7, dtype=torch.int32, device=dev)
+        self.counts = torch.full((L, R, 3), -7, dtype=torch.int32, device=dev)
+        self.out = torch.full((L, R, H, 512), float("nan"), dtype=torch.float32, device=dev)
+        self.lse = torch.full((L, R, H), float("nan"), dtype=torch.float32, device=dev)
+        self.d_step = torch.zeros(1, dtype=torch.int32, device=dev)
+        G = L // w.index_share
+        self.topk = torch.empty((G, R, K), dtype=torch.int32, device=dev)
+        self.q = torch.empty((L, R, H, 576), dtype=torch.int16, device=dev)
+
+    def load(self, w, t, sel_t):
+        import torch
+
+        self.d_step.fill_(t)
+        self.topk.copy_(torch.from_numpy(np.ascontiguousarray(sel_t, dtype=np.int32)))
+        self.q.copy_(torch.from_numpy(queries(w, t).view(np.int16)))
+
+    def snapshot(self):
+        return tuple(x.cpu().numpy().copy() for x in (self.rows, self.counts, self.out, self.lse))
+
+
+def _run_step_path(hs, w, tr, buf):
+    import torch
+
+    snaps = []
+    for t in range(w.steps):
+        buf.load(w, t, tr[t])
+        hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+        torch.cuda.synchronize(hs.device)
+        snaps.append(buf.snapshot())
+    return snaps
+
+
+def _run_sync_path(hs, w, tr, buf):
+    """hisparse_resolve of each group, then hisparse_sparse_mla_decode per layer."""
+    import torch
+
+    snaps = []
+    g = w.index_share
+    for t in range(w.steps):
+        buf.load(w, t, tr[t])
+        for gi in range(w.num_layers // g):
+            l0 = gi * g
+            hs.resolve(l0, g, buf.d_step, buf.topk[gi], buf.rows[l0:l0 + g], buf.counts[l0:l0 + g])
+            for l in range(l0, l0 + g):
+                hs.decode(l, buf.q[l], buf.rows[l], w.scale, buf.out[l], buf.lse[l])
+        torch.cuda.synchronize(hs.device)
+        snaps.append(buf.snapshot())
+    return snaps
+
+
+def _assert_same(a, b, what, exact_attention=True):
+    """rows and counts bit for bit; O and lse bit for bit, or (when the two
+    runs split the keys differently) within the oracle tolerances."""
+    for t, (x, y) in enumerate(zip(a, b)):
+        for name, u, v in zip(("rows", "counts", "out", "lse"), x, y):
+            if exact_attention or name in ("rows", "counts"):
+                assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"{what}: {name} differs at step {t}"
+            elif name == "out":
+                for l in range(u.shape[0]):
+                    for r in range(u.shape[1]):
+                        den = max(np.abs(u[l, r]).max(), 1e-30)
+                        err = np.abs(u[l, r].astype(np.float64) - v[l, r]).max() / den
+                        assert err <= O_TOL, f"{what}: O l={l} r={r} step {t} rel err {err:.3e}"
+            else:
+                fin = np.isfinite(u)
+                assert np.array_equal(fin, np.isfinite(v)), f"{what}: lse finiteness differs at step {t}"
+                assert np.abs(u[fin].astype(np.float64) - v[fin]).max(initial=0.0) <= LSE_TOL, \
+                    f"{what}: lse differs at step {t}"
+
+
+def test_overlapped_step_matches_oracle_and_sync_path():
+    w = _grouped_workload()
+    tr = w.trace(w.steps)
+    hs = make_pool(w)
+    buf = _Buffers(w, hs.device)
+    log("overlapped step path, default fetch shape")
+    step_snaps = _run_step_path(hs, w, tr, buf)
+
+    # oracle: every step, every (layer, request)
+    dec = OracleDecoder(w)
+    pairs = [(l, r) for l in range(w.num_layers) for r in range(w.num_requests)]
+
+    class _View:
+        pass
+
+    for t in range(w.steps):
+        res = dec.resolve_step(t, tr[t])
+        rows, counts, out, lse = step_snaps[t]
+        for (l, r) in pairs:
+            rr = res[(l, r)]
+            assert np.array_equal(rows[l, r], np.asarray(rr.rows, np.int32)), f"rows t={t} l={l} r={r}"
+            assert tuple(int(x) for x in counts[l, r]) == (rr.n_resident, rr.n_hit, rr.n_miss), \
+                f"counts t={t} l={l} r={r}"
+        v = _View()
+        v.w = w
+        import torch
+
+        v.out = torch.from_numpy(out)
+        v.lse = torch.from_numpy(lse)
+        worst = check_attention(v, dec, t, tr[t], pairs)
+        assert worst <= O_TOL
+    check_state(hs, dec, pairs, w.steps - 1)
+    check_hot_bytes(hs, w, dec, [(0, 0), (2, 3), (5, 2)], w.steps - 1)
+
+    log("synchronous path after reset, odd whole-group fetch grid")
+    hs.reset_state()
+    hs.set_fetch_workgroups(whole_group=7, per_layer=0)
+    sync_snaps = _run_sync_path(hs, w, tr, buf)
+    _assert_same(step_snaps, sync_snaps, "sync path vs overlapped step", exact_attention=False)
+    check_state(hs, dec, pairs, w.steps - 1)
+
+    log("overlapped step path after reset, one workgroup per layer fetch")
+    hs.reset_state()
+    hs.set_fetch_workgroups(whole_group=0, per_layer=1)
+    again = _run_step_path(hs, w, tr, buf)
+    _assert_same(step_snaps, again, "per-layer fetch grid 1 vs default")
+    assert hs.check_errors() == 0
+    hs.close()
+
+
+def test_captured_step_graph_replays():
+    """A captured hisparse_step, replayed once per step with fresh inputs
+    copied in between, matches eager steps of a second pool bit for bit."""
+    import torch
+
+    w = _grouped_workload()
+    tr = w.trace(w.steps)
+    eager = make_pool(w)
+    ebuf = _Buffers(w, eager.device)
+    want = _run_step_path(eager, w, tr, ebuf)
+    eager.close()
+
+    hs = make_pool(w)
+    buf = _Buffers(w, hs.device)
+    side = torch.cuda.Stream(device=hs.device)
+    side.wait_stream(torch.cuda.current_stream(hs.device))
+    graph = torch.cuda.CUDAGraph()
+    buf.load(w, 0, tr[0])
+    torch.cuda.synchronize(hs.device)
+    with torch.cuda.graph(graph, stream=side):
+        hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+    torch.cuda.synchronize(hs.device)
+    # capture enqueues nothing: the state is still empty
+    owner, stamp = hs.export_state(0, 0)
+    assert np.all(owner == -1) and np.all(stamp == -1)
+    for t in range(w.steps):
+        buf.load(w, t, tr[t])
+        torch.cuda.synchronize(hs.device)
+        graph.replay()
+        torch.cuda.synchronize(hs.device)
+        got = buf.snapshot()
+        _assert_same([want[t]], [got], f"graph replay {t}")
+        log(f"graph replay step {t} ok")
+    assert hs.check_errors() == 0
+    del graph
+    hs.close()
