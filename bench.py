@@ -28,6 +28,24 @@ PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, published
 ROW_BYTES = 1152
 
 
+def pmc_bytes(workload: str, kernel: str):
+    """Per-launch bytes of `kernel` from the committed PMC summary of this
+    workload, or None when there is none or the kernel's source changed."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"pmc_bytes_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        e = json.load(f).get("kernels", {}).get(kernel)
+    if not e:
+        return None
+    with open(os.path.join(ROOT, e["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != e["source_sha256_16"]:
+            return None
+    return e
+
+
 def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -115,10 +133,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--fetch-wg", type=int, default=0,
-                    help="workgroups of each per-layer miss fetch in the overlapped step (0 = library default)")
+                    help="workgroups of each pipelined miss fetch of the step (0 = library default)")
+    ap.add_argument("--tail-chunks", type=int, default=0,
+                    help="request chunks of the last layer of a group (0 = library default)")
     ap.add_argument("--no-sync-path", action="store_true",
                     help="skip the replay of the same steps through the synchronous path")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph replay of the same steps")
+    ap.add_argument("--no-decode-only", action="store_true", help="skip the decode-only timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -170,8 +191,7 @@ def main() -> int:
     log("inputs staged in HBM")
 
     stream = torch.cuda.current_stream(dev)
-    if args.fetch_wg:
-        hs.set_fetch_workgroups(0, args.fetch_wg)
+    hs.set_pipeline(0, args.fetch_wg, args.tail_chunks)
 
     def step(t, s=None):
         H.hisparse_step(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(), d_q[t].data_ptr(), w.scale,
@@ -204,6 +224,7 @@ def main() -> int:
         torch.cuda.synchronize(dev)
         return e0.elapsed_time(e1)
 
+    # 1) eager steps; every kernel is bracketed by HIP events on its stream
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize(dev)
@@ -219,28 +240,91 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
-    prof = H.hisparse_profile_read(hs.pool)
+    eager_ms = ev0.elapsed_time(ev1)
+    prof_eager = H.hisparse_profile_read(hs.pool)
     H.hisparse_profile_enable(hs.pool, False)
     flags = hs.check_errors()
     if flags:
         log(f"device error flags {flags:#x}")
         return 1
-    log(f"timed {args.steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.1f} ms)")
-
+    log(f"eager: {args.steps} steps in {eager_ms:.3f} ms (wall {wall * 1e3:.1f} ms)")
     counts = d_counts[args.warmup:].cpu().numpy().astype(np.int64)  # [K][L][R][3]
+
+    # 2) the same steps as captured-graph replays (the timed region of the
+    #    headline), with the kernel events captured into the timed graphs
+    graph_ms, prof_graph = None, None
+    if not args.no_graph:
+        log("captured-graph replay of the same steps")
+        side = torch.cuda.Stream(device=dev)
+        graphs = []
+        hs.reset_state()
+        side.wait_stream(stream)
+        for t in range(n_steps):
+            H.hisparse_profile_enable(hs.pool, t >= args.warmup)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(t, side)
+            graphs.append(g)
+        H.hisparse_profile_enable(hs.pool, False)
+        torch.cuda.synchronize(dev)
+        graph_ms = time_steps(lambda t: graphs[t].replay())
+        try:
+            prof_graph = H.hisparse_profile_read(hs.pool)
+            if not prof_graph or any(not (ms > 0) for _, ms in prof_graph.values()):
+                log(f"kernel events inside graphs gave no usable times: {prof_graph}")
+                prof_graph = None
+        except H.HiSparseError as e:
+            log(f"kernel events inside graphs not readable ({e}); kernel times from the eager pass")
+            prof_graph = None
+        log(f"graph replay: {graph_ms / args.steps * 1e3:.1f} us/step")
+        if not np.array_equal(d_counts[args.warmup:].cpu().numpy(), counts):
+            log("graph replay counts differ from the eager steps")
+            return 1
+        del graphs
+    sync_ms = None
+    if not args.no_sync_path:
+        log("synchronous path (resolve, then per-layer decode, one stream)")
+        sync_ms = time_steps(sync_step)
+        log(f"synchronous path: {sync_ms / args.steps * 1e3:.1f} us/step")
+
+    # 3) decode alone: every layer of the last step, one launch per layer
+    #    (default key splits), over rows that are already resident
+    t_last = n_steps - 1
+    dec_us = None
+    if not args.no_decode_only:
+        dec_reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(dec_reps):
+            for l in range(L):
+                H.hisparse_sparse_mla_decode(hs.pool, l, d_q[t_last, l].data_ptr(), d_rows[t_last, l].data_ptr(),
+                                             w.scale, d_out[l].data_ptr(), d_lse[l].data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        dec_us = e0.elapsed_time(e1) * 1e3 / dec_reps
+    flags = hs.check_errors()
+    if flags:
+        log(f"device error flags {flags:#x} after the replays")
+        return 1
+
+    use_graph = graph_ms is not None
+    ms_total = graph_ms if use_graph else eager_ms
+    prof = prof_graph if prof_graph is not None else prof_eager
     valid = counts.sum(axis=3)  # valid selections per (step, l, r)
     misses = counts[..., 2]
     ms_step = ms_total / args.steps
     tokens_per_s = R * args.steps / (ms_total * 1e-3)
 
-    # algorithmic bytes per step
+    # algorithmic bytes per step (split partials and repeated reads are
+    # overhead, not counted)
     host_bytes = misses.sum(axis=(1, 2)) * ROW_BYTES  # per step
     attn_bytes = (valid.sum(axis=(1, 2)) * ROW_BYTES
                   + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4))
     attn_flops = valid.sum(axis=(1, 2)) * 2 * Hh * (576 + 512)
     meta_bytes = L * R * (2 * 3 * B * 4 + 2 * K * 4 + 12) + misses.sum(axis=(1, 2)) * 8
     hbm_step_bytes = attn_bytes + host_bytes + meta_bytes  # hot-row writes counted once in host_bytes
+    last_valid = valid[-1].sum()
+    dec_bytes = last_valid * ROW_BYTES + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4)
 
     kern = {}
     for name, (n, tot_ms) in prof.items():
@@ -256,43 +340,25 @@ def main() -> int:
             alg = meta_bytes.sum() / n
             bound, peak, unit = "alu", None, "GB/s"
         else:
-            alg = args.steps * L * R * Hh * 4 * (2 * (512 + 4) + 512 + 1) / n
+            alg = None  # split merge: overhead only
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
-        ach = alg / (avg_ms * 1e-3) / 1e9
-        kern[name] = {"launches": n, "avg_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg),
-                      "achieved": round(ach, 2), "bound": bound, "peak": peak, "unit": unit,
-                      "frac": round(ach / peak, 4) if peak else None,
+        ach = alg / (avg_ms * 1e-3) / 1e9 if alg is not None else None
+        kern[name] = {"launches": n, "avg_us": round(avg_ms * 1e3, 2),
+                      "alg_bytes_per_launch": int(alg) if alg is not None else None,
+                      "achieved": round(ach, 2) if ach is not None else None, "bound": bound, "peak": peak,
+                      "unit": unit, "frac": round(ach / peak, 4) if (peak and ach is not None) else None,
                       "busy_share_of_step": round(tot_ms / ms_total, 4)}
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kern[dom]
+    pmc = pmc_bytes(w.name, dom)
+    traffic = None
+    if pmc is not None:
+        # the host-link side of the fetch is what it reads; other kernels: reads + writes
+        traffic = pmc["read_bytes_per_launch"] if d["bound"] == "host_link" else pmc["traffic_bytes_per_launch"]
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
-                "frac": d["frac"], "traffic": None, "kernel": dom, "avg_us": d["avg_us"]}
-
-    graph_ms = None
-    if not args.no_graph:
-        log("captured-graph replay of the same steps")
-        side = torch.cuda.Stream(device=dev)
-        graphs = []
-        hs.reset_state()
-        side.wait_stream(stream)
-        for t in range(n_steps):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                step(t, side)
-            graphs.append(g)
-        torch.cuda.synchronize(dev)
-        graph_ms = time_steps(lambda t: graphs[t].replay())
-        log(f"graph replay: {graph_ms / args.steps * 1e3:.1f} us/step")
-        del graphs
-    sync_ms = None
-    if not args.no_sync_path:
-        log("synchronous path (resolve, then per-layer decode, one stream)")
-        sync_ms = time_steps(sync_step)
-        log(f"synchronous path: {sync_ms / args.steps * 1e3:.1f} us/step")
-    flags = hs.check_errors()
-    if flags:
-        log(f"device error flags {flags:#x} after the replays")
-        return 1
+                "frac": d["frac"], "traffic": traffic, "kernel": dom, "avg_us": d["avg_us"],
+                "alg_bytes_per_launch": d["alg_bytes_per_launch"],
+                "traffic_read_write": [pmc["read_bytes_per_launch"], pmc["write_bytes_per_launch"]] if pmc else None}
 
     probe = None
     if not args.no_probe:
@@ -343,10 +409,16 @@ def main() -> int:
                  "host_GBs": round(float(host_bytes.mean()) / (ms_step * 1e-3) / 1e9, 2),
                  "miss_rate": round(float(misses.sum() / max(valid.sum(), 1)), 4),
                  "attn_gflop": round(float(attn_flops.mean()) / 1e9, 2)},
-        "layer_ahead": {"fetch_wg_per_layer": args.fetch_wg or None,
-                        "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None,
+        "timing": {"timed_region": "graph replays" if use_graph else "eager steps",
+                   "kernel_times_from": "graph replays" if prof_graph is not None else "eager steps",
+                   "eager_us_per_step": round(eager_ms / args.steps * 1e3, 2),
+                   "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
+        "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
                         "sync_path_tokens_per_s": round(R * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
+        "decode_only": {"us_per_step": round(dec_us, 2), "launches": L, "alg_bytes": int(dec_bytes),
+                        "achieved_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 2),
+                        "frac_of_hbm": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)} if dec_us else None,
         "host_link": probe,
         "cpu_baseline": cpu,
     }

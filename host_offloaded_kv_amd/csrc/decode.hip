@@ -392,23 +392,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   }
 }
 
-// Merge the split partials of one (layer, request, head) per wavefront:
-// lane i owns output columns [4i, 4i+4) and [256+4i, 256+4i+4).
+// Merge the split partials of one (layer, request, head) per wavefront.
+// The per-split (m, l, l_exact) triples are read by lanes in parallel and
+// reduced across the wave; the weights go through LDS, and the O rows are
+// then accumulated with the loads of several splits in flight.  Lane i
+// owns output columns [4i, 4i+4) and [256+4i, 256+4i+4).
 constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = kMaxTopK / kT;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) {
-  const int H = a.num_heads;
-  const size_t ph = (size_t)blockIdx.x * (kCombineThreads / 64) + (threadIdx.x >> 6);  // pair * H + head
+  __shared__ float f_s[kCombineThreads / 64][kMaxSplits];
+  const int H = a.num_heads, S = a.splits;
+  const int wv = threadIdx.x >> 6;
+  const size_t ph = (size_t)blockIdx.x * (kCombineThreads / 64) + wv;  // pair * H + head
   const int lane = threadIdx.x & 63;
   const size_t pair = ph / H;
   const int head = (int)(ph % H);
   const size_t sstride = (size_t)H * kPartW;  // floats between splits of one head
-  const float* part0 = a.partial + (pair * a.splits * H + head) * kPartW;
-  float mmax = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) {
+  const float* part0 = a.partial + (pair * S * H + head) * kPartW;
+  float mloc = -INFINITY;
+  for (int s = lane; s < S; s += 64) {
     const float* part = part0 + s * sstride;
-    if (part[kVDim + 1] > 0.f) mmax = fmaxf(mmax, part[kVDim]);
+    if (part[kVDim + 1] > 0.f) mloc = fmaxf(mloc, part[kVDim]);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+  const float mmax = mloc;
   float4* out = reinterpret_cast<float4*>(a.out + ph * kVDim);
   if (mmax == -INFINITY) {
     out[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -417,19 +426,33 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) 
     return;
   }
   float L = 0.f, LE = 0.f;
-  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-  for (int s = 0; s < a.splits; ++s) {
+  for (int s = lane; s < S; s += 64) {
     const float* part = part0 + s * sstride;
     const float ls = part[kVDim + 1];
+    float f = 0.f;
     if (ls > 0.f) {
-      const float f = exp2f(part[kVDim] - mmax);
+      f = exp2f(part[kVDim] - mmax);
       L += ls * f;
       LE += part[kVDim + 2] * f;
-      const float4 x0 = reinterpret_cast<const float4*>(part)[lane];
-      const float4 x1 = reinterpret_cast<const float4*>(part)[64 + lane];
-      o0.x += x0.x * f; o0.y += x0.y * f; o0.z += x0.z * f; o0.w += x0.w * f;
-      o1.x += x1.x * f; o1.y += x1.y * f; o1.z += x1.z * f; o1.w += x1.w * f;
     }
+    f_s[wv][s] = f;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    L += __shfl_xor(L, o, 64);
+    LE += __shfl_xor(LE, o, 64);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+    const float f = f_s[wv][s];
+    const float4* part = reinterpret_cast<const float4*>(part0 + s * sstride);
+    const float4 x0 = part[lane], x1 = part[64 + lane];
+    o0.x += x0.x * f; o0.y += x0.y * f; o0.z += x0.z * f; o0.w += x0.w * f;
+    o1.x += x1.x * f; o1.y += x1.y * f; o1.z += x1.z * f; o1.w += x1.w * f;
   }
   const float inv = 1.f / L;
   out[lane] = make_float4(o0.x * inv, o0.y * inv, o0.z * inv, o0.w * inv);

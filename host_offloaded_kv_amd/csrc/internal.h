@@ -23,17 +23,28 @@ constexpr int kMaxHeads = 256;
 // the GPU; a per-layer fetch of the overlapped step leaves most CUs to the
 // decode running beside it.
 constexpr int kDefaultGroupFetchWorkgroups = 256;
-constexpr int kDefaultLayerFetchWorkgroups = 32;
+constexpr int kDefaultUnitFetchWorkgroups = 32;
+// The last layer of an index-share group can be fetched and decoded in
+// request chunks, so that only the last chunk's decode is exposed; each
+// chunk's decode then pays the per-workgroup cost (Q load, partial write)
+// over fewer key tiles, which on MI355X made 2 or more chunks slower.
+constexpr int kDefaultTailChunks = 1;
+constexpr int kMaxTailChunks = 16;
+constexpr int kMaxIndexShare = 64;
 
 // Per-launch description of the fan-out copy of missed rows.
+// Pair pr of a launch is (layer layer_begin + pr / num_requests, request
+// request_begin + pr % num_requests); its miss list is pr of the arrays.
 struct FetchArgs {
   const int32_t* miss_count;   // [n_pairs]
   const int2* fetch;           // [n_pairs][K] (position, slot)
   const uint64_t* host_rows;   // [L*R] device-visible address of pool rows of (l, r)
   uint16_t* const* kv;         // [L] device pointers of the KV tensors (device array)
   int32_t layer_begin;
-  int32_t n_pairs;             // n_layers * R
-  int32_t num_requests;
+  int32_t n_pairs;             // layers * num_requests
+  int32_t num_requests;        // requests per layer in this launch
+  int32_t request_begin;
+  int32_t total_requests;      // R of the pool
   int32_t top_k;
   int32_t hot_slots;
   int64_t resident_rows;
@@ -59,9 +70,11 @@ struct ResolveArgs {
   int32_t num_requests;
   int32_t top_k;
   int32_t hot_slots;
-  int32_t hash_bits;       // slot hash has 1 << hash_bits entries (>= 2B)
   int32_t page_shift;
   int64_t resident_rows;
+  int16_t* posmap;          // [L][sum ctx] position -> slot (-1: not in the hot buffer)
+  const int64_t* map_off;   // [R] offset of request r within a layer's map
+  int64_t map_layer_stride; // sum of ctx_r
 };
 
 struct DecodeArgs {
@@ -85,8 +98,9 @@ struct DecodeArgs {
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
   size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, host_rows, kv_ptrs, err,
-      partial, total;
+      partial, posmap, map_off, total;
   int64_t bt_entries;
+  int64_t posmap_entries;   // L * sum ctx_r
   int32_t splits_max;      // largest split count any decode launch uses
   int32_t layers_batched;  // layers decoded by one launch in hisparse_step
 };
@@ -118,10 +132,11 @@ struct hisparse_pool {
   std::vector<uint64_t> host_rows_dev;  // [L*R] device-visible addresses
   std::vector<uint16_t*> kv;            // [L]
   int64_t kv_rows = 0;
-  int hash_bits = 0;
   size_t resolve_lds = 0;
   // device views into the workspace
   int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d;
+  int16_t* posmap;
+  int64_t* map_off;
   int2* fetch;
   uint64_t* host_rows_d;
   uint16_t** kv_d;
@@ -131,9 +146,10 @@ struct hisparse_pool {
   // priority) while the caller's stream decodes earlier layers.
   hipStream_t fetch_stream = nullptr;
   hipEvent_t ev_meta = nullptr;
-  std::vector<hipEvent_t> ev_fetch;  // one per layer of an index-share group
-  int fetch_wg_all = hs::kDefaultGroupFetchWorkgroups;  // workgroups of a whole-group fetch
-  int fetch_wg_layer = 0;            // workgroups of a per-layer fetch (0: default)
+  std::vector<hipEvent_t> ev_fetch;  // one per pipelined unit of an index-share group
+  int fetch_wg_all = hs::kDefaultGroupFetchWorkgroups;   // workgroups of a whole-group fetch
+  int fetch_wg_unit = hs::kDefaultUnitFetchWorkgroups;   // workgroups of a pipelined fetch
+  int tail_chunks = hs::kDefaultTailChunks;              // request chunks of a group's last layer
 };
 
 namespace hs {
@@ -145,7 +161,7 @@ void prof_begin(hisparse_pool* p, int kid, hipStream_t s);
 void prof_end(hisparse_pool* p, hipStream_t s);
 
 // resolve.hip
-size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits);
+size_t resolve_lds_bytes(int top_k, int hot_slots);
 hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s);
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);

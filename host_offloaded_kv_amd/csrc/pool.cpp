@@ -8,6 +8,7 @@
 // table whose resident entries are read in place and never evicted.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -35,8 +36,9 @@ hisparse_status check_config(const hisparse_config* c) {
     set_error("config is NULL");
     return HISPARSE_EINVAL;
   }
-  if (c->num_requests < 1 || c->num_layers < 1 || c->index_share < 1 || c->num_layers % c->index_share) {
-    set_error("need num_requests >= 1, num_layers >= 1, index_share >= 1 and num_layers % index_share == 0");
+  if (c->num_requests < 1 || c->num_layers < 1 || c->index_share < 1 || c->index_share > kMaxIndexShare ||
+      c->num_layers % c->index_share) {
+    set_error("need num_requests >= 1, num_layers >= 1, 1 <= index_share <= 64 and num_layers % index_share == 0");
     return HISPARSE_EINVAL;
   }
   if (c->latent_dim != kLatent || c->v_dim != kVDim) {
@@ -95,7 +97,11 @@ Layout make_layout(const hisparse_config* c) {
   const int s1 = decode_splits(1, c->num_requests, c->num_heads, c->top_k);
   const int sg = decode_splits(c->index_share, c->num_requests, c->num_heads, c->top_k);
   L.splits_max = s1 > sg ? s1 : sg;
-  size_t part_1 = s1 > 1 ? (size_t)s1 * R * c->num_heads * kPartW : 0;
+  size_t part_1 = 0;  // one layer, any request count up to R (pipelined chunks)
+  for (size_t nreq = 1; nreq <= R; ++nreq) {
+    const int sn = decode_splits(1, (int)nreq, c->num_heads, c->top_k);
+    if (sn > 1) part_1 = std::max(part_1, (size_t)sn * nreq * c->num_heads * kPartW);
+  }
   size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * c->num_heads * kPartW : 0;
   size_t off = 0;
   L.owner = off; off = align256(off + NL * R * B * 4);
@@ -111,6 +117,11 @@ Layout make_layout(const hisparse_config* c) {
   L.kv_ptrs = off; off = align256(off + NL * 8);
   L.err = off; off = align256(off + 4);
   L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
+  int64_t ctx_sum = 0;
+  for (size_t r = 0; r < R; ++r) ctx_sum += c->ctx_len[r];
+  L.posmap_entries = (int64_t)NL * ctx_sum;
+  L.posmap = off; off = align256(off + (size_t)L.posmap_entries * 2);
+  L.map_off = off; off = align256(off + R * 8);
   L.total = off;
   return L;
 }
@@ -226,10 +237,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     delete p;
     return hip_fail(e, "hipGetDevice");
   }
-  int hb = 1;
-  while ((1 << hb) < 2 * cfg->hot_slots) ++hb;
-  p->hash_bits = hb;
-  p->resolve_lds = resolve_lds_bytes(cfg->top_k, cfg->hot_slots, hb);
+  p->resolve_lds = resolve_lds_bytes(cfg->top_k, cfg->hot_slots);
   int max_lds = 0;
   e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
   if (e != hipSuccess) {
@@ -295,8 +303,16 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->kv_d = (uint16_t**)(w + lay.kv_ptrs);
   p->err = (uint32_t*)(w + lay.err);
   p->partial = (float*)(w + lay.partial);
+  p->posmap = (int16_t*)(w + lay.posmap);
+  p->map_off = (int64_t*)(w + lay.map_off);
 
   std::vector<int32_t> bt_off(R), ctx32(R);
+  std::vector<int64_t> map_off(R);
+  int64_t acc_m = 0;
+  for (int r = 0; r < R; ++r) {
+    map_off[r] = acc_m;
+    acc_m += p->ctx[r];
+  }
   p->n_pages.resize(R);
   int64_t acc = 0;
   for (int r = 0; r < R; ++r) {
@@ -308,6 +324,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   std::vector<uint64_t> kvp(NL);
   for (int l = 0; l < NL; ++l) kvp[l] = (uint64_t)p->kv[l];
   if ((e = hipMemcpyAsync(p->bt_off, bt_off.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(p->map_off, map_off.data(), R * 8, hipMemcpyHostToDevice, s)) != hipSuccess ||
       (e = hipMemcpyAsync(p->ctx_d, ctx32.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
       (e = hipMemcpyAsync(p->host_rows_d, p->host_rows_dev.data(), (size_t)NL * R * 8, hipMemcpyHostToDevice, s)) !=
           hipSuccess ||
@@ -317,7 +334,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     return hip_fail(e, "workspace initialisation");
   }
   // Side stream and events of the overlapped step (default priority).
-  p->ev_fetch.assign(cfg->index_share, nullptr);
+  p->ev_fetch.assign(cfg->index_share - 1 + kMaxTailChunks, nullptr);
   if ((e = hipStreamCreateWithFlags(&p->fetch_stream, hipStreamNonBlocking)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&p->ev_meta, hipEventDisableTiming)) != hipSuccess) {
     hisparse_destroy_pool(p);
@@ -403,27 +420,33 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.num_requests = p->cfg.num_requests;
   a.top_k = p->cfg.top_k;
   a.hot_slots = p->cfg.hot_slots;
-  a.hash_bits = p->hash_bits;
   int ps = 0;
   while ((1 << ps) < p->cfg.page_size) ++ps;
   a.page_shift = ps;
   a.resident_rows = p->cfg.resident_rows_per_layer;
+  a.posmap = p->posmap;
+  a.map_off = p->map_off;
+  a.map_layer_stride = p->lay.posmap_entries / p->cfg.num_layers;
   hipError_t e = launch_meta(p, a, s);
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "resolve metadata launch");
 }
 
-// Miss fetch of layers [layer, layer + n_layers): their miss lists (stored
-// per layer by the metadata kernel) are copied from the host pool.
-hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers, int grid, hipStream_t s) {
+// Miss fetch of requests [r0, r0 + nreq) of layers [layer, layer +
+// n_layers) (nreq < R only with one layer): their miss lists, stored per
+// (layer, request) by the metadata kernel, are copied from the host pool.
+hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers, int32_t r0, int32_t nreq, int grid,
+                              hipStream_t s) {
   const int R = p->cfg.num_requests;
   FetchArgs f;
-  f.miss_count = p->miss_count + (size_t)layer * R;
-  f.fetch = p->fetch + (size_t)layer * R * p->cfg.top_k;
+  f.miss_count = p->miss_count + (size_t)layer * R + r0;
+  f.fetch = p->fetch + ((size_t)layer * R + r0) * p->cfg.top_k;
   f.host_rows = p->host_rows_d;
   f.kv = p->kv_d;
   f.layer_begin = layer;
-  f.n_pairs = n_layers * R;
-  f.num_requests = R;
+  f.n_pairs = n_layers * nreq;
+  f.num_requests = nreq;
+  f.request_begin = r0;
+  f.total_requests = R;
   f.top_k = p->cfg.top_k;
   f.hot_slots = p->cfg.hot_slots;
   f.resident_rows = p->cfg.resident_rows_per_layer;
@@ -431,15 +454,13 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "miss fetch launch");
 }
 
-int layer_fetch_grid(const hisparse_pool* p) {
-  return p->fetch_wg_layer > 0 ? p->fetch_wg_layer : kDefaultLayerFetchWorkgroups;
-}
-
 // splits: key-range splits per (layer, request, head group); 0 picks the
 // count that fills the GPU (decode_splits).
-hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const uint16_t* d_q,
-                               const int32_t* d_rows, float scale, float* d_out, float* d_lse, hipStream_t s,
-                               int splits = 0) {
+// nreq: requests per layer covered by the pointers (a chunk of the pool's
+// requests when decoding one layer piecewise).
+hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, int32_t nreq,
+                               const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out, float* d_lse,
+                               hipStream_t s, int splits = 0) {
   DecodeArgs a;
   a.q = d_q;
   a.rows = d_rows;
@@ -450,10 +471,10 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.err = p->err;
   a.layer_begin = layer_begin;
   a.n_layers = n_layers;
-  a.num_requests = p->cfg.num_requests;
+  a.num_requests = nreq;
   a.num_heads = p->cfg.num_heads;
   a.top_k = p->cfg.top_k;
-  a.splits = splits > 0 ? splits : decode_splits(n_layers, p->cfg.num_requests, p->cfg.num_heads, p->cfg.top_k);
+  a.splits = splits > 0 ? splits : decode_splits(n_layers, nreq, p->cfg.num_heads, p->cfg.top_k);
   a.kv_rows = p->kv_rows;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = launch_decode(p, a, s);
@@ -476,7 +497,7 @@ hisparse_status hisparse_resolve(hisparse_pool* p, int32_t layer_begin, int32_t 
   hipStream_t s = (hipStream_t)stream;
   hisparse_status st = enqueue_resolve(p, layer_begin, n_layers, d_step, d_topk, d_rows, d_counts, s);
   if (st) return st;
-  return enqueue_fetch(p, layer_begin, n_layers, p->fetch_wg_all, s);
+  return enqueue_fetch(p, layer_begin, n_layers, 0, p->cfg.num_requests, p->fetch_wg_all, s);
 }
 
 hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, const uint16_t* d_q,
@@ -498,7 +519,7 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, cons
     set_error("hisparse_sparse_mla_decode: scale must be finite");
     return HISPARSE_EINVAL;
   }
-  return enqueue_decode(p, layer, 1, d_q, d_rows, scale, d_out, d_lse, (hipStream_t)stream);
+  return enqueue_decode(p, layer, 1, p->cfg.num_requests, d_q, d_rows, scale, d_out, d_lse, (hipStream_t)stream);
 }
 
 hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,
@@ -517,31 +538,43 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
   const int G = c.index_share;
   hipStream_t s = (hipStream_t)stream;
   hipStream_t fs = p->fetch_stream;
-  const int grid = layer_fetch_grid(p);
+  const int C = std::min<int>(p->tail_chunks, (int)R);
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
-    // One metadata launch for the whole group (the layers share the
-    // selection), then per-layer fetches on the side stream, so that the
-    // decode of layer l0+i overlaps the fetches of layers l0+i+1 ...
+    // One metadata launch for the whole group (its layers share the
+    // selection).  Then a pipeline of units on two streams: the side stream
+    // fetches unit after unit, the caller's stream decodes unit u as soon
+    // as its fetch is done, overlapping the fetches of the units after it.
+    // Units: each layer but the last, whole; the last layer in C request
+    // chunks, so that only the last chunk's decode is exposed.  A whole
+    // layer decoded under a later fetch runs unsplit (64 CUs or fewer, no
+    // partials); chunks of the last layer are split to fill the GPU.
     hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * K, d_rows + (size_t)l0 * R * K,
                                          d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
     if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
       return hip_fail(e, "hisparse_step: fork");
-    for (int i = 0; i < G; ++i) {
-      if ((st = enqueue_fetch(p, l0 + i, 1, grid, fs))) return st;
-      if ((e = hipEventRecord(p->ev_fetch[i], fs)) != hipSuccess) return hip_fail(e, "hisparse_step: fetch event");
+    struct Unit {
+      int layer, r0, nreq, splits;
+    };
+    Unit units[kMaxIndexShare - 1 + kMaxTailChunks];
+    int nu = 0;
+    for (int i = 0; i + 1 < G; ++i) units[nu++] = {l0 + i, 0, (int)R, 1};
+    for (int ch = 0; ch < C; ++ch) {
+      const int r0 = (int)(R * ch / C), r1 = (int)(R * (ch + 1) / C);
+      units[nu++] = {l0 + G - 1, r0, r1 - r0, 0};
     }
-    for (int i = 0; i < G; ++i) {
-      const int l = l0 + i;
-      if ((e = hipStreamWaitEvent(s, p->ev_fetch[i], 0)) != hipSuccess) return hip_fail(e, "hisparse_step: join");
-      // A layer decoded while a later layer's fetch is still streaming only
-      // has to finish before that fetch does: it runs unsplit (fewer CUs, no
-      // partials).  The group's last layer is exposed and is split to fill
-      // the GPU.
-      st = enqueue_decode(p, l, 1, d_q + (size_t)l * R * H * kLatent, d_rows + (size_t)l * R * K, scale,
-                          d_out + (size_t)l * R * H * kVDim, d_lse + (size_t)l * R * H, s, i + 1 < G ? 1 : 0);
+    for (int u = 0; u < nu; ++u) {
+      if ((st = enqueue_fetch(p, units[u].layer, 1, units[u].r0, units[u].nreq, p->fetch_wg_unit, fs))) return st;
+      if ((e = hipEventRecord(p->ev_fetch[u], fs)) != hipSuccess) return hip_fail(e, "hisparse_step: fetch event");
+    }
+    for (int u = 0; u < nu; ++u) {
+      const Unit& un = units[u];
+      const size_t pr = (size_t)un.layer * R + un.r0;  // first (layer, request) of the unit
+      if ((e = hipStreamWaitEvent(s, p->ev_fetch[u], 0)) != hipSuccess) return hip_fail(e, "hisparse_step: join");
+      st = enqueue_decode(p, un.layer, 1, un.nreq, d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                          d_out + pr * H * kVDim, d_lse + pr * H, s, un.splits);
       if (st) return st;
     }
   }
@@ -560,13 +593,16 @@ hisparse_status hisparse_reset_state(hisparse_pool* p, void* stream) {
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_reset_state");
 }
 
-hisparse_status hisparse_set_fetch_workgroups(hisparse_pool* p, int32_t whole_group, int32_t per_layer) {
-  if (!p || whole_group < 0 || per_layer < 0 || whole_group > 65536 || per_layer > 65536) {
-    set_error("hisparse_set_fetch_workgroups: bad argument");
+hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_workgroups,
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks) {
+  if (!p || group_fetch_workgroups < 0 || group_fetch_workgroups > 65536 || unit_fetch_workgroups < 0 ||
+      unit_fetch_workgroups > 65536 || tail_chunks < 0 || tail_chunks > kMaxTailChunks) {
+    set_error("hisparse_set_pipeline: bad argument");
     return HISPARSE_EINVAL;
   }
-  p->fetch_wg_all = whole_group > 0 ? whole_group : kDefaultGroupFetchWorkgroups;
-  p->fetch_wg_layer = per_layer;
+  p->fetch_wg_all = group_fetch_workgroups > 0 ? group_fetch_workgroups : kDefaultGroupFetchWorkgroups;
+  p->fetch_wg_unit = unit_fetch_workgroups > 0 ? unit_fetch_workgroups : kDefaultUnitFetchWorkgroups;
+  p->tail_chunks = tail_chunks > 0 ? tail_chunks : kDefaultTailChunks;
   return HISPARSE_OK;
 }
 
@@ -615,9 +651,7 @@ hisparse_status hisparse_profile_enable(hisparse_pool* p, int32_t enable) {
       if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
     }
   }
-  pr.on = enable != 0;
-  pr.n = 0;
-  pr.overflow = false;
+  pr.on = enable != 0;  // launches recorded so far are kept until the next read
   return HISPARSE_OK;
 }
 

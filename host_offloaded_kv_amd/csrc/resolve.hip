@@ -10,16 +10,16 @@
 // slot, nothing on the decode path waits for the CPU).
 //
 // Design on CDNA4:
-//  * resolve_meta: one 4-wavefront workgroup per (request, layer).  The
-//    slot owner, stamp and LRU-order arrays and the position->slot page
-//    table (an open-addressing hash rebuilt from the owner array on every
-//    call) live in LDS.  Misses are compacted with wavefront ballots in
-//    ascending position order; victims are the first unpinned slots of a
-//    persistent array that lists all slots in ascending (stamp, slot) order,
-//    so victim choice is a ballot scan with no sort.  After the fills the
-//    order array is rebuilt as [untouched slots with stamp < t, in old
-//    order] ++ [slots with stamp == t, by slot index], which keeps it
-//    sorted.  Only the owner and stamp entries that change are written back.
+//  * resolve_meta: one 16-wavefront workgroup per (request, layer).  The
+//    position->slot page table is a persistent int16 map per (layer,
+//    request) in device memory; the selection and the pin flags live in
+//    LDS.  Misses are compacted with wavefront ballots in ascending position
+//    order; victims are the first unpinned slots of a persistent array that
+//    lists all slots in ascending (stamp, slot) order, so victim choice is a
+//    ballot scan with no sort.  After the fills the order array is rebuilt
+//    as [untouched slots with stamp < t, in old order] ++ [slots with stamp
+//    == t, by slot index], which keeps it sorted.  Only the owner, stamp and
+//    map entries that change are written.
 //  * fetch_rows: a fan-out copy over the whole GPU.  Each workgroup scans
 //    the per-(request, layer) miss counts in LDS, then the grid walks a flat
 //    index of 16-byte chunks over every missed row (72 chunks per 1152-byte
@@ -32,10 +32,6 @@
 
 namespace hs {
 namespace {
-
-__device__ __forceinline__ uint32_t hash_pos(int32_t p, int bits) {
-  return ((uint32_t)p * 0x9E3779B1u) >> (32 - bits);
-}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
@@ -62,36 +58,37 @@ int ceil_log2(int64_t v) {
   return b;
 }
 
-constexpr int kMetaThreads = 256;  // 4 wavefronts per (request, layer)
+constexpr int kMetaThreads = 1024;  // 16 wavefronts per (request, layer)
 constexpr int kMetaWaves = kMetaThreads / 64;
+constexpr int kSelChunks = kMaxTopK / kMetaThreads;       // 64-entry chunks of the selection per wave (max)
+constexpr int kSlotChunks = kMaxHotSlots / kMetaThreads;  // 64-entry chunks of the order array per wave (max)
 
 struct LdsMap {
-  size_t owner, stamp, lru, sel, mpos, mj, vic, btv, flag, missf, region, total;
+  size_t sel, mpos, mj, vic, tflag, region, total;
 };
 
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-__host__ __device__ inline LdsMap lds_map(int K, int B, int hash_bits, int seen_bits) {
+__host__ __device__ inline int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+__host__ __device__ inline LdsMap lds_map(int K, int B) {
   LdsMap m;
-  m.owner = 0;
-  m.stamp = m.owner + 4 * (size_t)B;
-  m.lru = m.stamp + 4 * (size_t)B;
-  m.sel = m.lru + 4 * (size_t)B;
+  m.sel = 0;
   m.mpos = m.sel + 4 * (size_t)K;
   m.mj = m.mpos + 4 * (size_t)K;
   m.vic = m.mj + 4 * (size_t)K;
-  m.btv = m.vic + 4 * (size_t)K;
-  m.flag = round16(m.btv + 4 * (size_t)K);
-  m.missf = m.flag + round16((size_t)B);
-  m.region = m.missf + round16((size_t)K);
-  const size_t hash_bytes = (size_t)4 << hash_bits;
-  const size_t seen_bytes = (size_t)8 << seen_bits;  // also holds the miss sort (<= K entries)
-  m.total = m.region + (hash_bytes > seen_bytes ? hash_bytes : seen_bytes);
+  m.tflag = m.vic + 4 * (size_t)K;
+  m.region = m.tflag + round16((size_t)B);
+  m.total = m.region + 8 * (size_t)next_pow2(K);  // (position, index) sort keys, slow path only
   return m;
 }
 
 // Direct-to-LDS copy of n int32 by one workgroup: wave w issues chunks
-// w, w+4, ... of 64 dwords; lanes past n are masked off.
+// w, w+16, ... of 64 dwords; lanes past n are masked off.
 __device__ __forceinline__ void g2l_block(int32_t* lds, const int32_t* g, int n, int wid, int lane) {
   for (int c = wid * 64; c < n; c += kMetaThreads)
     if (c + lane < n) __builtin_amdgcn_global_load_lds(g + c + lane, (lds_void*)(lds + c), 4, 0, 0);
@@ -110,30 +107,50 @@ __device__ __forceinline__ int wave_base(const int* cnt, int wid, int* total) {
   return base;
 }
 
-// One workgroup (4 wavefronts) per (request, layer).  Element-wise passes
-// are split over all 256 threads; the order-preserving compactions (the
-// miss list in ascending position, the victims in (stamp, slot) order, the
-// rebuilt order array) give each wave a contiguous quarter of the input,
-// count with ballots, exchange the four counts through LDS and then write
-// at base + ballot prefix.
-__global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int seen_bits) {
+// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by the
+// whole workgroup.
+__device__ void bitonic_sort(unsigned long long* k, int n, int tid) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n; i += kMetaThreads) {
+        const int ixj = i ^ stride;
+        if (ixj > i) {
+          const unsigned long long x = k[i], y = k[ixj];
+          if ((x > y) == ((i & size) == 0)) {
+            k[i] = y;
+            k[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// One workgroup (16 wavefronts) per (request, layer).
+//  * The position -> slot page table is a persistent int16 map over the
+//    request's positions in device memory (exact: map[p] = s iff owner[s] =
+//    p), so a lookup is one gather and a fill changes two entries.
+//  * Pinning is a byte per slot in LDS (bit 0: hit or filled by this call;
+//    bit 1: already stamped with this step by an earlier call of the same
+//    step).  Stamps themselves are only written, except on that rare path.
+//  * Order-preserving compactions (misses in input order, victims in order
+//    array order, the rebuilt order array) give each wave a contiguous range,
+//    keep its ballots in registers, exchange the sixteen counts through LDS
+//    and write at base + ballot prefix.  The order array is read once into
+//    registers and rewritten at the end.
+__global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int cnt_s[2][kMetaWaves];
   __shared__ int red_s[2][kMetaWaves];
   const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
-  const LdsMap M = lds_map(K, B, a.hash_bits, seen_bits);
-  int32_t* owner_s = (int32_t*)(smem + M.owner);
-  int32_t* stamp_s = (int32_t*)(smem + M.stamp);
-  int32_t* lru_s = (int32_t*)(smem + M.lru);
+  const LdsMap M = lds_map(K, B);
   int32_t* sel_s = (int32_t*)(smem + M.sel);
   int32_t* mpos_s = (int32_t*)(smem + M.mpos);
   int32_t* mj_s = (int32_t*)(smem + M.mj);
   int32_t* vic_s = (int32_t*)(smem + M.vic);
-  int32_t* btv_s = (int32_t*)(smem + M.btv);
-  unsigned char* flag_s = smem + M.flag;
-  unsigned char* missf_s = smem + M.missf;
-  int32_t* hash_s = (int32_t*)(smem + M.region);
-  unsigned long long* kv64_s = (unsigned long long*)(smem + M.region);
+  unsigned char* tflag_s = smem + M.tflag;
+  unsigned long long* key_s = (unsigned long long*)(smem + M.region);
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,12 +164,13 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int 
   int32_t* rows_out = a.rows + cpair * K;
   const int32_t* topk = a.topk + (size_t)r * K;
   const int t = *a.step;
+  const int last = a.last_t[pair];
   const int ctx = a.ctx[r];
   const int64_t hot_base = a.resident_rows + (int64_t)r * B;
   const int page_shift = a.page_shift;
   const int page_mask = (1 << page_shift) - 1;
 
-  if (t < 0 || t < a.last_t[pair]) {
+  if (t < 0 || t < last) {
     for (int j = tid; j < K; j += kMetaThreads) rows_out[j] = -1;
     if (tid == 0) {
       a.counts[cpair * 3 + 0] = 0;
@@ -163,17 +181,35 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int 
     }
     return;
   }
+  const bool same_step = t == last;
 
   int32_t* owner_g = a.owner + pair * B;
   int32_t* stamp_g = a.stamp + pair * B;
   int32_t* lru_g = a.lru + pair * B;
-  // State and selection arrive together through direct-to-LDS loads.
-  g2l_block(owner_s, owner_g, B, wid, lane);
-  g2l_block(stamp_s, stamp_g, B, wid, lane);
-  g2l_block(lru_s, lru_g, B, wid, lane);
+  int16_t* map = a.posmap + (size_t)l * a.map_layer_stride + a.map_off[r];
+
+  // Wave ranges: selection entries [jb, je), order-array entries [ib, ie).
+  const int Kq = (K + kMetaThreads - 1) / kMetaThreads * 64;
+  const int jb = wid * Kq, je = min(K, jb + Kq);
+  const int njc = Kq / 64;
+  const int Bq = (B + kMetaThreads - 1) / kMetaThreads * 64;
+  const int ib = wid * Bq, ie = min(B, ib + Bq);
+  const int nsc = Bq / 64;
+
   g2l_block(sel_s, topk, K, wid, lane);
-  for (int i = tid; i < (int)(round16(B) / 4); i += kMetaThreads) ((uint32_t*)flag_s)[i] = 0u;
+  int lv[kSlotChunks];  // order-array entries of this wave
+#pragma unroll
+  for (int c = 0; c < kSlotChunks; ++c) {
+    const int i = ib + 64 * c + lane;
+    lv[c] = (c < nsc && i < ie) ? lru_g[i] : 0;
+  }
+  for (int i = tid; i < (int)(round16(B) / 4); i += kMetaThreads) ((uint32_t*)tflag_s)[i] = 0u;
   wait_vmem_and_sync();
+  if (same_step) {
+    for (int s = tid; s < B; s += kMetaThreads)
+      if (stamp_g[s] == t) tflag_s[s] = 2;
+    __syncthreads();
+  }
 
   // Selection: validate the range; note whether it is strictly ascending
   // with padding only at the end (then it has no repeats and its misses
@@ -194,239 +230,169 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a, int 
     if (!(k0 < k1 || (k0 == INT_MAX && k1 == INT_MAX))) bad = true;
   }
   const bool fast = __syncthreads_or(bad) == 0;
-  // Block-table entry of every selected page, gathered straight into LDS.
-  const int32_t* bt = a.bt + a.bt_off[r];
-  for (int c = wid * 64; c < K; c += kMetaThreads) {
-    const int j = c + lane;
-    if (j < K) {
-      const int p = sel_s[j];
-      __builtin_amdgcn_global_load_lds(bt + (p >= 0 ? (p >> page_shift) : 0), (lds_void*)(btv_s + c), 4, 0, 0);
-    }
-  }
+  const int KP = next_pow2(K);
 
   if (!fast) {
-    // Repeated positions: keep the earliest entry (smallest j) of each.
-    const int ES = 1 << seen_bits;
-    for (int i = tid; i < ES; i += kMetaThreads) kv64_s[i] = ~0ull;
-    __syncthreads();
-    for (int j = tid; j < K; j += kMetaThreads) {
-      const int p = sel_s[j];
-      if (p < 0) continue;
-      const unsigned long long ent = ((unsigned long long)(uint32_t)p << 32) | (uint32_t)j;
-      uint32_t h = hash_pos(p, seen_bits);
-      while (true) {
-        const unsigned long long old = atomicCAS(&kv64_s[h], ~0ull, ent);
-        if (old == ~0ull) break;
-        if ((uint32_t)(old >> 32) == (uint32_t)p) {
-          atomicMin(&kv64_s[h], ent);
-          break;
-        }
-        h = (h + 1) & (ES - 1);
-      }
+    // Repeated positions: sort (position, index) and keep the earliest
+    // index of each position.
+    for (int i = tid; i < KP; i += kMetaThreads) {
+      const int p = i < K ? sel_s[i] : -1;
+      key_s[i] = p >= 0 ? (((unsigned long long)(uint32_t)p << 32) | (uint32_t)i) : ~0ull;
     }
     __syncthreads();
-    for (int j = tid; j < K; j += kMetaThreads) {
-      const int p = sel_s[j];
-      if (p < 0) continue;
-      uint32_t h = hash_pos(p, seen_bits);
-      while ((uint32_t)(kv64_s[h] >> 32) != (uint32_t)p) h = (h + 1) & (ES - 1);
-      if ((uint32_t)kv64_s[h] != (uint32_t)j) {
-        sel_s[j] = -1;
+    bitonic_sort(key_s, KP, tid);
+    for (int i = tid + 1; i < KP; i += kMetaThreads) {
+      const unsigned long long x = key_s[i];
+      if (x != ~0ull && (x >> 32) == (key_s[i - 1] >> 32)) {
+        sel_s[(uint32_t)x] = -1;
         errbits |= HISPARSE_ERR_DUP;
       }
     }
     __syncthreads();
   }
 
-  // Page table: position -> slot, rebuilt from the owner array.
-  const int HS = 1 << a.hash_bits;
-  for (int i = tid; i < HS; i += kMetaThreads) hash_s[i] = -1;
-  __syncthreads();
-  for (int s0 = 0; s0 < B; s0 += 4 * kMetaThreads) {
-    // four inserts per thread in flight at once
-    int sl[4];
-    uint32_t h[4];
-    bool pend[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sl[u] = s0 + kMetaThreads * u + tid;
-      const int p = sl[u] < B ? owner_s[sl[u]] : -1;
-      pend[u] = p >= 0;
-      h[u] = pend[u] ? hash_pos(p, a.hash_bits) : 0u;
-    }
-    while (pend[0] || pend[1] || pend[2] || pend[3]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pend[u]) {
-          if (atomicCAS(&hash_s[h[u]], -1, sl[u]) == -1) pend[u] = false;
-          else h[u] = (h[u] + 1) & (HS - 1);
-        }
-      }
-    }
-  }
-  wait_vmem_and_sync();  // also completes the block-table gather
-
   // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
-  // Wave w takes entries [w Kq, (w+1) Kq), so wave order is input order.
-  const int Kq = (K + kMetaThreads - 1) / kMetaThreads * 64;
-  const int jb = wid * Kq, je = min(K, jb + Kq);
+  const int32_t* bt = a.bt + a.bt_off[r];
+  int pv[kSelChunks], bv[kSelChunks], sv[kSelChunks];
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c) {
+    const int j = jb + 64 * c + lane;
+    const int p = (c < njc && j < je) ? sel_s[j] : -1;
+    pv[c] = p;
+    bv[c] = p >= 0 ? bt[p >> page_shift] : -1;
+    sv[c] = p >= 0 ? (int)map[p] : -1;
+  }
   int n_res = 0, n_hit = 0, mloc = 0;
-  for (int j0 = jb; j0 < je; j0 += 64) {
-    const int j = j0 + lane;
+  uint64_t mb[kSelChunks];
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c) {
+    const int j = jb + 64 * c + lane;
+    const int p = pv[c];
     bool miss = false;
-    if (j < je) {
-      const int p = sel_s[j];
+    if (c < njc && j < je) {
       int row = -1;
       if (p >= 0) {
-        const int blk = btv_s[j];
-        if (blk >= 0) {
-          row = (blk << page_shift) + (p & page_mask);
+        if (bv[c] >= 0) {
+          row = (bv[c] << page_shift) + (p & page_mask);
           ++n_res;
+        } else if (sv[c] >= 0) {
+          const int s = sv[c];
+          tflag_s[s] |= 1;
+          stamp_g[s] = t;
+          row = (int)(hot_base + s);
+          ++n_hit;
         } else {
-          uint32_t h = hash_pos(p, a.hash_bits);
-          int s;
-          while ((s = hash_s[h]) >= 0 && owner_s[s] != p) h = (h + 1) & (HS - 1);
-          if (s >= 0) {
-            stamp_s[s] = t;
-            stamp_g[s] = t;
-            flag_s[s] = 1;
-            row = (int)(hot_base + s);
-            ++n_hit;
-          } else {
-            miss = true;
-          }
+          miss = true;
         }
       }
       if (!miss) rows_out[j] = row;
-      missf_s[j] = miss ? 1 : 0;
     }
-    mloc += __popcll(__ballot(miss));
+    mb[c] = __ballot(miss);
+    mloc += __popcll(mb[c]);
   }
   if (lane == 0) cnt_s[0][wid] = mloc;
   __syncthreads();
   int m;
   {
     int run = wave_base(cnt_s[0], wid, &m);
-    for (int j0 = jb; j0 < je; j0 += 64) {
-      const int j = j0 + lane;
-      const bool miss = j < je && missf_s[j];
-      const uint64_t bm = __ballot(miss);
-      if (miss) {
-        const int idx = run + __popcll(bm & lt);
-        mpos_s[idx] = sel_s[j];
-        mj_s[idx] = j;
+#pragma unroll
+    for (int c = 0; c < kSelChunks; ++c) {
+      if ((mb[c] >> lane) & 1) {
+        const int idx = run + __popcll(mb[c] & lt);
+        mpos_s[idx] = pv[c];
+        mj_s[idx] = jb + 64 * c + lane;
       }
-      run += __popcll(bm);
+      run += __popcll(mb[c]);
     }
   }
   __syncthreads();
 
   if (!fast && m > 1) {
-    // Ascending position order of the misses: bitonic sort of (pos, j).
-    int mp = 1;
-    while (mp < m) mp <<= 1;
+    // Ascending position order of the misses.
+    const int mp = next_pow2(m);
     for (int i = tid; i < mp; i += kMetaThreads)
-      kv64_s[i] = i < m ? (((unsigned long long)(uint32_t)mpos_s[i] << 32) | (uint32_t)mj_s[i]) : ~0ull;
+      key_s[i] = i < m ? (((unsigned long long)(uint32_t)mpos_s[i] << 32) | (uint32_t)mj_s[i]) : ~0ull;
     __syncthreads();
-    for (int k = 2; k <= mp; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < mp; i += kMetaThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const unsigned long long x = kv64_s[i], y = kv64_s[ixj];
-            const bool up = (i & k) == 0;
-            if ((x > y) == up) {
-              kv64_s[i] = y;
-              kv64_s[ixj] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+    bitonic_sort(key_s, mp, tid);
     for (int i = tid; i < m; i += kMetaThreads) {
-      mpos_s[i] = (int)(kv64_s[i] >> 32);
-      mj_s[i] = (int)(uint32_t)kv64_s[i];
+      mpos_s[i] = (int)(key_s[i] >> 32);
+      mj_s[i] = (int)(uint32_t)key_s[i];
     }
     __syncthreads();
   }
 
   // Victims: the first m unpinned slots of the (stamp, slot) order array.
-  // Wave w scans entries [w Bq, (w+1) Bq) of the array.
-  const int Bq = (B + kMetaThreads - 1) / kMetaThreads * 64;
-  const int ib = wid * Bq, ie = min(B, ib + Bq);
   {
+    uint64_t vb[kSlotChunks];
     int uloc = 0;
-    for (int i0 = ib; i0 < ie; i0 += 64) {
-      const int i = i0 + lane;
-      const bool cand = i < ie && flag_s[lru_s[i]] == 0;
-      uloc += __popcll(__ballot(cand));
+#pragma unroll
+    for (int c = 0; c < kSlotChunks; ++c) {
+      const int i = ib + 64 * c + lane;
+      const bool cand = c < nsc && i < ie && (tflag_s[lv[c]] & 1) == 0;
+      vb[c] = __ballot(cand);
+      uloc += __popcll(vb[c]);
     }
     if (lane == 0) cnt_s[1][wid] = uloc;
-  }
-  __syncthreads();
-  {
+    __syncthreads();
     int unpinned;
     int run = wave_base(cnt_s[1], wid, &unpinned);
-    for (int i0 = ib; i0 < ie && run < m; i0 += 64) {
-      const int i = i0 + lane;
-      const int s = i < ie ? lru_s[i] : 0;
-      const bool cand = i < ie && flag_s[s] == 0;
-      const uint64_t bm = __ballot(cand);
-      if (cand) {
-        const int rank = run + __popcll(bm & lt);
-        if (rank < m) vic_s[rank] = s;
+#pragma unroll
+    for (int c = 0; c < kSlotChunks; ++c) {
+      if ((vb[c] >> lane) & 1) {
+        const int rank = run + __popcll(vb[c] & lt);
+        if (rank < m) vic_s[rank] = lv[c];
       }
-      run += __popcll(bm);
+      run += __popcll(vb[c]);
     }
   }
   __syncthreads();
 
-  // Fill: i-th smallest missing position -> i-th victim.
+  // Fill: i-th smallest missing position -> i-th victim.  The evicted
+  // position cannot be in this selection (its slot would be pinned), so the
+  // map entries cleared and set here are all distinct.
   int2* fetch = a.fetch + cpair * K;
   for (int i = tid; i < m; i += kMetaThreads) {
     const int v = vic_s[i], p = mpos_s[i], j = mj_s[i];
-    owner_s[v] = p;
-    stamp_s[v] = t;
-    flag_s[v] = 1;
+    const int old = owner_g[v];
+    if (old >= 0) map[old] = -1;
+    map[p] = (int16_t)v;
     owner_g[v] = p;
     stamp_g[v] = t;
+    tflag_s[v] |= 1;
     rows_out[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
   __syncthreads();
 
-  // New order: untouched slots older than t (old order), then every slot
-  // stamped t, by slot index.  Both parts are counted in one pass.
+  // New order: slots with stamp < t (untouched; old order), then every slot
+  // stamped t, by slot index.
   {
+    uint64_t ka[kSlotChunks], kb[kSlotChunks];
     int ca = 0, cb = 0;
-    for (int i0 = ib; i0 < ie; i0 += 64) {
-      const int i = i0 + lane;
-      const bool keep = i < ie && stamp_s[lru_s[i]] < t;
-      const bool inB = i < ie && stamp_s[i] == t;
-      ca += __popcll(__ballot(keep));
-      cb += __popcll(__ballot(inB));
+#pragma unroll
+    for (int c = 0; c < kSlotChunks; ++c) {
+      const int i = ib + 64 * c + lane;
+      const bool in = c < nsc && i < ie;
+      ka[c] = __ballot(in && tflag_s[lv[c]] == 0);
+      kb[c] = __ballot(in && tflag_s[i] != 0);
+      ca += __popcll(ka[c]);
+      cb += __popcll(kb[c]);
     }
     if (lane == 0) {
       cnt_s[0][wid] = ca;
       cnt_s[1][wid] = cb;
     }
-  }
-  __syncthreads();
-  {
+    __syncthreads();
     int nA, nB;
     int ra = wave_base(cnt_s[0], wid, &nA);
     int rb = nA + wave_base(cnt_s[1], wid, &nB);
-    for (int i0 = ib; i0 < ie; i0 += 64) {
-      const int i = i0 + lane;
-      const int s = i < ie ? lru_s[i] : 0;
-      const bool keep = i < ie && stamp_s[s] < t;
-      const bool inB = i < ie && stamp_s[i] == t;
-      const uint64_t ba = __ballot(keep), bb = __ballot(inB);
-      if (keep) lru_g[ra + __popcll(ba & lt)] = s;
-      if (inB) lru_g[rb + __popcll(bb & lt)] = i;
-      ra += __popcll(ba);
-      rb += __popcll(bb);
+#pragma unroll
+    for (int c = 0; c < kSlotChunks; ++c) {
+      const int i = ib + 64 * c + lane;
+      if ((ka[c] >> lane) & 1) lru_g[ra + __popcll(ka[c] & lt)] = lv[c];
+      if ((kb[c] >> lane) & 1) lru_g[rb + __popcll(kb[c] & lt)] = i;
+      ra += __popcll(ka[c]);
+      rb += __popcll(kb[c]);
     }
   }
 
@@ -488,7 +454,7 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
   if (tid == kFetchThreads - 1) pre_s[n] = acc;
   __syncthreads();
   const int64_t total_chunks = (int64_t)pre_s[n] * kRowChunks;
-  const int R = a.num_requests;
+  const int R = a.num_requests, RT = a.total_requests;
 
   for (int64_t base = (int64_t)blockIdx.x * kFetchThreads * kFetchUnroll; base < total_chunks;
        base += (int64_t)gridDim.x * kFetchThreads * kFetchUnroll) {
@@ -510,11 +476,11 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
         const int i = gi - pre_s[pr];
         const int2 e = a.fetch[(size_t)pr * a.top_k + i];
         const int li = pr / R;
-        const int r = pr - li * R;
+        const int r = a.request_begin + (pr - li * R);
         const int l = a.layer_begin + li;
         if ((unsigned)e.y < (unsigned)a.hot_slots && e.x >= 0 && e.x < ctx[r]) {
           const u32x4* src = reinterpret_cast<const u32x4*>(
-              reinterpret_cast<const char*>(a.host_rows[(size_t)l * R + r]) + (size_t)e.x * kRowBytes) + c;
+              reinterpret_cast<const char*>(a.host_rows[(size_t)l * RT + r]) + (size_t)e.x * kRowBytes) + c;
           const int64_t row = a.resident_rows + (int64_t)r * a.hot_slots + e.y;
           dst[u] = reinterpret_cast<u32x4*>(a.kv[l] + row * kLatent) + c;
           v[u] = __builtin_nontemporal_load(src);
@@ -553,9 +519,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy16(u32x4* __restrict__ dst, 
 
 }  // namespace
 
-size_t resolve_lds_bytes(int top_k, int hot_slots, int hash_bits) {
-  return lds_map(top_k, hot_slots, hash_bits, ceil_log2(2 * (int64_t)top_k)).total;
-}
+size_t resolve_lds_bytes(int top_k, int hot_slots) { return lds_map(top_k, hot_slots).total; }
 
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   const auto& c = p->cfg;
@@ -565,6 +529,7 @@ hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   if ((e = hipMemsetAsync(p->stamp, 0xFF, pairs * c.hot_slots * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->last_t, 0xFF, pairs * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->miss_count, 0, pairs * 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->posmap, 0xFF, p->lay.posmap_entries * 2, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(iota_lru, dim3(1024), dim3(256), 0, s, p->lru, pairs, c.hot_slots);
   return hipGetLastError();
 }
@@ -577,10 +542,9 @@ hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
 }
 
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
-  const int seen_bits = ceil_log2(2 * (int64_t)a.top_k);
-  const size_t lds = lds_map(a.top_k, a.hot_slots, a.hash_bits, seen_bits).total;
+  const size_t lds = lds_map(a.top_k, a.hot_slots).total;
   prof_begin(p, kKMeta, s);
-  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(kMetaThreads), lds, s, a, seen_bits);
+  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(kMetaThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   return e;

@@ -33,7 +33,7 @@ EXPORTED = (
     "hisparse_last_error", "hisparse_workspace_bytes", "hisparse_kv_rows_per_layer",
     "hisparse_create_pool", "hisparse_destroy_pool", "hisparse_host_rows",
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
-    "hisparse_step", "hisparse_reset_state", "hisparse_set_fetch_workgroups",
+    "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_export_state", "hisparse_check_errors",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
     "hisparse_profile_enable", "hisparse_profile_read",
@@ -74,6 +74,12 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    try:
+        # torch carries its own HIP runtime; load it first so that the
+        # library binds to the same runtime instance as torch's tensors.
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     sigs = {
         "hisparse_last_error": (ctypes.c_char_p, []),
@@ -88,7 +94,7 @@ def load() -> ctypes.CDLL:
         "hisparse_sparse_mla_decode": (_I32, [_VP, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
-        "hisparse_set_fetch_workgroups": (_I32, [_VP, _I32, _I32]),
+        "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
         "hisparse_export_state": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
         "hisparse_check_errors": (_I32, [_VP, _VP, ctypes.POINTER(ctypes.c_uint32)]),
         "hisparse_host_alloc": (_I32, [ctypes.c_size_t, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP)]),
@@ -180,8 +186,9 @@ def hisparse_reset_state(pool: int, stream: int) -> None:
     _check(load().hisparse_reset_state(pool, stream))
 
 
-def hisparse_set_fetch_workgroups(pool: int, whole_group: int, per_layer: int) -> None:
-    _check(load().hisparse_set_fetch_workgroups(pool, whole_group, per_layer))
+def hisparse_set_pipeline(pool: int, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
+                          tail_chunks: int = 0) -> None:
+    _check(load().hisparse_set_pipeline(pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks))
 
 
 def hisparse_export_state(pool: int, r: int, l: int, hot_slots: int, stream: int):
@@ -281,8 +288,9 @@ class HiSparse:
     def reset_state(self) -> None:
         hisparse_reset_state(self.pool, self.stream)
 
-    def set_fetch_workgroups(self, whole_group: int = 0, per_layer: int = 0) -> None:
-        hisparse_set_fetch_workgroups(self.pool, whole_group, per_layer)
+    def set_pipeline(self, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
+                     tail_chunks: int = 0) -> None:
+        hisparse_set_pipeline(self.pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks)
 
     def export_state(self, r: int, l: int):
         return hisparse_export_state(self.pool, r, l, self.cfg["hot_slots"], self.stream)

@@ -77,7 +77,7 @@ typedef struct hisparse_pool hisparse_pool;
 typedef struct {
   int32_t num_requests;  /* R >= 1 */
   int32_t num_layers;    /* L >= 1 sparse layers */
-  int32_t index_share;   /* g: consecutive layers sharing one selection; L % g == 0 */
+  int32_t index_share;   /* g: consecutive layers sharing one selection, 1..64; L % g == 0 */
   int32_t latent_dim;    /* must be 576 */
   int32_t v_dim;         /* must be 512 */
   int32_t top_k;         /* K: positions per selection, 1..4096 */
@@ -164,11 +164,12 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* pool, int32_t layer, c
  * Layer-ahead fetch (the shared selection of an index-share group is known
  * before the group's first layer is decoded; HiSparse summary article,
  * sections 03-04, on prefetch): after the group's metadata kernel, the miss
- * fetches run one layer at a time on a stream the pool owns, and the decode
- * of layer l waits (by event) only for layer l's fetch, so it overlaps the
- * fetches of the group's later layers (such a layer is decoded without
- * key splits, on few CUs; the group's last layer is split to fill the
- * GPU).  `stream` waits for every fetch
+ * fetches run unit by unit on a stream the pool owns -- each layer but the
+ * last whole, the last layer in request chunks (hisparse_set_pipeline) --
+ * and the decode of a unit waits (by event) only for that unit's fetch, so
+ * it overlaps the fetches of the units after it (a whole layer is decoded
+ * without key splits, on few CUs; chunks of the last layer are split to
+ * fill the GPU).  `stream` waits for every fetch
  * before the call's last decode, so work enqueued on `stream` afterwards
  * sees the whole step; under graph capture the side stream is forked from
  * and joined back into `stream`.  Row ids, counts and the LRU state are
@@ -185,12 +186,18 @@ hisparse_status hisparse_step(hisparse_pool* pool, const int32_t* d_step, const 
  * synchronises `stream`.  Errors: EINVAL, EHIP. */
 hisparse_status hisparse_reset_state(hisparse_pool* pool, void* stream);
 
-/* Tuning: 1024-thread workgroups launched by the miss fetch.  whole_group
- * is used by hisparse_resolve (0 = default 256); per_layer by the per-layer
- * fetches of hisparse_step (0 = default 32), which leave the remaining CUs
- * to the decode running beside them.  Counts above 65536 or negative:
- * EINVAL. */
-hisparse_status hisparse_set_fetch_workgroups(hisparse_pool* pool, int32_t whole_group, int32_t per_layer);
+/* Tuning of the fetch and of hisparse_step's pipeline (0 = default):
+ *   group_fetch_workgroups: 1024-thread workgroups of the whole-group miss
+ *     fetch of hisparse_resolve (default 256);
+ *   unit_fetch_workgroups: workgroups of each pipelined fetch of
+ *     hisparse_step (default 32), which leave the other CUs to the decode
+ *     running beside them;
+ *   tail_chunks: request chunks the last layer of an index-share group is
+ *     fetched and decoded in (default 1, at most 16, capped at R).
+ * Results do not depend on these settings, except the rounding of O and
+ * lse of the chunked layer.  Errors: EINVAL. */
+hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks);
 
 /* Copy the LRU state of (request r, layer l) to host arrays of B int32:
  * owner (logical position per slot, -1 empty) and stamp (step of last use,
@@ -207,7 +214,9 @@ hisparse_status hisparse_check_errors(hisparse_pool* pool, void* stream, uint32_
 /* Per-kernel timing with HIP events recorded on the launch stream around
  * every kernel the pool enqueues (resolve metadata, miss fetch, decode,
  * split combine).  Off by default; while on, each launch adds two event
- * records.  Up to 8192 launches are kept between reads. */
+ * records.  Up to 8192 launches are kept between reads; switching the
+ * profiler on or off keeps them.  Launches enqueued under HIP graph capture
+ * record their events when the graph is replayed. */
 typedef struct {
   const char* name;   /* kernel name (static storage) */
   int32_t launches;   /* launches timed since the last read */

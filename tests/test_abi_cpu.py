@@ -71,7 +71,7 @@ def test_null_arguments_rejected():
     assert lib.hisparse_host_rows(None, 0, 0) is None
     assert lib.hisparse_stream_copy(None, None, 16, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_reset_state(None, None) == H.HISPARSE_EINVAL
-    assert lib.hisparse_set_fetch_workgroups(None, 0, 0) == H.HISPARSE_EINVAL
+    assert lib.hisparse_set_pipeline(None, 0, 0, 0) == H.HISPARSE_EINVAL
     c, keep = _cfg()
     out = ctypes.c_void_p()
     assert lib.hisparse_create_pool(ctypes.byref(c), None, 0, None, None, ctypes.byref(out)) == H.HISPARSE_EINVAL

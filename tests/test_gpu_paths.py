@@ -132,16 +132,22 @@ def test_overlapped_step_matches_oracle_and_sync_path():
 
     log("synchronous path after reset, odd whole-group fetch grid")
     hs.reset_state()
-    hs.set_fetch_workgroups(whole_group=7, per_layer=0)
+    hs.set_pipeline(group_fetch_workgroups=7)
     sync_snaps = _run_sync_path(hs, w, tr, buf)
     _assert_same(step_snaps, sync_snaps, "sync path vs overlapped step", exact_attention=False)
     check_state(hs, dec, pairs, w.steps - 1)
 
-    log("overlapped step path after reset, one workgroup per layer fetch")
+    log("overlapped step path after reset, one workgroup per fetch, last layer unchunked")
     hs.reset_state()
-    hs.set_fetch_workgroups(whole_group=0, per_layer=1)
+    hs.set_pipeline(unit_fetch_workgroups=1, tail_chunks=1)
     again = _run_step_path(hs, w, tr, buf)
-    _assert_same(step_snaps, again, "per-layer fetch grid 1 vs default")
+    _assert_same(step_snaps, again, "fetch grid 1, no tail chunks vs default", exact_attention=False)
+
+    log("overlapped step path after reset, one request per tail chunk")
+    hs.reset_state()
+    hs.set_pipeline(unit_fetch_workgroups=5, tail_chunks=16)
+    again = _run_step_path(hs, w, tr, buf)
+    _assert_same(step_snaps, again, "4 tail chunks of one request vs default", exact_attention=False)
     assert hs.check_errors() == 0
     hs.close()
 
