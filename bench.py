@@ -107,7 +107,7 @@ def cpu_baseline(w, trace, budget_s=20.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    reqs = [0, 1]
+    reqs = list(range(min(2, w.num_requests)))
     dec = OracleDecoder(w, requests=reqs)
     t0 = time.time()
     steps = 0
@@ -290,26 +290,37 @@ def main() -> int:
     # 3) decode alone: every layer of the last step, one launch per layer
     #    (default key splits), over rows that are already resident
     t_last = n_steps - 1
-    dec_us = None
+    dec_us = dec_layer_us = None
     if not args.no_decode_only:
+        # (a) one launch per index-share group; (b) one launch per layer
         dec_reps = 10
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
+        for _ in range(dec_reps):
+            for gi in range(w.groups):
+                l0 = gi * w.index_share
+                H.hisparse_sparse_mla_decode_layers(hs.pool, l0, w.index_share, d_q[t_last, l0].data_ptr(),
+                                                    d_rows[t_last, l0].data_ptr(), w.scale, d_out[l0].data_ptr(),
+                                                    d_lse[l0].data_ptr(), stream.cuda_stream)
+        e1.record(stream)
         for _ in range(dec_reps):
             for l in range(L):
                 H.hisparse_sparse_mla_decode(hs.pool, l, d_q[t_last, l].data_ptr(), d_rows[t_last, l].data_ptr(),
                                              w.scale, d_out[l].data_ptr(), d_lse[l].data_ptr(), stream.cuda_stream)
-        e1.record(stream)
+        e2.record(stream)
         torch.cuda.synchronize(dev)
         dec_us = e0.elapsed_time(e1) * 1e3 / dec_reps
+        dec_layer_us = e1.elapsed_time(e2) * 1e3 / dec_reps
     flags = hs.check_errors()
     if flags:
         log(f"device error flags {flags:#x} after the replays")
         return 1
 
-    use_graph = graph_ms is not None
+    # the headline is the faster of the two timed modes, with the kernel
+    # times recorded in that same mode
+    use_graph = graph_ms is not None and prof_graph is not None and graph_ms <= eager_ms
     ms_total = graph_ms if use_graph else eager_ms
-    prof = prof_graph if prof_graph is not None else prof_eager
+    prof = prof_graph if use_graph else prof_eager
     valid = counts.sum(axis=3)  # valid selections per (step, l, r)
     misses = counts[..., 2]
     ms_step = ms_total / args.steps
@@ -410,15 +421,20 @@ def main() -> int:
                  "miss_rate": round(float(misses.sum() / max(valid.sum(), 1)), 4),
                  "attn_gflop": round(float(attn_flops.mean()) / 1e9, 2)},
         "timing": {"timed_region": "graph replays" if use_graph else "eager steps",
-                   "kernel_times_from": "graph replays" if prof_graph is not None else "eager steps",
+                   "kernel_times_from": "graph replays" if use_graph else "eager steps",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 2),
                    "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
                         "sync_path_tokens_per_s": round(R * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
-        "decode_only": {"us_per_step": round(dec_us, 2), "launches": L, "alg_bytes": int(dec_bytes),
-                        "achieved_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 2),
-                        "frac_of_hbm": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)} if dec_us else None,
+        "decode_only": {"alg_bytes": int(dec_bytes),
+                        "per_group_launch": {"us_per_step": round(dec_us, 2), "launches": w.groups,
+                                             "achieved_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 2),
+                                             "frac_of_hbm": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                        "per_layer_launch": {"us_per_step": round(dec_layer_us, 2), "launches": L,
+                                             "achieved_GBs": round(dec_bytes / (dec_layer_us * 1e-6) / 1e9, 2),
+                                             "frac_of_hbm": round(dec_bytes / (dec_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                                  4)}} if dec_us else None,
         "host_link": probe,
         "cpu_baseline": cpu,
     }

@@ -522,6 +522,31 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, cons
   return enqueue_decode(p, layer, 1, p->cfg.num_requests, d_q, d_rows, scale, d_out, d_lse, (hipStream_t)stream);
 }
 
+hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
+                                                  const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out,
+                                                  float* d_lse, void* stream) {
+  if (!p || !d_q || !d_rows || !d_out || !d_lse) {
+    set_error("hisparse_sparse_mla_decode_layers: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  const int g = p->cfg.index_share;
+  if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > p->cfg.num_layers ||
+      layer_begin / g != (layer_begin + n_layers - 1) / g) {
+    set_error("hisparse_sparse_mla_decode_layers: layers must lie inside one index-share group");
+    return HISPARSE_EINVAL;
+  }
+  if ((uintptr_t)d_q % 16) {
+    set_error("hisparse_sparse_mla_decode_layers: d_q must be 16-byte aligned");
+    return HISPARSE_EINVAL;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("hisparse_sparse_mla_decode_layers: scale must be finite");
+    return HISPARSE_EINVAL;
+  }
+  return enqueue_decode(p, layer_begin, n_layers, p->cfg.num_requests, d_q, d_rows, scale, d_out, d_lse,
+                        (hipStream_t)stream);
+}
+
 hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,
                               float scale, int32_t* d_rows, int32_t* d_counts, float* d_out, float* d_lse,
                               void* stream) {
@@ -553,6 +578,16 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
     hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * K, d_rows + (size_t)l0 * R * K,
                                          d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
+    if (G == 1 && C == 1) {
+      // One layer, one unit: nothing to overlap, so no fork; the fetch takes
+      // the whole-group launch shape.
+      const size_t pr = (size_t)l0 * R;
+      if ((st = enqueue_fetch(p, l0, 1, 0, (int)R, p->fetch_wg_all, s))) return st;
+      st = enqueue_decode(p, l0, 1, (int)R, d_q + pr * H * kLatent, d_rows + pr * K, scale, d_out + pr * H * kVDim,
+                          d_lse + pr * H, s);
+      if (st) return st;
+      continue;
+    }
     if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
       return hip_fail(e, "hisparse_step: fork");
     struct Unit {

@@ -33,6 +33,7 @@ EXPORTED = (
     "hisparse_last_error", "hisparse_workspace_bytes", "hisparse_kv_rows_per_layer",
     "hisparse_create_pool", "hisparse_destroy_pool", "hisparse_host_rows",
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
+    "hisparse_sparse_mla_decode_layers",
     "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_export_state", "hisparse_check_errors",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
@@ -92,6 +93,7 @@ def load() -> ctypes.CDLL:
         "hisparse_set_block_table": (_I32, [_VP, _I32, _VP, _I32, _VP]),
         "hisparse_resolve": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_sparse_mla_decode": (_I32, [_VP, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
+        "hisparse_sparse_mla_decode_layers": (_I32, [_VP, _I32, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
         "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
@@ -176,6 +178,11 @@ def hisparse_resolve(pool, layer_begin, n_layers, d_step, d_topk, d_rows, d_coun
 
 def hisparse_sparse_mla_decode(pool, layer, d_q, d_rows, scale, d_out, d_lse, stream) -> None:
     _check(load().hisparse_sparse_mla_decode(pool, layer, d_q, d_rows, float(scale), d_out, d_lse, stream))
+
+
+def hisparse_sparse_mla_decode_layers(pool, layer_begin, n_layers, d_q, d_rows, scale, d_out, d_lse, stream) -> None:
+    _check(load().hisparse_sparse_mla_decode_layers(pool, layer_begin, n_layers, d_q, d_rows, float(scale), d_out,
+                                                    d_lse, stream))
 
 
 def hisparse_step(pool, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse, stream) -> None:
@@ -280,6 +287,10 @@ class HiSparse:
     def decode(self, layer, d_q, d_rows, scale, d_out, d_lse) -> None:
         hisparse_sparse_mla_decode(self.pool, layer, d_q.data_ptr(), d_rows.data_ptr(), scale,
                                    d_out.data_ptr(), d_lse.data_ptr(), self.stream)
+
+    def decode_layers(self, layer_begin, n_layers, d_q, d_rows, scale, d_out, d_lse) -> None:
+        hisparse_sparse_mla_decode_layers(self.pool, layer_begin, n_layers, d_q.data_ptr(), d_rows.data_ptr(), scale,
+                                          d_out.data_ptr(), d_lse.data_ptr(), self.stream)
 
     def step(self, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse) -> None:
         hisparse_step(self.pool, d_step.data_ptr(), d_topk.data_ptr(), d_q.data_ptr(), scale,

@@ -157,6 +157,19 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* pool, int32_t layer, c
                                            const int32_t* d_rows, float scale, float* d_out,
                                            float* d_lse, void* stream);
 
+/* Sparse MLA decode of layers [layer_begin, layer_begin + n_layers) in one
+ * launch (the layers must lie in one index-share group, whose row-id
+ * arrays hisparse_resolve fills together).  Same arithmetic as
+ * hisparse_sparse_mla_decode per layer; a launch over several layers
+ * needs fewer key splits to fill the GPU (none for 4 layers x 32 requests
+ * x 128 heads).
+ *   d_q [n_layers][R][H][576], d_rows [n_layers][R][K],
+ *   d_out [n_layers][R][H][512], d_lse [n_layers][R][H].
+ * Errors: EINVAL (layers outside one group, null or misaligned pointers). */
+hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers,
+                                                  const uint16_t* d_q, const int32_t* d_rows, float scale,
+                                                  float* d_out, float* d_lse, void* stream);
+
 /* One decode step over every layer: for each index-share group, RESOLVE all
  * of its layers with the group's selection, then decode each layer.
  *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],
@@ -169,7 +182,9 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* pool, int32_t layer, c
  * and the decode of a unit waits (by event) only for that unit's fetch, so
  * it overlaps the fetches of the units after it (a whole layer is decoded
  * without key splits, on few CUs; chunks of the last layer are split to
- * fill the GPU).  `stream` waits for every fetch
+ * fill the GPU).  A group of one layer fetched in one piece has nothing
+ * to overlap and runs resolve, fetch and decode on `stream` alone.
+ * `stream` waits for every fetch
  * before the call's last decode, so work enqueued on `stream` afterwards
  * sees the whole step; under graph capture the side stream is forked from
  * and joined back into `stream`.  Row ids, counts and the LRU state are

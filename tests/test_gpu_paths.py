@@ -188,3 +188,37 @@ def test_captured_step_graph_replays():
     assert hs.check_errors() == 0
     del graph
     hs.close()
+
+
+def test_decode_layers_matches_oracle():
+    """hisparse_sparse_mla_decode_layers over a whole group, on the rows a
+    step resolved, equals the oracle's attention for every (layer, request)."""
+    import torch
+
+    w = _grouped_workload()
+    tr = w.trace(w.steps)
+    hs = make_pool(w)
+    buf = _Buffers(w, hs.device)
+    dec = OracleDecoder(w)
+    pairs = [(l, r) for l in range(w.num_layers) for r in range(w.num_requests)]
+    out2 = torch.full_like(buf.out, float("nan"))
+    lse2 = torch.full_like(buf.lse, float("nan"))
+    for t in range(3):
+        buf.load(w, t, tr[t])
+        hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+        dec.resolve_step(t, tr[t])
+        g = w.index_share
+        for gi in range(w.num_layers // g):
+            l0 = gi * g
+            hs.decode_layers(l0, g, buf.q[l0:l0 + g], buf.rows[l0:l0 + g], w.scale, out2[l0:l0 + g], lse2[l0:l0 + g])
+        torch.cuda.synchronize(hs.device)
+
+        class _View:
+            pass
+
+        v = _View()
+        v.w, v.out, v.lse = w, out2.cpu(), lse2.cpu()
+        worst = check_attention(v, dec, t, tr[t], pairs)
+        log(f"decode_layers step {t}: worst O rel err {worst:.3e}")
+    assert hs.check_errors() == 0
+    hs.close()
