@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhisparse.so")
-SOURCES = ["pool.cpp", "resolve.hip", "decode.hip"]
+SOURCES = ["pool.cpp", "resolve.hip", "decode.hip", "residency.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -40,6 +40,8 @@ struct FetchArgs {
   const int2* fetch;           // [n_pairs][K] (position, slot)
   const uint64_t* host_rows;   // [L*R] device-visible address of pool rows of (l, r)
   uint16_t* const* kv;         // [L] device pointers of the KV tensors (device array)
+  const int32_t* hv;           // [L][R] positions below hv[l][r] are held by the host pool
+  uint32_t* err;
   int32_t layer_begin;
   int32_t n_pairs;             // layers * num_requests
   int32_t num_requests;        // requests per layer in this launch
@@ -48,6 +50,34 @@ struct FetchArgs {
   int32_t top_k;
   int32_t hot_slots;
   int64_t resident_rows;
+};
+
+// Append of one token per request (all layers) into the tail page.
+struct AppendArgs {
+  const uint16_t* rows;        // [L][R][576] new rows
+  uint16_t* const* kv;         // [L] device array of KV tensor pointers
+  int32_t* ctx;                // [R] current context lengths (advanced)
+  const int32_t* capacity;     // [R]
+  const int32_t* bt;           // concatenated block tables
+  const int32_t* bt_off;       // [R]
+  uint32_t* err;
+  int32_t num_layers;
+  int32_t num_requests;
+  int32_t page_shift;
+};
+
+// Copy of completed pages from their resident blocks to the host pool.
+struct WritebackArgs {
+  uint16_t* const* kv;         // [L]
+  const uint64_t* host_rows;   // [L*R] device-visible address of the pool rows of (l, r)
+  const int32_t* ctx;          // [R]
+  int32_t* hv;                 // [L][R] (advanced)
+  const int32_t* bt;
+  const int32_t* bt_off;
+  uint32_t* err;
+  int32_t num_layers;
+  int32_t num_requests;
+  int32_t page_shift;
 };
 
 struct ResolveArgs {
@@ -97,7 +127,7 @@ struct DecodeArgs {
 
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
-  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, host_rows, kv_ptrs, err,
+  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, cap, hv, host_rows, kv_ptrs, err,
       partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
@@ -122,8 +152,11 @@ struct Profiler {
 struct hisparse_pool {
   hisparse_config cfg;
   hs::Profiler prof;
-  std::vector<int64_t> ctx;
-  std::vector<int32_t> n_pages;
+  std::vector<int64_t> ctx;             // context length at creation
+  std::vector<int64_t> cap;             // capacity (host rows, block-table pages, map entries)
+  std::vector<int32_t> n_pages;         // block-table pages per request: ceil(cap / page_size)
+  std::vector<int32_t> init_ctx32;      // [R] lengths at creation (source of resets)
+  std::vector<int32_t> init_hv32;       // [L][R] host-held prefix at creation (= ctx_len)
   int device = 0;
   hs::Layout lay;
   char* ws = nullptr;
@@ -134,7 +167,7 @@ struct hisparse_pool {
   int64_t kv_rows = 0;
   size_t resolve_lds = 0;
   // device views into the workspace
-  int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d;
+  int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d, *cap_d, *hv_d;
   int16_t* posmap;
   int64_t* map_off;
   int2* fetch;
@@ -167,6 +200,10 @@ hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);
 hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& a, int grid, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// residency.hip
+hipError_t launch_append(hisparse_pool* p, const AppendArgs& a, hipStream_t s);
+hipError_t launch_writeback(hisparse_pool* p, const WritebackArgs& a, hipStream_t s);
 
 // decode.hip
 int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);

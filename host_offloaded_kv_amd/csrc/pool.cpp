@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -29,6 +30,10 @@ int ilog2_exact(int v) {
   int b = 0;
   while ((1 << b) < v) ++b;
   return (1 << b) == v ? b : -1;
+}
+
+int64_t capacity_of(const hisparse_config* c, int r) {
+  return c->ctx_capacity ? c->ctx_capacity[r] : c->ctx_len[r];
 }
 
 hisparse_status check_config(const hisparse_config* c) {
@@ -74,6 +79,10 @@ hisparse_status check_config(const hisparse_config* c) {
       set_error("ctx_len[" + std::to_string(r) + "] must be in [1, 2^30]");
       return HISPARSE_EINVAL;
     }
+    if (capacity_of(c, r) < c->ctx_len[r] || capacity_of(c, r) > (int64_t{1} << 30)) {
+      set_error("ctx_capacity[" + std::to_string(r) + "] must be in [ctx_len[r], 2^30]");
+      return HISPARSE_EINVAL;
+    }
   }
   const int64_t rows = c->resident_rows_per_layer + (int64_t)c->num_requests * c->hot_slots;
   if (rows >= (int64_t{1} << 31)) {
@@ -91,7 +100,7 @@ Layout make_layout(const hisparse_config* c) {
   Layout L{};
   const size_t R = c->num_requests, NL = c->num_layers, B = c->hot_slots, K = c->top_k;
   int64_t bt_entries = 0;
-  for (size_t r = 0; r < R; ++r) bt_entries += (c->ctx_len[r] + c->page_size - 1) / c->page_size;
+  for (size_t r = 0; r < R; ++r) bt_entries += (capacity_of(c, (int)r) + c->page_size - 1) / c->page_size;
   L.bt_entries = bt_entries;
   L.layers_batched = c->index_share;
   const int s1 = decode_splits(1, c->num_requests, c->num_heads, c->top_k);
@@ -113,12 +122,14 @@ Layout make_layout(const hisparse_config* c) {
   L.bt = off; off = align256(off + (size_t)bt_entries * 4);
   L.bt_off = off; off = align256(off + R * 4);
   L.ctx = off; off = align256(off + R * 4);
+  L.cap = off; off = align256(off + R * 4);
+  L.hv = off; off = align256(off + NL * R * 4);
   L.host_rows = off; off = align256(off + NL * R * 8);
   L.kv_ptrs = off; off = align256(off + NL * 8);
   L.err = off; off = align256(off + 4);
   L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
   int64_t ctx_sum = 0;
-  for (size_t r = 0; r < R; ++r) ctx_sum += c->ctx_len[r];
+  for (size_t r = 0; r < R; ++r) ctx_sum += capacity_of(c, (int)r);
   L.posmap_entries = (int64_t)NL * ctx_sum;
   L.posmap = off; off = align256(off + (size_t)L.posmap_entries * 2);
   L.map_off = off; off = align256(off + R * 8);
@@ -227,6 +238,9 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   const int R = cfg->num_requests, NL = cfg->num_layers;
   p->ctx.assign(cfg->ctx_len, cfg->ctx_len + R);
   p->cfg.ctx_len = p->ctx.data();
+  p->cap.resize(R);
+  for (int r = 0; r < R; ++r) p->cap[r] = capacity_of(cfg, r);
+  p->cfg.ctx_capacity = p->cap.data();
   p->lay = lay;
   p->ws = (char*)d_workspace;
   p->kv.resize(NL);
@@ -265,7 +279,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->host_rows.assign((size_t)NL * R, nullptr);
   p->host_rows_dev.assign((size_t)NL * R, 0);
   for (int r = 0; r < R; ++r) {
-    const size_t per_layer = (size_t)p->ctx[r] * kRowBytes;
+    const size_t per_layer = (size_t)p->cap[r] * kRowBytes;
     void* h = nullptr;
     e = hipHostMalloc(&h, per_layer * NL, flags);
     if (e != hipSuccess || !h) {
@@ -299,6 +313,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->bt = (int32_t*)(w + lay.bt);
   p->bt_off = (int32_t*)(w + lay.bt_off);
   p->ctx_d = (int32_t*)(w + lay.ctx);
+  p->cap_d = (int32_t*)(w + lay.cap);
+  p->hv_d = (int32_t*)(w + lay.hv);
   p->host_rows_d = (uint64_t*)(w + lay.host_rows);
   p->kv_d = (uint16_t**)(w + lay.kv_ptrs);
   p->err = (uint32_t*)(w + lay.err);
@@ -306,26 +322,31 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->posmap = (int16_t*)(w + lay.posmap);
   p->map_off = (int64_t*)(w + lay.map_off);
 
-  std::vector<int32_t> bt_off(R), ctx32(R);
+  std::vector<int32_t> bt_off(R), ctx32(R), cap32(R);
   std::vector<int64_t> map_off(R);
   int64_t acc_m = 0;
   for (int r = 0; r < R; ++r) {
     map_off[r] = acc_m;
-    acc_m += p->ctx[r];
+    acc_m += p->cap[r];
   }
   p->n_pages.resize(R);
   int64_t acc = 0;
   for (int r = 0; r < R; ++r) {
     bt_off[r] = (int32_t)acc;
-    p->n_pages[r] = (int32_t)((p->ctx[r] + cfg->page_size - 1) / cfg->page_size);
+    p->n_pages[r] = (int32_t)((p->cap[r] + cfg->page_size - 1) / cfg->page_size);
     acc += p->n_pages[r];
     ctx32[r] = (int32_t)p->ctx[r];
+    cap32[r] = (int32_t)p->cap[r];
   }
+  p->init_ctx32 = ctx32;
+  p->init_hv32.resize((size_t)NL * R);
+  for (int l = 0; l < NL; ++l)
+    for (int r = 0; r < R; ++r) p->init_hv32[(size_t)l * R + r] = ctx32[r];
   std::vector<uint64_t> kvp(NL);
   for (int l = 0; l < NL; ++l) kvp[l] = (uint64_t)p->kv[l];
   if ((e = hipMemcpyAsync(p->bt_off, bt_off.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
       (e = hipMemcpyAsync(p->map_off, map_off.data(), R * 8, hipMemcpyHostToDevice, s)) != hipSuccess ||
-      (e = hipMemcpyAsync(p->ctx_d, ctx32.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(p->cap_d, cap32.data(), R * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
       (e = hipMemcpyAsync(p->host_rows_d, p->host_rows_dev.data(), (size_t)NL * R * 8, hipMemcpyHostToDevice, s)) !=
           hipSuccess ||
       (e = hipMemcpyAsync(p->kv_d, kvp.data(), (size_t)NL * 8, hipMemcpyHostToDevice, s)) != hipSuccess ||
@@ -378,7 +399,7 @@ hisparse_status hisparse_set_block_table(hisparse_pool* p, int32_t r, const int3
     return HISPARSE_EINVAL;
   }
   if (n_pages != p->n_pages[r]) {
-    set_error("hisparse_set_block_table: n_pages must be ceil(ctx_r / page_size) = " +
+    set_error("hisparse_set_block_table: n_pages must be ceil(capacity_r / page_size) = " +
               std::to_string(p->n_pages[r]));
     return HISPARSE_EINVAL;
   }
@@ -450,6 +471,8 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
   f.top_k = p->cfg.top_k;
   f.hot_slots = p->cfg.hot_slots;
   f.resident_rows = p->cfg.resident_rows_per_layer;
+  f.hv = p->hv_d;
+  f.err = p->err;
   hipError_t e = launch_fetch(p, f, grid, s);
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "miss fetch launch");
 }
@@ -626,6 +649,107 @@ hisparse_status hisparse_reset_state(hisparse_pool* p, void* stream) {
   if (e == hipSuccess) e = launch_state_reset(p, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_reset_state");
+}
+
+hisparse_status hisparse_append(hisparse_pool* p, const uint16_t* d_rows, void* stream) {
+  if (!p || !d_rows) {
+    set_error("hisparse_append: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  if ((uintptr_t)d_rows % 16) {
+    set_error("hisparse_append: d_rows must be 16-byte aligned");
+    return HISPARSE_EINVAL;
+  }
+  AppendArgs a;
+  a.rows = d_rows;
+  a.kv = p->kv_d;
+  a.ctx = p->ctx_d;
+  a.capacity = p->cap_d;
+  a.bt = p->bt;
+  a.bt_off = p->bt_off;
+  a.err = p->err;
+  a.num_layers = p->cfg.num_layers;
+  a.num_requests = p->cfg.num_requests;
+  a.page_shift = ilog2_exact(p->cfg.page_size);
+  hipError_t e = launch_append(p, a, (hipStream_t)stream);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_append");
+}
+
+hisparse_status hisparse_writeback(hisparse_pool* p, void* stream) {
+  if (!p) {
+    set_error("hisparse_writeback: pool is NULL");
+    return HISPARSE_EINVAL;
+  }
+  WritebackArgs a;
+  a.kv = p->kv_d;
+  a.host_rows = p->host_rows_d;
+  a.ctx = p->ctx_d;
+  a.hv = p->hv_d;
+  a.bt = p->bt;
+  a.bt_off = p->bt_off;
+  a.err = p->err;
+  a.num_layers = p->cfg.num_layers;
+  a.num_requests = p->cfg.num_requests;
+  a.page_shift = ilog2_exact(p->cfg.page_size);
+  hipError_t e = launch_writeback(p, a, (hipStream_t)stream);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_writeback");
+}
+
+hisparse_status hisparse_get_lengths(hisparse_pool* p, int32_t* host_ctx, int32_t* host_held, void* stream) {
+  if (!p || !host_ctx || !host_held) {
+    set_error("hisparse_get_lengths: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  const size_t R = p->cfg.num_requests, L = p->cfg.num_layers;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(host_ctx, p->ctx_d, R * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_held, p->hv_d, L * R * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_get_lengths");
+}
+
+hisparse_status hisparse_set_pages(hisparse_pool* p, int32_t r, int32_t first_page, int32_t n,
+                                   const int32_t* host_blocks, void* stream) {
+  if (!p || !host_blocks || r < 0 || r >= p->cfg.num_requests || first_page < 0 || n < 1 ||
+      first_page + n > p->n_pages[r]) {
+    set_error("hisparse_set_pages: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  const int64_t nblocks = p->cfg.resident_rows_per_layer / p->cfg.page_size;
+  for (int i = 0; i < n; ++i) {
+    if (host_blocks[i] < -1 || host_blocks[i] >= nblocks) {
+      set_error("hisparse_set_pages: block id out of range at page " + std::to_string(first_page + i));
+      return HISPARSE_EINVAL;
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const size_t R = p->cfg.num_requests, L = p->cfg.num_layers;
+  int32_t off = 0;
+  for (int i = 0; i < r; ++i) off += p->n_pages[i];
+  // A page may become a placeholder only once every layer's host pool holds
+  // every position of it that exists (the write-back has run), so that a
+  // later miss reads correct rows.
+  std::vector<int32_t> held(L * R), cur(n);
+  int32_t ctx_now = 0;
+  hipError_t e = hipMemcpyAsync(held.data(), p->hv_d, L * R * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(cur.data(), p->bt + off + first_page, (size_t)n * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&ctx_now, p->ctx_d + r, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hisparse_set_pages");
+  int64_t min_held = INT64_MAX;
+  for (size_t l = 0; l < L; ++l) min_held = std::min<int64_t>(min_held, held[l * R + r]);
+  for (int i = 0; i < n; ++i) {
+    // positions of the page that exist so far
+    const int64_t page_end = std::min<int64_t>((int64_t)(first_page + i + 1) * p->cfg.page_size, ctx_now);
+    if (host_blocks[i] < 0 && cur[i] >= 0 && page_end > min_held) {
+      set_error("hisparse_set_pages: page " + std::to_string(first_page + i) +
+                " is not yet held by the host pool (run hisparse_writeback after it completes)");
+      return HISPARSE_EINVAL;
+    }
+  }
+  e = hipMemcpyAsync(p->bt + off + first_page, host_blocks, (size_t)n * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_set_pages");
 }
 
 hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_workgroups,

@@ -478,7 +478,9 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
         const int li = pr / R;
         const int r = a.request_begin + (pr - li * R);
         const int l = a.layer_begin + li;
-        if ((unsigned)e.y < (unsigned)a.hot_slots && e.x >= 0 && e.x < ctx[r]) {
+        const bool held = e.x < a.hv[(size_t)l * RT + r];  // the host pool holds this position
+        if (!held && c == 0) atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
+        if ((unsigned)e.y < (unsigned)a.hot_slots && e.x >= 0 && e.x < ctx[r] && held) {
           const u32x4* src = reinterpret_cast<const u32x4*>(
               reinterpret_cast<const char*>(a.host_rows[(size_t)l * RT + r]) + (size_t)e.x * kRowBytes) + c;
           const int64_t row = a.resident_rows + (int64_t)r * a.hot_slots + e.y;
@@ -530,6 +532,10 @@ hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   if ((e = hipMemsetAsync(p->last_t, 0xFF, pairs * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->miss_count, 0, pairs * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->posmap, 0xFF, p->lay.posmap_entries * 2, s)) != hipSuccess) return e;
+  if ((e = hipMemcpyAsync(p->ctx_d, p->init_ctx32.data(), c.num_requests * 4, hipMemcpyHostToDevice, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = hipMemcpyAsync(p->hv_d, p->init_hv32.data(), pairs * 4, hipMemcpyHostToDevice, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(iota_lru, dim3(1024), dim3(256), 0, s, p->lru, pairs, c.hot_slots);
   return hipGetLastError();
 }

@@ -24,6 +24,14 @@ HISPARSE_ENOMEM = -2
 HISPARSE_EHIP = -3
 HISPARSE_EDEVICE = -4
 HISPARSE_ESTATE = -5
+
+# device error flag bits (hisparse_check_errors)
+HISPARSE_ERR_RANGE = 1
+HISPARSE_ERR_DUP = 2
+HISPARSE_ERR_STEP = 4
+HISPARSE_ERR_ROW = 8
+HISPARSE_ERR_APPEND = 16
+HISPARSE_ERR_UNMATERIALIZED = 32
 ERR_RANGE = 1
 ERR_DUP = 2
 ERR_STEP = 4
@@ -35,6 +43,7 @@ EXPORTED = (
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
     "hisparse_sparse_mla_decode_layers",
     "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
+    "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
     "hisparse_export_state", "hisparse_check_errors",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
     "hisparse_profile_enable", "hisparse_profile_read",
@@ -50,6 +59,7 @@ class hisparse_config(ctypes.Structure):
         ("num_heads", ctypes.c_int32), ("host_coherent", ctypes.c_int32),
         ("resident_rows_per_layer", ctypes.c_int64),
         ("ctx_len", ctypes.POINTER(ctypes.c_int64)),
+        ("ctx_capacity", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -97,6 +107,10 @@ def load() -> ctypes.CDLL:
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
         "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
+        "hisparse_append": (_I32, [_VP, _VP, _VP]),
+        "hisparse_writeback": (_I32, [_VP, _VP]),
+        "hisparse_set_pages": (_I32, [_VP, _I32, _I32, _I32, _VP, _VP]),
+        "hisparse_get_lengths": (_I32, [_VP, _VP, _VP, _VP]),
         "hisparse_export_state": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
         "hisparse_check_errors": (_I32, [_VP, _VP, ctypes.POINTER(ctypes.c_uint32)]),
         "hisparse_host_alloc": (_I32, [ctypes.c_size_t, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP)]),
@@ -121,6 +135,9 @@ def _check(status: int) -> None:
 def make_config(cfg: dict) -> tuple[hisparse_config, object]:
     """Build a ``hisparse_config`` from a dict; returns (struct, keep-alive)."""
     ctx = (ctypes.c_int64 * len(cfg["ctx_len"]))(*[int(c) for c in cfg["ctx_len"]])
+    cap = None
+    if cfg.get("ctx_capacity") is not None:
+        cap = (ctypes.c_int64 * len(cfg["ctx_capacity"]))(*[int(c) for c in cfg["ctx_capacity"]])
     c = hisparse_config(
         num_requests=cfg["num_requests"], num_layers=cfg["num_layers"],
         index_share=cfg.get("index_share", 1), latent_dim=cfg.get("latent_dim", 576),
@@ -129,8 +146,9 @@ def make_config(cfg: dict) -> tuple[hisparse_config, object]:
         host_coherent=cfg.get("host_coherent", 0),
         resident_rows_per_layer=cfg.get("resident_rows_per_layer", 0),
         ctx_len=ctypes.cast(ctx, ctypes.POINTER(ctypes.c_int64)),
+        ctx_capacity=ctypes.cast(cap, ctypes.POINTER(ctypes.c_int64)) if cap is not None else None,
     )
-    return c, ctx
+    return c, (ctx, cap)
 
 
 def hisparse_last_error() -> str:
@@ -196,6 +214,27 @@ def hisparse_reset_state(pool: int, stream: int) -> None:
 def hisparse_set_pipeline(pool: int, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
                           tail_chunks: int = 0) -> None:
     _check(load().hisparse_set_pipeline(pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks))
+
+
+def hisparse_append(pool: int, d_rows: int, stream: int) -> None:
+    _check(load().hisparse_append(pool, d_rows, stream))
+
+
+def hisparse_writeback(pool: int, stream: int) -> None:
+    _check(load().hisparse_writeback(pool, stream))
+
+
+def hisparse_set_pages(pool: int, r: int, first_page: int, blocks, stream: int) -> None:
+    blocks = np.ascontiguousarray(blocks, dtype=np.int32)
+    _check(load().hisparse_set_pages(pool, r, first_page, blocks.shape[0], blocks.ctypes.data, stream))
+
+
+def hisparse_get_lengths(pool: int, num_requests: int, num_layers: int, stream: int):
+    """(ctx [R], held [L][R]) as int32 arrays."""
+    ctx = np.empty(num_requests, np.int32)
+    held = np.empty((num_layers, num_requests), np.int32)
+    _check(load().hisparse_get_lengths(pool, ctx.ctypes.data, held.ctypes.data, stream))
+    return ctx, held
 
 
 def hisparse_export_state(pool: int, r: int, l: int, hot_slots: int, stream: int):
@@ -275,7 +314,9 @@ class HiSparse:
         return hisparse_host_rows(self.pool, r, l)
 
     def host_rows(self, r: int, l: int) -> np.ndarray:
-        return host_array(self.host_rows_ptr(r, l), (int(self.cfg["ctx_len"][r]), 576))
+        """NumPy view of the host pool rows of (r, l): [capacity_r][576] bf16 bits."""
+        cap = self.cfg.get("ctx_capacity") or self.cfg["ctx_len"]
+        return host_array(self.host_rows_ptr(r, l), (int(cap[r]), 576))
 
     def set_block_table(self, r: int, bt) -> None:
         hisparse_set_block_table(self.pool, r, bt, self.stream)
@@ -302,6 +343,18 @@ class HiSparse:
     def set_pipeline(self, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
                      tail_chunks: int = 0) -> None:
         hisparse_set_pipeline(self.pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks)
+
+    def append(self, d_rows) -> None:
+        hisparse_append(self.pool, d_rows.data_ptr(), self.stream)
+
+    def writeback(self) -> None:
+        hisparse_writeback(self.pool, self.stream)
+
+    def set_pages(self, r: int, first_page: int, blocks) -> None:
+        hisparse_set_pages(self.pool, r, first_page, blocks, self.stream)
+
+    def get_lengths(self):
+        return hisparse_get_lengths(self.pool, self.cfg["num_requests"], self.cfg["num_layers"], self.stream)
 
     def export_state(self, r: int, l: int):
         return hisparse_export_state(self.pool, r, l, self.cfg["hot_slots"], self.stream)

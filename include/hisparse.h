@@ -71,6 +71,8 @@ typedef int32_t hisparse_status;
 #define HISPARSE_ERR_DUP 2u   /* a position repeated within one selection (later copies dropped) */
 #define HISPARSE_ERR_STEP 4u  /* step index negative or below the last one seen by a (request, layer) */
 #define HISPARSE_ERR_ROW 8u   /* decode saw a row id outside the KV tensor (treated as padding) */
+#define HISPARSE_ERR_APPEND 16u /* append with the tail page not resident or the context full (not appended) */
+#define HISPARSE_ERR_UNMATERIALIZED 32u /* a row was needed from the host pool before it was written there */
 
 typedef struct hisparse_pool hisparse_pool;
 
@@ -87,6 +89,9 @@ typedef struct {
   int32_t host_coherent; /* 0: coarse-grained (non-coherent) pinned pool, 1: coherent */
   int64_t resident_rows_per_layer; /* rows of each KV tensor reserved for resident pages (multiple of page_size) */
   const int64_t* ctx_len; /* [R] host array, context length per request (>= 1); copied */
+  const int64_t* ctx_capacity; /* [R] host array or NULL (= ctx_len): the length the context may
+                                  grow to by hisparse_append; sizes the host pool, the block
+                                  table and the position map; copied */
 } hisparse_config;
 
 /* Message describing the calling thread's last failure ("" if none). */
@@ -124,7 +129,7 @@ uint16_t* hisparse_host_rows(hisparse_pool* pool, int32_t r, int32_t l);
 
 /* Set the block table of request r: host_bt[page] is the resident block id
  * of that page, or -1 (host-only placeholder); n_pages must equal
- * ceil(ctx_r / page_size).  Block ids must satisfy
+ * ceil(capacity_r / page_size).  Block ids must satisfy
  * (id + 1) * page_size <= resident_rows_per_layer.  The library never edits
  * a block table, so resident pages (the tail included) are never evicted.
  * The caller must keep resident rows equal to the host rows they mirror.
@@ -196,10 +201,53 @@ hisparse_status hisparse_step(hisparse_pool* pool, const int32_t* d_step, const 
                               float* d_out, float* d_lse, void* stream);
 
 /* Return every (request, layer) to the empty state (owner -1, stamp -1,
- * no step seen); block tables and host rows are kept.  Waits for the
- * pool's own stream, enqueues memory fills (not graph-capturable) and
+ * no step seen) and every context to its length at creation (host pool
+ * held up to that length); block tables and host rows are kept.  Waits for
+ * the pool's own stream, enqueues memory fills (not graph-capturable) and
  * synchronises `stream`.  Errors: EINVAL, EHIP. */
 hisparse_status hisparse_reset_state(hisparse_pool* pool, void* stream);
+
+/* ---- residency transitions (vLLM Hybrid HiSparse blog, "工作原理") ----
+ * Per request the device keeps the current context length ctx_r (starts
+ * at ctx_len[r]) and, per layer, the length held_lr of the prefix the host
+ * pool holds (starts at ctx_len[r]: the caller fills those host rows).
+ * RESOLVE and decode read ctx_r on the device, so a step after appends
+ * accepts the new positions. */
+
+/* Append one token per request: d_rows [L][R][576] bf16 (16-byte aligned)
+ * is the new token's latent row of every layer, written to the resident
+ * block of the request's tail page (page ctx_r / page_size) at row ctx_r %
+ * page_size; then ctx_r += 1.  The caller leases the tail block with
+ * hisparse_set_pages before the append that starts a new page.  A request
+ * whose tail page is a placeholder, or whose context is at capacity, is
+ * left unchanged and sets HISPARSE_ERR_APPEND.  Enqueue only
+ * (graph-capturable). */
+hisparse_status hisparse_append(hisparse_pool* pool, const uint16_t* d_rows, void* stream);
+
+/* Materialise completed pages: for every (layer, request), copy the rows
+ * [held_lr, floor(ctx_r / page_size) * page_size) from their resident
+ * blocks into the host pool (one launch for all layers, zero-copy 16-byte
+ * stores), then held_lr = that bound.  The GPU keeps serving those pages;
+ * afterwards they may be turned into placeholders without another copy.
+ * A completed page that is already a placeholder sets
+ * HISPARSE_ERR_UNMATERIALIZED and leaves held_lr.  Enqueue only
+ * (graph-capturable). */
+hisparse_status hisparse_writeback(hisparse_pool* pool, void* stream);
+
+/* Change block-table entries [first_page, first_page + n) of request r:
+ * host_blocks[i] is a resident block id or -1 (placeholder).  Turning a
+ * resident page into a placeholder requires every layer's host pool to
+ * hold every position of the page below ctx_r (after hisparse_writeback),
+ * so that later misses read correct rows; otherwise EINVAL and nothing
+ * changes.  A newly leased block
+ * holds whatever the caller puts there (hisparse_append writes the rows of
+ * the tail page).  Synchronises `stream`.  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_set_pages(hisparse_pool* pool, int32_t r, int32_t first_page, int32_t n,
+                                   const int32_t* host_blocks, void* stream);
+
+/* Read ctx_r ([R]) and held_lr ([L][R]) into host arrays.  Synchronises
+ * `stream`.  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_get_lengths(hisparse_pool* pool, int32_t* host_ctx, int32_t* host_held, void* stream);
 
 /* Tuning of the fetch and of hisparse_step's pipeline (0 = default):
  *   group_fetch_workgroups: 1024-thread workgroups of the whole-group miss

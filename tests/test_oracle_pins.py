@@ -323,3 +323,59 @@ def test_footprint_pages_numbers():
     hot_gb = g["full_kv_gb"] / ratio
     assert abs(hot_gb - g["hisparse_kv_gb_approx"]) < 0.05
     assert footprint.hot_buffer_bytes(4096, 4, 1152) * 32 == footprint.full_kv_bytes(131072, 4, 1152)
+
+
+# --------------------------------------------------------------------------
+# P12: growing contexts and block-table transitions (vLLM Hybrid HiSparse
+# blog, "工作原理": the tail page stays resident, completed pages become
+# host-only once their host copy exists).  The oracle must agree with the
+# brute-force replay under a changing block table and context length, every
+# miss must be for a position the host pool already holds, and reading the
+# rows the oracle names -- with appends written to the tail block and
+# fetches to hot rows -- must return exactly the selected positions.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(8))
+def test_growth_transitions(seed):
+    from tracegen.residency import growing_schedule
+
+    rng = np.random.default_rng(5000 + seed)
+    page, R, steps, k, b = 8, 3, 48, 6, 10
+    ctx0 = [int(rng.integers(12, 70)) for _ in range(R)]
+    sch = growing_schedule(ctx0, steps, page, total_blocks=4 * R, keep=2)
+    hot_base = 10_000
+    st = {r: LruState(b) for r in range(R)}
+    bf = {r: ([-1] * b, [-1] * b) for r in range(R)}
+    # device rows as labels (request, position); resident pages present at creation hold their rows
+    dev = {}
+    for r in range(R):
+        for pg, blk in enumerate(sch.initial_bt[r]):
+            if blk >= 0:
+                for off in range(page):
+                    if pg * page + off < ctx0[r]:
+                        dev[blk * page + off] = (r, pg * page + off)
+    drops_seen = 0
+    for t in range(steps):
+        for r in range(R):
+            pos = ctx0[r] + t  # this step's append
+            bt = sch.bt_at[t][r]
+            blk = bt[pos // page]
+            assert blk >= 0, "the schedule leases the tail page before the append"
+            dev[blk * page + pos % page] = (r, pos)
+            ctx = sch.ctx_at(t, r)
+            held = max(ctx0[r], ((ctx0[r] + t) // page) * page)  # after the previous step's write-back
+            sel = list(rng.choice(ctx, size=k, replace=False))
+            if rng.random() < 0.7 and ctx - 1 not in sel:
+                sel[0] = ctx - 1
+            res = resolve(st[r], sel, t, ctx, bt, page, hot_base + 100 * r)
+            rows, counts, o, s = bruteforce.replay(*bf[r], sel, t, ctx, bt, page, hot_base + 100 * r)
+            assert res.rows == rows, f"seed {seed} t {t} r {r}"
+            assert (res.n_resident, res.n_hit, res.n_miss) == counts
+            assert st[r].owner == o and st[r].stamp == s
+            bf[r] = (o, s)
+            for p, slot in res.fetches:
+                assert p < held, f"miss of position {p} the host pool does not hold yet (held {held})"
+                dev[hot_base + 100 * r + slot] = (r, p)
+            got = [dev[row] for row in res.rows if row >= 0]
+            assert got == [(r, int(p)) for p in sel if p >= 0]
+        drops_seen += len(sch.post[t])
+    assert drops_seen > 0, "the trace exercises pages turning into placeholders"

@@ -68,3 +68,38 @@ def test_named_workloads_shapes():
     assert np.array_equal(np.sort(ids), np.arange(w.resident_blocks))
     w3 = named_workload("r32_ctx128k_l4")
     assert w3.groups == 1 and w3.resident_rows_per_layer == 32 * 64
+
+
+def test_growing_trace_structure():
+    from tracegen import growing_selection_trace
+
+    ctx0 = [300, 190, 64]
+    tr = growing_selection_trace(7, ctx0, 64, 24, 2, 0.7, 0.8)
+    again = growing_selection_trace(7, ctx0, 64, 24, 2, 0.7, 0.8)
+    assert np.array_equal(tr, again)
+    newest = 0
+    for t in range(24):
+        for g in range(2):
+            for r, c0 in enumerate(ctx0):
+                s = tr[t, g, r]
+                v = s[s >= 0]
+                assert v.shape[0] == min(64, c0 + t + 1)
+                assert np.all(np.diff(v) > 0) and v.min() >= 0 and v.max() < c0 + t + 1
+                newest += int(v.max() == c0 + t)
+    assert newest > 24 * 2 * 3 // 2  # recency weighting picks the just-appended token most steps
+
+
+def test_growing_schedule_invariants():
+    from tracegen.residency import growing_schedule
+
+    ctx0, page, steps = [100, 64, 37], 16, 90
+    sch = growing_schedule(ctx0, steps, page, total_blocks=12, keep=2)
+    for t in range(steps):
+        for r in range(3):
+            bt = sch.bt_at[t][r]
+            pos = ctx0[r] + t
+            assert bt[pos // page] >= 0  # tail page resident at its append
+            res = [b for b in bt if b >= 0]
+            assert len(res) == len(set(res)) and len(res) <= 3
+        used = [b for r in range(3) for b in sch.bt_at[t][r] if b >= 0]
+        assert len(used) == len(set(used))  # no block shared between requests

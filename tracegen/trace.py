@@ -98,3 +98,60 @@ def selection_trace(seed: int, ctx_lens, k: int, steps: int, groups: int,
             for t in range(steps):
                 out[t, g, r] = s.next()
     return out
+
+
+class GrowingSelectionStream:
+    """Selection stream of a context that grows by one token per step.
+
+    At step t the candidates are positions [0, ctx0 + t + 1): the token
+    appended at step t can already be selected.  Weights are recomputed for
+    the current length each step (recency relative to the newest token);
+    retain and resample as in ``SelectionStream``.  Randomness:
+    ``Generator(PCG64(SeedSequence([seed, group, request, 1])))``, drawing
+    per step (t > 0 only) ``rng.choice(prev, n_keep, replace=False)``, then
+    ``rng.random(ctx_t)``.
+    """
+
+    def __init__(self, seed: int, group: int, request: int, ctx0: int, k: int,
+                 retain: float, alpha: float | None):
+        self.rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, group, request, 1])))
+        self.ctx0 = int(ctx0)
+        self.k = int(k)
+        self.retain = float(retain)
+        self.alpha = alpha
+        self.t = 0
+        self.prev: np.ndarray | None = None
+
+    def next(self) -> np.ndarray:
+        ctx = self.ctx0 + self.t + 1
+        self.t += 1
+        w = recency_weights(ctx, self.alpha) if self.alpha is not None else np.ones(ctx)
+        kk = min(self.k, ctx)
+        if self.prev is None:
+            sel = es_top(self.rng.random(ctx), w, kk, None)
+        else:
+            n_keep = int(np.floor(self.retain * min(kk, self.prev.shape[0]) + 0.5))
+            kept = self.rng.choice(self.prev, size=n_keep, replace=False) if n_keep > 0 else np.zeros(0, np.int64)
+            u = self.rng.random(ctx)
+            excl = np.zeros(ctx, dtype=bool)
+            excl[kept] = True
+            fresh = es_top(u, w, kk - n_keep, excl)
+            sel = np.concatenate([kept.astype(np.int64), fresh.astype(np.int64)])
+        sel = np.sort(sel.astype(np.int64))
+        self.prev = sel
+        out = np.full(self.k, -1, dtype=np.int32)
+        out[: sel.shape[0]] = sel
+        return out
+
+
+def growing_selection_trace(seed: int, ctx0s, k: int, steps: int, groups: int,
+                            retain: float, alpha: float | None) -> np.ndarray:
+    """int32 [steps][groups][R][k]; step t selects from [0, ctx0_r + t + 1)."""
+    ctx0s = list(ctx0s)
+    out = np.empty((steps, groups, len(ctx0s), k), dtype=np.int32)
+    for g in range(groups):
+        for r, c0 in enumerate(ctx0s):
+            s = GrowingSelectionStream(seed, g, r, c0, k, retain, alpha)
+            for t in range(steps):
+                out[t, g, r] = s.next()
+    return out
