@@ -91,6 +91,50 @@ def host_link_probe(torch, H, dev, nbytes=256 << 20, reps=5):
     return out
 
 
+def residency_probe(torch, H, w, dev, ctx=8192):
+    """Cost of the residency transitions at the workload's request, layer and
+    head shape: the per-step append (one token per request, every layer) into
+    leased tail pages, and the write-back once every (request, layer) has
+    completed a page (one launch, zero-copy stores into the host pool)."""
+    import numpy as np
+
+    R, L, page = w.num_requests, w.num_layers, w.page_size
+    cfg = dict(num_requests=R, num_layers=L, index_share=w.index_share, top_k=w.top_k, hot_slots=w.hot_slots,
+               page_size=page, num_heads=w.num_heads, resident_rows_per_layer=R * page,
+               ctx_len=[ctx] * R, ctx_capacity=[ctx + page] * R)
+    hs = H.HiSparse(cfg, dev)
+    try:
+        for r in range(R):
+            bt = np.full((ctx + page + page - 1) // page, -1, np.int32)
+            bt[ctx // page] = r
+            hs.set_block_table(r, bt)
+        rows = torch.zeros((L, R, 576), dtype=torch.int16, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        hs.append(rows)  # warm
+        e0.record(stream)
+        for _ in range(page - 1):
+            hs.append(rows)
+        e1.record(stream)
+        hs.writeback()
+        e2.record(stream)
+        torch.cuda.synchronize(dev)
+        if hs.check_errors():
+            return None
+        n_ctx, held = hs.get_lengths()
+        if not (np.all(n_ctx == ctx + page) and np.all(held == ctx + page)):
+            return None
+        wb_bytes = R * L * page * ROW_BYTES
+        wb_ms = e1.elapsed_time(e2)
+        return {"append_us": round(e0.elapsed_time(e1) * 1e3 / (page - 1), 2),
+                "append_bytes": R * L * ROW_BYTES,
+                "writeback_us": round(wb_ms * 1e3, 2), "writeback_bytes": wb_bytes,
+                "writeback_GBs": round(wb_bytes / (wb_ms * 1e-3) / 1e9, 2),
+                "writeback_us_per_step_amortised": round(wb_ms * 1e3 / page, 2)}
+    finally:
+        hs.close()
+
+
 def ctypes_fill(addr: int, nbytes: int) -> None:
     import ctypes
 
@@ -140,6 +184,7 @@ def main() -> int:
                     help="skip the replay of the same steps through the synchronous path")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph replay of the same steps")
     ap.add_argument("--no-decode-only", action="store_true", help="skip the decode-only timing")
+    ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -371,6 +416,12 @@ def main() -> int:
                 "alg_bytes_per_launch": d["alg_bytes_per_launch"],
                 "traffic_read_write": [pmc["read_bytes_per_launch"], pmc["write_bytes_per_launch"]] if pmc else None}
 
+    residency = None
+    if not args.no_residency:
+        log("residency transitions (append, write-back)")
+        residency = residency_probe(torch, H, w, dev)
+        log(f"residency: {residency}")
+
     probe = None
     if not args.no_probe:
         log("host-link probe")
@@ -435,6 +486,7 @@ def main() -> int:
                                              "achieved_GBs": round(dec_bytes / (dec_layer_us * 1e-6) / 1e9, 2),
                                              "frac_of_hbm": round(dec_bytes / (dec_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                                                   4)}} if dec_us else None,
+        "residency": residency,
         "host_link": probe,
         "cpu_baseline": cpu,
     }
