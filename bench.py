@@ -185,6 +185,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph replay of the same steps")
     ap.add_argument("--no-decode-only", action="store_true", help="skip the decode-only timing")
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
+    ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
+    ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -237,6 +239,8 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
     hs.set_pipeline(0, args.fetch_wg, args.tail_chunks)
+    if args.policy != "lru":
+        hs.set_replacement(args.policy, args.policy_seed)
 
     def step(t, s=None):
         H.hisparse_step(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(), d_q[t].data_ptr(), w.scale,
@@ -463,7 +467,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "requests": R, "ctx": int(w.ctx_len[0]), "layers": L,
                    "index_share": w.index_share, "heads": Hh, "top_k": K, "hot_slots": B,
-                   "seed": w.seed, "host_coherent": args.host_coherent},
+                   "seed": w.seed, "host_coherent": args.host_coherent, "policy": args.policy},
         "roofline": roofline,
         "kernels": kern,
         "step": {"us": round(ms_step * 1e3, 2),

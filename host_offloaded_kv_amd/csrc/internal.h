@@ -102,6 +102,8 @@ struct ResolveArgs {
   int32_t hot_slots;
   int32_t page_shift;
   int64_t resident_rows;
+  int32_t policy;           // HISPARSE_POLICY_*
+  uint64_t policy_seed;     // random replacement: SplitMix64 seed
   int16_t* posmap;          // [L][sum ctx] position -> slot (-1: not in the hot buffer)
   const int64_t* map_off;   // [R] offset of request r within a layer's map
   int64_t map_layer_stride; // sum of ctx_r
@@ -166,6 +168,8 @@ struct hisparse_pool {
   std::vector<uint16_t*> kv;            // [L]
   int64_t kv_rows = 0;
   size_t resolve_lds = 0;
+  int32_t policy = HISPARSE_POLICY_LRU;
+  uint64_t policy_seed = 0;
   // device views into the workspace
   int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d, *cap_d, *hv_d;
   int16_t* posmap;

@@ -445,6 +445,8 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   while ((1 << ps) < p->cfg.page_size) ++ps;
   a.page_shift = ps;
   a.resident_rows = p->cfg.resident_rows_per_layer;
+  a.policy = p->policy;
+  a.policy_seed = p->policy_seed;
   a.posmap = p->posmap;
   a.map_off = p->map_off;
   a.map_layer_stride = p->lay.posmap_entries / p->cfg.num_layers;
@@ -750,6 +752,16 @@ hisparse_status hisparse_set_pages(hisparse_pool* p, int32_t r, int32_t first_pa
   e = hipMemcpyAsync(p->bt + off + first_page, host_blocks, (size_t)n * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_set_pages");
+}
+
+hisparse_status hisparse_set_replacement(hisparse_pool* p, int32_t policy, uint64_t seed, void* stream) {
+  if (!p || (policy != HISPARSE_POLICY_LRU && policy != HISPARSE_POLICY_FIFO && policy != HISPARSE_POLICY_RANDOM)) {
+    set_error("hisparse_set_replacement: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  p->policy = policy;
+  p->policy_seed = seed;
+  return hisparse_reset_state(p, stream);
 }
 
 hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_workgroups,

@@ -83,7 +83,9 @@ __host__ __device__ inline LdsMap lds_map(int K, int B) {
   m.vic = m.mj + 4 * (size_t)K;
   m.tflag = m.vic + 4 * (size_t)K;
   m.region = m.tflag + round16((size_t)B);
-  m.total = m.region + 8 * (size_t)next_pow2(K);  // (position, index) sort keys, slow path only
+  // sort keys: (position, index) on the unsorted-input path, (priority,
+  // slot) of the random replacement policy
+  m.total = m.region + 8 * (size_t)next_pow2(K > B ? K : B);
   return m;
 }
 
@@ -127,13 +129,28 @@ __device__ void bitonic_sort(unsigned long long* k, int n, int tid) {
   }
 }
 
+// SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): the generator's output for
+// state x -- add the golden gamma, then the mixing function.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 // One workgroup (16 wavefronts) per (request, layer).
 //  * The position -> slot page table is a persistent int16 map over the
 //    request's positions in device memory (exact: map[p] = s iff owner[s] =
 //    p), so a lookup is one gather and a fill changes two entries.
 //  * Pinning is a byte per slot in LDS (bit 0: hit or filled by this call;
 //    bit 1: already stamped with this step by an earlier call of the same
-//    step).  Stamps themselves are only written, except on that rare path.
+//    step; bit 2: stamped by this call -- every fill, and hits except under
+//    FIFO).  Stamps themselves are only written, except on that rare path.
+//  * Replacement policy (the HiSparse summary article, section 04, compares
+//    LRU with FIFO and random): LRU and FIFO take victims from the order
+//    array (sorted by the stamp, which FIFO does not refresh on a hit);
+//    random sorts (empty slots by index, then (31-bit SplitMix64 priority,
+//    slot)) over the unpinned slots.
 //  * Order-preserving compactions (misses in input order, victims in order
 //    array order, the rebuilt order array) give each wave a contiguous range,
 //    keep its ballots in registers, exchange the sixteen counts through LDS
@@ -277,8 +294,12 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
           ++n_res;
         } else if (sv[c] >= 0) {
           const int s = sv[c];
-          tflag_s[s] |= 1;
-          stamp_g[s] = t;
+          if (a.policy == HISPARSE_POLICY_FIFO) {
+            tflag_s[s] |= 1;  // pinned; the fill stamp stays
+          } else {
+            tflag_s[s] |= 5;
+            stamp_g[s] = t;
+          }
           row = (int)(hot_base + s);
           ++n_hit;
         } else {
@@ -321,6 +342,25 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     __syncthreads();
   }
 
+  if (a.policy == HISPARSE_POLICY_RANDOM) {
+    // Victims: empty slots by index, then ascending (priority, slot); the
+    // priority of slot s is the top 31 bits of SplitMix64(k ^ s) with k
+    // derived from (seed, t, layer, request).
+    const uint64_t k = splitmix64(splitmix64(splitmix64(a.policy_seed) ^ (uint64_t)(uint32_t)t) ^
+                                  (((uint64_t)(uint32_t)l << 32) | (uint32_t)r));
+    const int BP = next_pow2(B);
+    for (int i = tid; i < BP; i += kMetaThreads) {
+      unsigned long long key = ~0ull;
+      if (i < B && !(tflag_s[i] & 1)) {
+        key = owner_g[i] < 0 ? (unsigned long long)i
+                             : ((1ull << 63) | ((splitmix64(k ^ (uint64_t)i) >> 33) << 32) | (uint32_t)i);
+      }
+      key_s[i] = key;
+    }
+    __syncthreads();
+    bitonic_sort(key_s, BP, tid);
+    for (int i = tid; i < m; i += kMetaThreads) vic_s[i] = (int)(uint32_t)key_s[i];
+  } else {
   // Victims: the first m unpinned slots of the (stamp, slot) order array.
   {
     uint64_t vb[kSlotChunks];
@@ -345,6 +385,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
       run += __popcll(vb[c]);
     }
   }
+  }
   __syncthreads();
 
   // Fill: i-th smallest missing position -> i-th victim.  The evicted
@@ -358,7 +399,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     map[p] = (int16_t)v;
     owner_g[v] = p;
     stamp_g[v] = t;
-    tflag_s[v] |= 1;
+    tflag_s[v] |= 5;
     rows_out[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
@@ -373,8 +414,9 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     for (int c = 0; c < kSlotChunks; ++c) {
       const int i = ib + 64 * c + lane;
       const bool in = c < nsc && i < ie;
-      ka[c] = __ballot(in && tflag_s[lv[c]] == 0);
-      kb[c] = __ballot(in && tflag_s[i] != 0);
+      // stamp < t: neither stamped by this call nor earlier in this step
+      ka[c] = __ballot(in && (tflag_s[lv[c]] & 6) == 0);
+      kb[c] = __ballot(in && (tflag_s[i] & 6) != 0);
       ca += __popcll(ka[c]);
       cb += __popcll(kb[c]);
     }

@@ -32,6 +32,12 @@ HISPARSE_ERR_STEP = 4
 HISPARSE_ERR_ROW = 8
 HISPARSE_ERR_APPEND = 16
 HISPARSE_ERR_UNMATERIALIZED = 32
+
+# replacement policies (hisparse_set_replacement)
+HISPARSE_POLICY_LRU = 0
+HISPARSE_POLICY_FIFO = 1
+HISPARSE_POLICY_RANDOM = 2
+POLICIES = {"lru": HISPARSE_POLICY_LRU, "fifo": HISPARSE_POLICY_FIFO, "random": HISPARSE_POLICY_RANDOM}
 ERR_RANGE = 1
 ERR_DUP = 2
 ERR_STEP = 4
@@ -44,6 +50,7 @@ EXPORTED = (
     "hisparse_sparse_mla_decode_layers",
     "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
+    "hisparse_set_replacement",
     "hisparse_export_state", "hisparse_check_errors",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
     "hisparse_profile_enable", "hisparse_profile_read",
@@ -108,6 +115,7 @@ def load() -> ctypes.CDLL:
         "hisparse_reset_state": (_I32, [_VP, _VP]),
         "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
         "hisparse_append": (_I32, [_VP, _VP, _VP]),
+        "hisparse_set_replacement": (_I32, [_VP, _I32, ctypes.c_uint64, _VP]),
         "hisparse_writeback": (_I32, [_VP, _VP]),
         "hisparse_set_pages": (_I32, [_VP, _I32, _I32, _I32, _VP, _VP]),
         "hisparse_get_lengths": (_I32, [_VP, _VP, _VP, _VP]),
@@ -214,6 +222,10 @@ def hisparse_reset_state(pool: int, stream: int) -> None:
 def hisparse_set_pipeline(pool: int, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
                           tail_chunks: int = 0) -> None:
     _check(load().hisparse_set_pipeline(pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks))
+
+
+def hisparse_set_replacement(pool: int, policy: int, seed: int, stream: int) -> None:
+    _check(load().hisparse_set_replacement(pool, policy, seed & ((1 << 64) - 1), stream))
 
 
 def hisparse_append(pool: int, d_rows: int, stream: int) -> None:
@@ -343,6 +355,9 @@ class HiSparse:
     def set_pipeline(self, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
                      tail_chunks: int = 0) -> None:
         hisparse_set_pipeline(self.pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks)
+
+    def set_replacement(self, policy: str, seed: int = 0) -> None:
+        hisparse_set_replacement(self.pool, POLICIES[policy], seed, self.stream)
 
     def append(self, d_rows) -> None:
         hisparse_append(self.pool, d_rows.data_ptr(), self.stream)

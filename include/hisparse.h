@@ -74,6 +74,11 @@ typedef int32_t hisparse_status;
 #define HISPARSE_ERR_APPEND 16u /* append with the tail page not resident or the context full (not appended) */
 #define HISPARSE_ERR_UNMATERIALIZED 32u /* a row was needed from the host pool before it was written there */
 
+/* Replacement policies (hisparse_set_replacement). */
+#define HISPARSE_POLICY_LRU 0    /* victims: least recently used first (default) */
+#define HISPARSE_POLICY_FIFO 1   /* victims: earliest filled first; a hit does not refresh */
+#define HISPARSE_POLICY_RANDOM 2 /* victims: empty slots, then a per-call random order */
+
 typedef struct hisparse_pool hisparse_pool;
 
 typedef struct {
@@ -248,6 +253,22 @@ hisparse_status hisparse_set_pages(hisparse_pool* pool, int32_t r, int32_t first
 /* Read ctx_r ([R]) and held_lr ([L][R]) into host arrays.  Synchronises
  * `stream`.  Errors: EINVAL, EHIP. */
 hisparse_status hisparse_get_lengths(hisparse_pool* pool, int32_t* host_ctx, int32_t* host_held, void* stream);
+
+/* Replacement policy of every (request, layer), for the comparison in the
+ * HiSparse summary article (section 04: LRU against FIFO and random
+ * replacement).  All policies pin the current selection and fill the i-th
+ * smallest missing position into the i-th victim; the victims are the
+ * unpinned slots in ascending order of
+ *   LRU:    (step of last use, slot);
+ *   FIFO:   (step of the fill, slot) -- stamps hold fill steps;
+ *   RANDOM: empty slots first (by slot), then (priority, slot), where the
+ *           priority of slot s is SplitMix64(k ^ s) >> 33 with
+ *           k = SplitMix64(SplitMix64(SplitMix64(seed) ^ t) ^ (layer << 32 | r))
+ *           and SplitMix64(x) the generator's output for state x (add
+ *           0x9E3779B97F4A7C15, then its mixing function).
+ * Resets the pool to the empty state (as hisparse_reset_state, so it
+ * synchronises `stream`).  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, uint64_t seed, void* stream);
 
 /* Tuning of the fetch and of hisparse_step's pipeline (0 = default):
  *   group_fetch_workgroups: 1024-thread workgroups of the whole-group miss

@@ -70,13 +70,18 @@ class ResolveResult:
 
 
 def resolve(state: LruState, sel, t: int, ctx: int, block_table, page_size: int,
-            hot_base: int) -> ResolveResult:
+            hot_base: int, policy: str = "lru", priority=None, next_use=None) -> ResolveResult:
     """One RESOLVE call for one (request, layer); mutates ``state``.
 
     ``sel``: the K selected logical positions (-1 = padding), in the
     indexer's order.  ``block_table[page]``: block id of a GPU-resident page,
     or -1 for a page that lives only on the host.  Resident row ids are
     ``block * page_size + offset``; hot row ids are ``hot_base + slot``.
+
+    ``policy`` picks the victim order (``oracle.policy``): "lru" (default),
+    "fifo", "random" (``priority(slot)`` gives this call's priorities) or
+    "belady" (``next_use(p)`` gives the next step that selects p).  Stamps
+    hold the step of last use, except under FIFO the step of the fill.
     """
     B = state.hot_slots
     K = len(sel)
@@ -111,7 +116,8 @@ def resolve(state: LruState, sel, t: int, ctx: int, block_table, page_size: int,
             n_res += 1
         elif p in state.slot_of:
             s = state.slot_of[p]
-            state.stamp[s] = t
+            if policy != "fifo":
+                state.stamp[s] = t
             pinned[s] = True
             rows[j] = hot_base + s
             n_hit += 1
@@ -121,8 +127,17 @@ def resolve(state: LruState, sel, t: int, ctx: int, block_table, page_size: int,
     # Misses are filled in ascending logical order; victims are the unpinned
     # slots in ascending (stamp, slot) order.
     misses.sort()
-    candidates = sorted((state.stamp[s], s) for s in range(B) if not pinned[s])
-    victims = [s for _, s in candidates[: len(misses)]]
+    free = [s for s in range(B) if not pinned[s]]
+    if policy in ("lru", "fifo"):
+        candidates = sorted((state.stamp[s], s) for s in free)
+    elif policy == "random":
+        candidates = sorted(((0, s) if state.owner[s] < 0 else (1 + priority(s), s)) for s in free)
+    elif policy == "belady":
+        candidates = sorted(((0, 0.0, s) if state.owner[s] < 0 else (1, -next_use(state.owner[s]), s))
+                            for s in free)
+    else:
+        raise ValueError(f"unknown policy {policy}")
+    victims = [c[-1] for c in candidates[: len(misses)]]
     fetches = []
     for (p, j), v in zip(misses, victims):
         old = state.owner[v]

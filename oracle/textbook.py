@@ -26,3 +26,46 @@ def miss_sequence(accesses, capacity: int) -> list:
             cache[a] = True
             out.append(True)
     return out
+
+
+def fifo_miss_sequence(accesses, capacity: int) -> list:
+    """True/False per access in a first-in-first-out cache: a hit leaves the
+    queue unchanged; a miss on a full cache evicts the oldest insertion."""
+    from collections import deque
+
+    queue, present, out = deque(), set(), []
+    for a in accesses:
+        if a in present:
+            out.append(False)
+            continue
+        if len(queue) >= capacity:
+            present.discard(queue.popleft())
+        queue.append(a)
+        present.add(a)
+        out.append(True)
+    return out
+
+
+def min_miss_sequence(accesses, capacity: int) -> list:
+    """True/False per access in Belady's MIN cache (L. A. Belady, "A study of
+    replacement algorithms for a virtual-storage computer", IBM Systems
+    Journal 5(2), 1966): on a miss with a full cache, evict the resident
+    item whose next access is furthest away (never again counts as
+    furthest).  Quadratic look-ahead; tiny streams only."""
+    cache, out = [], []
+    for i, a in enumerate(accesses):
+        if a in cache:
+            out.append(False)
+            continue
+        if len(cache) >= capacity:
+            def next_access(x):
+                for k in range(i + 1, len(accesses)):
+                    if accesses[k] == x:
+                        return k
+                return float("inf")
+            dist = [next_access(x) for x in cache]
+            far = max(range(len(cache)), key=lambda k: (dist[k], -k))
+            cache.pop(far)
+        cache.append(a)
+        out.append(True)
+    return out

@@ -379,3 +379,84 @@ def test_growth_transitions(seed):
             assert got == [(r, int(p)) for p in sel if p >= 0]
         drops_seen += len(sch.post[t])
     assert drops_seen > 0, "the trace exercises pages turning into placeholders"
+
+
+# --------------------------------------------------------------------------
+# P13: replacement policies of the HiSparse summary article's comparison
+# (section 04: LRU vs FIFO, random and Belady).
+# --------------------------------------------------------------------------
+def test_splitmix64_published_outputs():
+    from oracle.policy import GAMMA, MASK64, splitmix64
+
+    # first outputs of SplitMix64 from state 0 (reference implementation)
+    state, out = 0, []
+    for _ in range(3):
+        out.append(splitmix64(state))
+        state = (state + GAMMA) & MASK64
+    assert out == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def _k1_policy_misses(stream, b, policy, seed=3):
+    from oracle.policy import next_use_table, random_priority
+
+    st = LruState(b)
+    nu = next_use_table([[p] for p in stream])
+    out = []
+    for t, p in enumerate(stream):
+        res = resolve(st, [p], t, 10_000, [-1] * 200, 64, 0, policy=policy,
+                      priority=random_priority(seed, t, 0, 0), next_use=lambda q, t=t: nu(t, q))
+        out.append(res.n_miss == 1)
+    return out
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 8])
+def test_k1_fifo_and_belady_are_textbook(b):
+    rng = np.random.default_rng(77 + b)
+    for trial in range(6):
+        stream = [int(x) for x in rng.integers(0, 3 * b + 2, size=300)]
+        assert _k1_policy_misses(stream, b, "fifo") == textbook.fifo_miss_sequence(stream, b)
+        bel = _k1_policy_misses(stream, b, "belady")
+        assert sum(bel) == sum(textbook.min_miss_sequence(stream, b))
+        # MIN is optimal for demand paging: no online policy misses less
+        for pol in ("lru", "fifo", "random"):
+            assert sum(bel) <= sum(_k1_policy_misses(stream, b, pol))
+
+
+@pytest.mark.parametrize("policy", ["lru", "fifo", "random", "belady"])
+def test_policies_miss_only_on_first_touch_when_buffer_is_large(policy):
+    from oracle.policy import next_use_table, random_priority
+
+    rng = np.random.default_rng(11)
+    ctx, k = 60, 8
+    sels = [list(rng.choice(ctx, size=k, replace=False)) for _ in range(30)]
+    nu = next_use_table(sels)
+    st = LruState(ctx)
+    seen = set()
+    for t, sel in enumerate(sels):
+        res = resolve(st, sel, t, ctx, [-1] * 1, 64, 0, policy=policy, priority=random_priority(5, t, 0, 0),
+                      next_use=lambda q, t=t: nu(t, q))
+        assert res.n_miss == len(set(sel) - seen)
+        seen |= set(sel)
+
+
+def test_random_victims_are_uniform():
+    # one miss per call into a full buffer with one pinned hit: the victim is
+    # one of the B - 1 unpinned slots, each equally likely
+    from oracle.policy import random_priority
+
+    b = 8
+    counts = np.zeros(b)
+    for t in range(4000):
+        st = LruState(b)
+        for s in range(b):
+            st.owner[s] = s
+            st.slot_of[s] = s
+            st.stamp[s] = 0
+        res = resolve(st, [0, 100], t + 1, 1000, [-1] * 20, 64, 0, policy="random",
+                      priority=random_priority(9, t, 0, 0))
+        assert res.n_hit == 1 and res.n_miss == 1
+        counts[res.fetches[0][1]] += 1
+    assert counts[0] == 0  # the pinned slot is never the victim
+    exp = 4000 / (b - 1)
+    chi2 = ((counts[1:] - exp) ** 2 / exp).sum()
+    assert chi2 < 24.3  # 99.9th percentile of chi-square with 6 degrees of freedom
