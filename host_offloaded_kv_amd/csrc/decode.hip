@@ -20,9 +20,10 @@
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
 //    every head of the group (fp32 accumulators in AGPRs); it multiplies the
 //    transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo
-//    (one tile read, two MFMAs), and it also loads
-//    the tiles: global loads into registers one tile ahead, stored to LDS
-//    after use.
+//    (one tile read, two MFMAs).
+// Both roles stage the row tiles: the value waves gather the even tiles and
+// the score waves the odd ones, each through registers two tiles ahead, so
+// two tiles' loads are in flight per workgroup while a third is consumed.
 // The value waves run one tile behind the score waves, so each tile costs a
 // single workgroup barrier and the two waves sharing a SIMD overlap each
 // other's LDS and softmax latency with MFMA work.  Split partials are merged
@@ -75,7 +76,7 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
 }
 
 // Tile loads go through VGPRs: each loading thread fetches 9 16-byte chunks
-// of a tile with ordinary global loads one tile ahead, and writes them to
+// of a tile with ordinary global loads two tiles ahead, and writes them to
 // LDS after the current tile's work.  On MI355X this sustains ~7.3 TB/s for a random
 // 1152-byte row gather, where direct-to-LDS loads stayed under 3 TB/s.  The
 // loads use global-address-space pointers: flat loads would also count
@@ -152,65 +153,49 @@ __device__ __forceinline__ void agpr_drain(f32x4 (&acc)[N]) {
 }
 
 template <int HG>
-__global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
-  constexpr int NBP = HG / 16;  // 16-head blocks
-  __shared__ __align__(16) unsigned char xs[kNBuf][kTileBytes];
-  __shared__ __align__(16) uint16_t ps[2][2][HG][kPPitch];  // [tile parity][hi, lo][head][row]
-  __shared__ int rowid_all[kMaxTopK];
-  __shared__ float lred[HG];
-  __shared__ float lexact_s[HG];
-  __shared__ float mfin_s[HG];
-  __shared__ int overflow_s;
+struct DecodeSmem {
+  unsigned char xs[kNBuf][kTileBytes];  // row tiles: scored, multiplied, being stored
+  uint16_t ps[2][2][HG][kPPitch];       // [tile parity][hi, lo][head][row]
+  int rowid[kMaxTopK];                  // row ids of the workgroup's K range
+  float lsum[HG], lexact[HG], mfin[HG];
+  int overflow;
+};
 
-  const int H = a.num_heads, R = a.num_requests, K = a.top_k;
-  // XCD-aware order: consecutive logical blocks (the head groups and splits
-  // of one request) share blockIdx % 8, i.e. one XCD and its L2.
-  int li = blockIdx.x;
-  if (gridDim.x % 8 == 0) li = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const int split = li % a.splits;
-  li /= a.splits;
-  const int hg = li % nhg;
-  const int pair = li / nhg;
-  const int l = a.layer_begin + pair / R;
-  const uint16_t* kv = a.kv[l];
-  const int32_t* rows = a.rows + (size_t)pair * K;
+// Iteration it of either role ends by moving tile it+1 from registers to its
+// LDS slot (last read in iteration it-1), if this role stages it, and then
+// starting the load of tile it+3 into the same registers.  The value waves
+// stage the even tiles and the score waves the odd ones, so two tiles'
+// loads are in flight while a third is consumed.
+template <int HG>
+__device__ __forceinline__ void stage_next(u32x4* st, DecodeSmem<HG>& sm, const uint16_t* kv, int it, int n_tiles,
+                                           int parity, int lt) {
+  const int nx = it + 1;
+  if (nx < n_tiles && (nx & 1) == parity) {
+    store_tile(st, sm.xs[nx % kNBuf], lt);
+    if (nx + 2 < n_tiles) load_tile(st, kv, sm.rowid + (nx + 2) * kT, lt);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, g = lane >> 4, i16 = lane & 15;
-  const bool score_wave = w < 4;
-  const bool s_active = score_wave && 16 * w < HG;  // score wave with heads to own
-  const int cw = w - 4;                             // value wave: column block
-  const int lt = tid - 256;                         // value wave: loader thread index
-
-  int per = (K + a.splits - 1) / a.splits;
-  per = (per + kT - 1) / kT * kT;
-  const int k0 = split * per;
-  const int k1 = min(K, k0 + per);
-  const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
-
-  // One AGPR-resident array serves both roles, so the compiler allocates
-  // it once: a value wave accumulates O^T in acc[mb * NBP + nb]; a score
-  // wave keeps the Q of its 16 heads in acc[0 .. 18) as MFMA B operands
-  // (lane (g, i16) holding dims 32 s + 8 g .. +7 of head 16 w + i16).
-  constexpr int kAcc = 8 * NBP > kLatent / 32 ? 8 * NBP : kLatent / 32;
-  f32x4 acc[kAcc];
-  u32x4 st[kStage];  // value wave: one tile of staged loads
-  float m_run = -INFINITY, m_seen = -INFINITY, l_run = 0.f, l_exact = 0.f;
-  if (s_active) {
-    const int head = hg * HG + 16 * w + i16;
-    gu32x4* qp = (gu32x4*)(a.q + ((size_t)pair * H + head) * kLatent + 8 * g);
+// Score waves 0-3: wave w owns heads 16w .. 16w+15 of the group.  Each role
+// runs its own loop with the same barriers, so the registers of one role
+// (Q here, the O accumulators there) are never live in the other.
+template <int HG>
+__device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
+                                           size_t head0, int n_tiles, int w, int g, int i16, int tid) {
+  const bool active = 16 * w < HG;  // waves past the group's heads only stage tiles
+  // Q of the wave's 16 heads as MFMA B operands in AGPRs: lane (g, i16)
+  // holds dims 32 s + 8 g .. +7 of head 16 w + i16.
+  f32x4 q[kLatent / 32];
+  if (active) {
+    gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * w + i16) * kLatent + 8 * g);
 #pragma unroll
-    for (int s = 0; s < kLatent / 32; ++s) acc[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
+    for (int s = 0; s < kLatent / 32; ++s) q[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
     asm volatile("s_nop 4" ::: "memory");  // AGPR writes -> MFMA reads
 #pragma unroll
-    for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+a"(acc[s]), "+a"(acc[s + 1]));
+    for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+a"(q[s]), "+a"(q[s + 1]));
   }
-
-  // Row ids of the whole K range, validated once.
-  for (int k = tid; k < n_tiles * kT; k += kThreads) rowid_all[k] = load_row_id(a, rows, k0 + k, k1);
-  if (tid == 0) overflow_s = 0;
-  __syncthreads();
+  u32x4 st[kStage];
+  float m_run = -INFINITY, m_seen = -INFINITY, l_run = 0.f, l_exact = 0.f;
 
   // Softmax with a fixed reference max per head: the first valid tile sets
   // m, and P = 2^(s*scale*log2e - m) accumulates unnormalised, so the O
@@ -219,100 +204,139 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   // is recomputed once with m = the true maximum, which no tile can exceed.
   // Both passes give the exact softmax.
   for (int pass = 0; pass < 2; ++pass) {
-    if (!score_wave) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBP; ++nb) zero_agpr(acc[mb * NBP + nb]);
-      if (n_tiles > 0) {
-        load_tile(st, kv, rowid_all, lt);
-        store_tile(st, xs[0], lt);
-      }
-      if (n_tiles > 1) load_tile(st, kv, rowid_all + kT, lt);
-    }
+    if (n_tiles > 1) load_tile(st, kv, sm.rowid + kT, tid);
     l_run = 0.f;
     l_exact = 0.f;
     lds_barrier();
-
-    // Iteration it: score tile it, multiply tile it-1.
     for (int it = 0; it <= n_tiles; ++it) {
-      if (score_wave) {
-        if (s_active && it < n_tiles) {
-          const unsigned char* xb = xs[it % kNBuf];
-          const int* rowid_t = rowid_all + it * kT;
-          f32x4 sacc[2];
-          // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
-          const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
+      if (active && it < n_tiles) {
+        const unsigned char* xb = sm.xs[it % kNBuf];
+        const int* rowid_t = sm.rowid + it * kT;
+        f32x4 sacc[2];
+        // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
+        const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
 #pragma unroll
-          for (int s = 0; s < kLatent / 32; ++s) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
-            if (s == 0) {
-              mfma_score_first(sacc[0], a0, acc[0]);
-              mfma_score_first(sacc[1], a1, acc[0]);
-            } else {
-              mfma_score(sacc[0], a0, acc[s]);
-              mfma_score(sacc[1], a1, acc[s]);
-            }
-            if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
+        for (int s = 0; s < kLatent / 32; ++s) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
+          if (s == 0) {
+            mfma_score_first(sacc[0], a0, q[0]);
+            mfma_score_first(sacc[1], a1, q[0]);
+          } else {
+            mfma_score(sacc[0], a0, q[s]);
+            mfma_score(sacc[1], a1, q[s]);
           }
-          score_drain(sacc[0], sacc[1]);
-          // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
-          bool valid[2][4];
-          float mx = -INFINITY;
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              valid[rb][v] = rowid_t[16 * rb + 4 * g + v] >= 0;
-              sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * a.scale_log2 : -INFINITY;
-              mx = fmaxf(mx, sacc[rb][v]);
-            }
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          m_seen = fmaxf(m_seen, mx);
-          if (m_run == -INFINITY) {
-            m_run = mx;  // first valid rows of this head: O and l are still zero
-          } else if (mx > m_run + kMaxGrowLog2) {
-            overflow_s = 1;  // this pass is discarded; P may overflow below
-          }
-          uint16_t* prow_hi = &ps[it & 1][0][16 * w + i16][0];
-          uint16_t* prow_lo = &ps[it & 1][1][16 * w + i16][0];
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            float p[4], r[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
-            l_exact += (p[0] + p[1]) + (p[2] + p[3]);
-            const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-            const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
-                                __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
-#pragma unroll
-            for (int v = 0; v < 4; ++v) r[v] = p[v] - h[v];  // exact in fp32
-            const u32x2 lo = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-            *reinterpret_cast<u32x2*>(prow_hi + 16 * rb + 4 * g) = hi;
-            *reinterpret_cast<u32x2*>(prow_lo + 16 * rb + 4 * g) = lo;
-            // O is normalised by the sum of the weights PV actually multiplies
-            // (P_hi + P_lo), so it is a convex combination of the value rows;
-            // lse uses the sum of the unrounded weights.
-            l_run += ((h[0] + __uint_as_float(lo[0] << 16)) + (h[1] + __uint_as_float(lo[0] & 0xFFFF0000u))) +
-                     ((h[2] + __uint_as_float(lo[1] << 16)) + (h[3] + __uint_as_float(lo[1] & 0xFFFF0000u)));
-          }
+          if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
         }
-      } else if (it >= 1) {
-        // ---- O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T[32 x HG] ----
+        score_drain(sacc[0], sacc[1]);
+        // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
+        bool valid[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            valid[rb][v] = rowid_t[16 * rb + 4 * g + v] >= 0;
+            sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sacc[rb][v]);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_seen = fmaxf(m_seen, mx);
+        if (m_run == -INFINITY) {
+          m_run = mx;  // first valid rows of this head: O and l are still zero
+        } else if (mx > m_run + kMaxGrowLog2) {
+          sm.overflow = 1;  // this pass is discarded; P may overflow below
+        }
+        uint16_t* prow_hi = &sm.ps[it & 1][0][16 * w + i16][0];
+        uint16_t* prow_lo = &sm.ps[it & 1][1][16 * w + i16][0];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float p[4], r[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
+          l_exact += (p[0] + p[1]) + (p[2] + p[3]);
+          const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+          const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
+                              __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) r[v] = p[v] - h[v];  // exact in fp32
+          const u32x2 lo = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+          *reinterpret_cast<u32x2*>(prow_hi + 16 * rb + 4 * g) = hi;
+          *reinterpret_cast<u32x2*>(prow_lo + 16 * rb + 4 * g) = lo;
+          // O is normalised by the sum of the weights PV actually multiplies
+          // (P_hi + P_lo), so it is a convex combination of the value rows;
+          // lse uses the sum of the unrounded weights.
+          l_run += ((h[0] + __uint_as_float(lo[0] << 16)) + (h[1] + __uint_as_float(lo[0] & 0xFFFF0000u))) +
+                   ((h[2] + __uint_as_float(lo[1] << 16)) + (h[3] + __uint_as_float(lo[1] & 0xFFFF0000u)));
+        }
+      }
+      stage_next(st, sm, kv, it, n_tiles, 1, tid);
+      lds_barrier();
+    }
+    if (!sm.overflow) break;
+    m_run = m_seen;
+    lds_barrier();
+  }
+
+  // Normaliser, reference max and exact weight sum per head for the value waves.
+  if (active) {
+    float ls = l_run, le = l_exact;
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    le += __shfl_xor(le, 16, 64);
+    le += __shfl_xor(le, 32, 64);
+    if (g == 0) {
+      sm.lsum[16 * w + i16] = ls;
+      sm.lexact[16 * w + i16] = le;
+      sm.mfin[16 * w + i16] = m_run;
+    }
+  }
+  __syncthreads();
+}
+
+// Value waves 4-7: wave 4+cw owns output columns 128cw .. 128cw+127 of every
+// head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
+template <int HG>
+__device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
+                                           size_t head0, int pair, int split, int hg, int n_tiles, int cw, int g,
+                                           int i16, int lt) {
+  constexpr int NBP = HG / 16;  // 16-head blocks
+  f32x4 acc[8 * NBP];           // acc[mb * NBP + nb]: columns 16 mb.., heads 16 nb..
+  u32x4 st[kStage];
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBP; ++nb) zero_agpr(acc[mb * NBP + nb]);
+    // Tile 0 goes straight to LDS; tile 2 stays in flight in registers
+    // (tile 1 is the score waves').
+    if (n_tiles > 0) {
+      load_tile(st, kv, sm.rowid, lt);
+      store_tile(st, sm.xs[0], lt);
+    }
+    if (n_tiles > 2) load_tile(st, kv, sm.rowid + 2 * kT, lt);
+    lds_barrier();
+    // Iteration it multiplies tile it-1 (the score waves score tile it).
+    for (int it = 0; it <= n_tiles; ++it) {
+      if (it >= 1) {
         const int tp = it - 1;
-        const unsigned char* xb = xs[tp % kNBuf];
+        const unsigned char* xb = sm.xs[tp % kNBuf];
         u32x4 bp[NBP], bq[NBP];  // P_hi, P_lo operands
 #pragma unroll
         for (int nb = 0; nb < NBP; ++nb) {
-          bp[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][0][16 * nb + i16][8 * g]);
-          bq[nb] = *reinterpret_cast<const u32x4*>(&ps[tp & 1][1][16 * nb + i16][8 * g]);
+          bp[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][0][16 * nb + i16][8 * g]);
+          bq[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][1][16 * nb + i16][8 * g]);
         }
         // Transposed A operand: lane i16 of each 16-lane group supplies row
         // j0 + i16/4, columns c0 + 4 (i16 % 4) .. +3, and receives column
-        // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).
-        const lds_u8* xl = (const lds_u8*)xb + (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
+        // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).  The
+        // transposed-read builtin takes no immediate offset, so an opaque
+        // per-iteration base keeps the compiler from hoisting 16
+        // precomputed addresses out of the loop.
+        uint32_t xoff = (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
+        asm volatile("" : "+v"(xoff));
+        const lds_u8* xl = (const lds_u8*)xb + xoff;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
           const s16x4 lo =
@@ -328,42 +352,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
           if (mb & 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (!score_wave && it + 1 < n_tiles) {
-        // Tile it+1: registers -> its LDS slot (last read two iterations ago),
-        // then start loading tile it+2.
-        store_tile(st, xs[(it + 1) % kNBuf], lt);
-        if (it + 2 < n_tiles) load_tile(st, kv, rowid_all + (it + 2) * kT, lt);
-      }
+      stage_next(st, sm, kv, it, n_tiles, 0, lt);
       lds_barrier();
     }
-    if (!overflow_s) break;
-    m_run = m_seen;
+    if (!sm.overflow) break;
     lds_barrier();
   }
+  __syncthreads();  // the score waves' normalisers are in LDS
 
-  // ---- epilogue: normaliser per head, then O / l and lse ------------------
-  if (s_active) {
-    float ls = l_run, le = l_exact;
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    le += __shfl_xor(le, 16, 64);
-    le += __shfl_xor(le, 32, 64);
-    if (g == 0) {
-      lred[16 * w + i16] = ls;
-      lexact_s[16 * w + i16] = le;
-      mfin_s[16 * w + i16] = m_run;
-    }
-  }
-  __syncthreads();
-  if (score_wave) return;
   agpr_drain(acc);
-  const size_t head0 = (size_t)pair * H + hg * HG;
+  const int H = a.num_heads;
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
     const int h = nb * 16 + i16;
-    const float lsum = lred[h];
-    const float lex = lexact_s[h];
-    const float m = mfin_s[h];
+    const float lsum = sm.lsum[h];
+    const float lex = sm.lexact[h];
+    const float m = sm.mfin[h];
     if (a.splits == 1) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
       float* out = a.out + (head0 + h) * kVDim + 128 * cw + 4 * g;
@@ -390,6 +394,44 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
       }
     }
   }
+}
+
+template <int HG>
+__global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
+  __shared__ __align__(16) DecodeSmem<HG> sm;
+  const int H = a.num_heads, R = a.num_requests, K = a.top_k;
+  // XCD-aware order: consecutive logical blocks (the head groups and splits
+  // of one request) share blockIdx % 8, i.e. one XCD and its L2.
+  int li = blockIdx.x;
+  if (gridDim.x % 8 == 0) li = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int split = li % a.splits;
+  li /= a.splits;
+  const int hg = li % nhg;
+  const int pair = li / nhg;
+  const int l = a.layer_begin + pair / R;
+  const uint16_t* kv = a.kv[l];
+  const int32_t* rows = a.rows + (size_t)pair * K;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, i16 = lane & 15;
+
+  int per = (K + a.splits - 1) / a.splits;
+  per = (per + kT - 1) / kT * kT;
+  const int k0 = split * per;
+  const int k1 = min(K, k0 + per);
+  const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
+
+  // Row ids of the whole K range, validated once.
+  for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
+  if (tid == 0) sm.overflow = 0;
+  __syncthreads();
+
+  const size_t head0 = (size_t)pair * H + hg * HG;
+  if (w < 4)
+    score_role<HG>(a, sm, kv, head0, n_tiles, w, g, i16, tid);
+  else
+    value_role<HG>(a, sm, kv, head0, pair, split, hg, n_tiles, w - 4, g, i16, tid - 256);
 }
 
 // Merge the split partials of one (layer, request, head) per wavefront.
