@@ -12,14 +12,15 @@
 //
 // Work split: a workgroup handles (layer, request, group of up to 64 heads,
 // K split) with 8 wavefronts, two per SIMD, specialised by role:
-//  * score waves 0-3: wave w owns heads 16w .. 16w+15 of the group; it keeps
-//    their Q in registers, computes the 32x16 score block of each 32-row
-//    tile on 16x16x32 bf16 MFMA, applies the softmax (all rows of its heads
-//    are in the wave, so no cross-wave reduction is needed) and writes the
+//  * score waves 0-3: wave 2 hb + rb keeps the Q of 32 heads (16 when the
+//    group has 16) in registers and scores rows 16 rb .. 16 rb + 15 of each
+//    32-row tile on 16x16x32 bf16 MFMA, one LDS read of the rows feeding
+//    both 16-head blocks; it applies the softmax with a reference max that
+//    the two row halves of a head agree on once, and writes the
 //    probabilities P to LDS as two bf16 planes, P = P_hi + P_lo;
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
-//    every head of the group (fp32 accumulators in AGPRs); it multiplies the
-//    transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo
+//    every head of the group (fp32 accumulators in registers); it multiplies
+//    the transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo
 //    (one tile read, two MFMAs).
 // Both roles stage the row tiles: the value waves gather the even tiles and
 // the score waves the odd ones, each through registers two tiles ahead, so
@@ -101,55 +102,57 @@ __device__ __forceinline__ void store_tile(const u32x4* st, unsigned char* xs, i
 // not wait for outstanding global loads, so tile loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// D += A * B on a 16x16x32 bf16 MFMA (fp32 accumulate), compiler-scheduled.
-__device__ __forceinline__ void mfma16(f32x4& d, const u32x4& a, const u32x4& b) {
-  d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
-}
-
-// The value accumulators are pinned to AGPRs with inline asm ("a"
-// constraint); with the builtin the register allocator moves them between
-// register files around the MFMAs.  The compiler does not see these as
-// MFMAs, so the hazards they can meet are covered by hand:
+// All MFMAs are written as inline asm with every operand in VGPRs (the
+// kernel uses no AGPRs, so both roles may use up to 256 VGPRs at two waves
+// per SIMD); with the builtin the register allocator moves accumulators
+// between register files around the MFMAs.  The compiler does not see
+// these as MFMAs, so the hazards they can meet are covered by hand:
 //  * an operand written by a VALU instruction just before: two wait states
 //    in front of the first MFMA that reads a freshly assembled operand;
-//  * reading the accumulators afterwards (v_accvgpr_read): agpr_drain()
-//    inserts 128 wait states after the last MFMA;
-//  * the accumulators must never be copied by the compiler inside the loop
-//    (checked in the generated code), since such a copy would read an AGPR
-//    that an MFMA may still be writing.
+//  * reading results afterwards: score_drain() and acc_drain() insert wait
+//    states after the last MFMA;
+//  * accumulators must never be copied or touched by other instructions
+//    inside the loops (checked in the generated code), since such an
+//    access could meet an MFMA still writing them.
 // Back-to-back MFMAs that chain through srcC need no wait states.
-__device__ __forceinline__ void mfma16_agpr(f32x4& d, const u32x4& a, const u32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_acc(f32x4& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma16_agpr_after_valu(f32x4& d, const u32x4& a, const u32x4& b) {
-  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_acc_after_valu(f32x4& d, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void zero_agpr(f32x4& d) {
+__device__ __forceinline__ void zero_acc(f32x4& d) {
   const u32x4 z = {0u, 0u, 0u, 0u};
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(d) : "v"(z));
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=&v"(d) : "v"(z));
 }
-// Score MFMAs: A (tile rows) in VGPRs, B (Q) in AGPRs, scores in VGPRs.
-// The first k-step starts from srcC = 0.  score_drain() must separate the
-// last one from any VALU read of the scores (the compiler does not see
-// these as MFMAs either).
+// Score MFMAs: A (tile rows) and B (Q) in VGPRs; the first k-step starts
+// from srcC = 0.
 __device__ __forceinline__ void mfma_score_first(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_score(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// The drains name the registers they protect as read-write operands, so no
-// later read of those registers can be scheduled above the wait states.
-__device__ __forceinline__ void score_drain(f32x4& s0, f32x4& s1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1)::"memory");
-}
+// The drains name the registers they protect as read-write operands of the
+// wait-state asm itself, so the MFMAs writing them stay above it and no
+// later read of them can be scheduled above it.
 template <int N>
-__device__ __forceinline__ void agpr_drain(f32x4 (&acc)[N]) {
+__device__ __forceinline__ void score_drain(f32x4 (&s)[N]) {
+  static_assert(N == 1 || N == 2, "one or two score accumulators");
+  if constexpr (N == 1)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0])::"memory");
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1])::"memory");
+}
+// acc_drain() follows the loop that issues the accumulating MFMAs, which
+// keeps them above it.
+template <int N>
+__device__ __forceinline__ void acc_drain(f32x4 (&acc)[N]) {
   asm volatile(
       "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < N; i += 2) asm volatile("" : "+a"(acc[i]), "+a"(acc[i + 1]));
+  for (int i = 0; i < N; i += 2) asm volatile("" : "+v"(acc[i]), "+v"(acc[i + 1]));
 }
 
 template <int HG>
@@ -157,8 +160,10 @@ struct DecodeSmem {
   unsigned char xs[kNBuf][kTileBytes];  // row tiles: scored, multiplied, being stored
   uint16_t ps[2][2][HG][kPPitch];       // [tile parity][hi, lo][head][row]
   int rowid[kMaxTopK];                  // row ids of the workgroup's K range
-  float lsum[HG], lexact[HG], mfin[HG];
+  float mx[2][HG];                      // per-head maxima of the two row halves (exchange)
+  float lexact[2][HG], mfin[HG];        // weight sums of the two row halves, reference max
   int overflow;
+  int first_valid;                      // first valid index of the K range
 };
 
 // Iteration it of either role ends by moving tile it+1 from registers to its
@@ -176,120 +181,154 @@ __device__ __forceinline__ void stage_next(u32x4* st, DecodeSmem<HG>& sm, const 
   }
 }
 
-// Score waves 0-3: wave w owns heads 16w .. 16w+15 of the group.  Each role
-// runs its own loop with the same barriers, so the registers of one role
-// (Q here, the O accumulators there) are never live in the other.
+// Score waves 0-3: wave w = 2 hb + rb scores rows 16 rb .. 16 rb + 15 of
+// each tile against QB blocks of 16 heads, heads 16 QB hb ..  (QB = 2 when
+// the group has 32 or more heads).  One A operand (16 rows x 32 dims, read
+// from LDS) feeds QB MFMAs, so the four score waves read the tile twice in
+// all instead of once each.  Each role runs its own loop with the same
+// barriers, so the registers of one role (Q here, the O accumulators there)
+// are never live in the other.
 template <int HG>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
-                                           size_t head0, int n_tiles, int w, int g, int i16, int tid) {
-  const bool active = 16 * w < HG;  // waves past the group's heads only stage tiles
-  // Q of the wave's 16 heads as MFMA B operands in AGPRs: lane (g, i16)
-  // holds dims 32 s + 8 g .. +7 of head 16 w + i16.
-  f32x4 q[kLatent / 32];
+                                           size_t head0, int n_tiles, int t_first, int w, int g, int i16,
+                                           int tid) {
+  constexpr int QB = HG >= 32 ? 2 : 1;     // 16-head blocks per score wave
+  constexpr int NHB = HG / (16 * QB);      // head-block groups (wave pairs with heads)
+  const int rb = w & 1, hb = w >> 1;
+  const bool active = hb < NHB;            // waves past the group's heads only stage tiles
+  // Q of the wave's heads as MFMA B operands: lane (g, i16) holds
+  // dims 32 s + 8 g .. +7 of head 16 (QB hb + qb) + i16.
+  f32x4 q[QB][kLatent / 32];
   if (active) {
-    gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * w + i16) * kLatent + 8 * g);
 #pragma unroll
-    for (int s = 0; s < kLatent / 32; ++s) q[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
-    asm volatile("s_nop 4" ::: "memory");  // AGPR writes -> MFMA reads
+    for (int qb = 0; qb < QB; ++qb) {
+      gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * (QB * hb + qb) + i16) * kLatent + 8 * g);
 #pragma unroll
-    for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+a"(q[s]), "+a"(q[s + 1]));
+      for (int s = 0; s < kLatent / 32; ++s) q[qb][s] = __builtin_bit_cast(f32x4, qp[4 * s]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[qb][s]), "+v"(q[qb][s + 1]));
   }
   u32x4 st[kStage];
-  float m_run = -INFINITY, m_seen = -INFINITY, l_run = 0.f, l_exact = 0.f;
+  // m: reference max per head (log2 units), shared by the two waves of a
+  // head; m_seen: the largest score this wave saw; l: sum of the unrounded
+  // weights of this wave's rows.
+  float m_run[QB], m_seen[QB], l_exact[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = m_seen[qb] = -INFINITY;
 
-  // Softmax with a fixed reference max per head: the first valid tile sets
-  // m, and P = 2^(s*scale*log2e - m) accumulates unnormalised, so the O
-  // accumulators are never rescaled inside the loop.  If a later tile
+  // Softmax with a fixed reference max per head: the first tile with a
+  // valid row sets m (the two waves of a head exchange their maxima once,
+  // through LDS), and P = 2^(s*scale*log2e - m) accumulates unnormalised, so
+  // the O accumulators are never rescaled inside the loop.  If a later tile
   // exceeds m by more than 2^64 (never for ordinary scores), the whole range
   // is recomputed once with m = the true maximum, which no tile can exceed.
   // Both passes give the exact softmax.
   for (int pass = 0; pass < 2; ++pass) {
     if (n_tiles > 1) load_tile(st, kv, sm.rowid + kT, tid);
-    l_run = 0.f;
-    l_exact = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_exact[qb] = 0.f;
     lds_barrier();
     for (int it = 0; it <= n_tiles; ++it) {
+      const bool xchg = pass == 0 && it == t_first;  // uniform: every wave takes the extra barrier
       if (active && it < n_tiles) {
         const unsigned char* xb = sm.xs[it % kNBuf];
-        const int* rowid_t = sm.rowid + it * kT;
-        f32x4 sacc[2];
+        f32x4 sacc[QB];
         // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
-        const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
+        const unsigned char* xrow = xb + (16 * rb + i16) * kPitch + 16 * g;
 #pragma unroll
         for (int s = 0; s < kLatent / 32; ++s) {
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
-          if (s == 0) {
-            mfma_score_first(sacc[0], a0, q[0]);
-            mfma_score_first(sacc[1], a1, q[0]);
-          } else {
-            mfma_score(sacc[0], a0, q[s]);
-            mfma_score(sacc[1], a1, q[s]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            if (s == 0)
+              mfma_score_first(sacc[qb], a0, q[qb][0]);
+            else
+              mfma_score(sacc[qb], a0, q[qb][s]);
           }
           if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
         }
-        score_drain(sacc[0], sacc[1]);
-        // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
-        bool valid[2][4];
-        float mx = -INFINITY;
+        score_drain(sacc);
+        // lane (g, i16): head 16 (QB hb + qb) + i16, rows 16 rb + 4 g + v
+        const int4 rid = *reinterpret_cast<const int4*>(sm.rowid + it * kT + 16 * rb + 4 * g);
+        const bool valid[4] = {rid.x >= 0, rid.y >= 0, rid.z >= 0, rid.w >= 0};
+        float mx[QB];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int qb = 0; qb < QB; ++qb) {
+          mx[qb] = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            valid[rb][v] = rowid_t[16 * rb + 4 * g + v] >= 0;
-            sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sacc[rb][v]);
+            sacc[qb][v] = valid[v] ? sacc[qb][v] * a.scale_log2 : -INFINITY;
+            mx[qb] = fmaxf(mx[qb], sacc[qb][v]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        m_seen = fmaxf(m_seen, mx);
-        if (m_run == -INFINITY) {
-          m_run = mx;  // first valid rows of this head: O and l are still zero
-        } else if (mx > m_run + kMaxGrowLog2) {
-          sm.overflow = 1;  // this pass is discarded; P may overflow below
+          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 16, 64));
+          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32, 64));
+          m_seen[qb] = fmaxf(m_seen[qb], mx[qb]);
         }
-        uint16_t* prow_hi = &sm.ps[it & 1][0][16 * w + i16][0];
-        uint16_t* prow_lo = &sm.ps[it & 1][1][16 * w + i16][0];
+        if (xchg) {
+          // first tile with a valid row: both waves of a head take the max
+          // over all 32 rows as the reference
+          if (g == 0) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+            for (int qb = 0; qb < QB; ++qb) sm.mx[rb][16 * (QB * hb + qb) + i16] = mx[qb];
+          }
+          lds_barrier();
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(mx[qb], sm.mx[rb ^ 1][16 * (QB * hb + qb) + i16]);
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (mx[qb] > m_run[qb] + kMaxGrowLog2) sm.overflow = 1;  // this pass is discarded
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int head = 16 * (QB * hb + qb) + i16;
           float p[4], r[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
-          l_exact += (p[0] + p[1]) + (p[2] + p[3]);
+          for (int v = 0; v < 4; ++v) p[v] = valid[v] ? __builtin_amdgcn_exp2f(sacc[qb][v] - m_run[qb]) : 0.f;
+          l_exact[qb] += (p[0] + p[1]) + (p[2] + p[3]);
           const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
           const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
                               __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
 #pragma unroll
           for (int v = 0; v < 4; ++v) r[v] = p[v] - h[v];  // exact in fp32
           const u32x2 lo = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-          *reinterpret_cast<u32x2*>(prow_hi + 16 * rb + 4 * g) = hi;
-          *reinterpret_cast<u32x2*>(prow_lo + 16 * rb + 4 * g) = lo;
-          // O is normalised by the sum of the weights PV actually multiplies
-          // (P_hi + P_lo), so it is a convex combination of the value rows;
-          // lse uses the sum of the unrounded weights.
-          l_run += ((h[0] + __uint_as_float(lo[0] << 16)) + (h[1] + __uint_as_float(lo[0] & 0xFFFF0000u))) +
-                   ((h[2] + __uint_as_float(lo[1] << 16)) + (h[3] + __uint_as_float(lo[1] & 0xFFFF0000u)));
+          *reinterpret_cast<u32x2*>(&sm.ps[it & 1][0][head][16 * rb + 4 * g]) = hi;
+          *reinterpret_cast<u32x2*>(&sm.ps[it & 1][1][head][16 * rb + 4 * g]) = lo;
         }
+      } else if (xchg) {
+        lds_barrier();
       }
       stage_next(st, sm, kv, it, n_tiles, 1, tid);
       lds_barrier();
     }
     if (!sm.overflow) break;
-    m_run = m_seen;
+    // Recompute with the true maximum of each head over both waves' rows.
+    if (active && g == 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sm.mx[rb][16 * (QB * hb + qb) + i16] = m_seen[qb];
+    }
     lds_barrier();
+    if (active) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(m_seen[qb], sm.mx[rb ^ 1][16 * (QB * hb + qb) + i16]);
+    }
   }
 
-  // Normaliser, reference max and exact weight sum per head for the value waves.
+  // Reference max and partial weight sums per head for the value waves.
   if (active) {
-    float ls = l_run, le = l_exact;
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    le += __shfl_xor(le, 16, 64);
-    le += __shfl_xor(le, 32, 64);
-    if (g == 0) {
-      sm.lsum[16 * w + i16] = ls;
-      sm.lexact[16 * w + i16] = le;
-      sm.mfin[16 * w + i16] = m_run;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float le = l_exact[qb];
+      le += __shfl_xor(le, 16, 64);
+      le += __shfl_xor(le, 32, 64);
+      if (g == 0) {
+        const int head = 16 * (QB * hb + qb) + i16;
+        sm.lexact[rb][head] = le;
+        if (rb == 0) sm.mfin[head] = m_run[qb];
+      }
     }
   }
   __syncthreads();
@@ -299,8 +338,8 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
 // head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
 template <int HG>
 __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
-                                           size_t head0, int pair, int split, int hg, int n_tiles, int cw, int g,
-                                           int i16, int lt) {
+                                           size_t head0, int pair, int split, int hg, int n_tiles, int t_first,
+                                           int cw, int g, int i16, int lt) {
   constexpr int NBP = HG / 16;  // 16-head blocks
   f32x4 acc[8 * NBP];           // acc[mb * NBP + nb]: columns 16 mb.., heads 16 nb..
   u32x4 st[kStage];
@@ -308,7 +347,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NBP; ++nb) zero_agpr(acc[mb * NBP + nb]);
+      for (int nb = 0; nb < NBP; ++nb) zero_acc(acc[mb * NBP + nb]);
     // Tile 0 goes straight to LDS; tile 2 stays in flight in registers
     // (tile 1 is the score waves').
     if (n_tiles > 0) {
@@ -319,6 +358,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
     lds_barrier();
     // Iteration it multiplies tile it-1 (the score waves score tile it).
     for (int it = 0; it <= n_tiles; ++it) {
+      if (pass == 0 && it == t_first) lds_barrier();  // the score waves' max exchange
       if (it >= 1) {
         const int tp = it - 1;
         const unsigned char* xb = sm.xs[tp % kNBuf];
@@ -344,11 +384,11 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
           const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          mfma16_agpr_after_valu(acc[mb * NBP], av, bp[0]);
+          mfma_acc_after_valu(acc[mb * NBP], av, bp[0]);
 #pragma unroll
-          for (int nb = 1; nb < NBP; ++nb) mfma16_agpr(acc[mb * NBP + nb], av, bp[nb]);
+          for (int nb = 1; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bp[nb]);
 #pragma unroll
-          for (int nb = 0; nb < NBP; ++nb) mfma16_agpr(acc[mb * NBP + nb], av, bq[nb]);
+          for (int nb = 0; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bq[nb]);
           if (mb & 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -360,13 +400,15 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
   }
   __syncthreads();  // the score waves' normalisers are in LDS
 
-  agpr_drain(acc);
+  acc_drain(acc);
   const int H = a.num_heads;
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
     const int h = nb * 16 + i16;
-    const float lsum = sm.lsum[h];
-    const float lex = sm.lexact[h];
+    // O is normalised by the sum of the unrounded weights; P_hi + P_lo
+    // carries each weight to about 2^-17 relative, far inside the tolerance.
+    const float lsum = sm.lexact[0][h] + sm.lexact[1][h];
+    const float lex = lsum;
     const float m = sm.mfin[h];
     if (a.splits == 1) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -422,16 +464,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   const int k1 = min(K, k0 + per);
   const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
 
-  // Row ids of the whole K range, validated once.
-  for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
-  if (tid == 0) sm.overflow = 0;
+  // Row ids of the whole K range, validated once, and the tile holding the
+  // first valid one (n_tiles if there is none).
+  if (tid == 0) {
+    sm.overflow = 0;
+    sm.first_valid = n_tiles * kT;
+  }
   __syncthreads();
+  for (int k = tid; k < n_tiles * kT; k += kThreads) {
+    const int rid = load_row_id(a, rows, k0 + k, k1);
+    sm.rowid[k] = rid;
+    if (rid >= 0) atomicMin(&sm.first_valid, k);
+  }
+  __syncthreads();
+  const int t_first = sm.first_valid / kT;
 
   const size_t head0 = (size_t)pair * H + hg * HG;
   if (w < 4)
-    score_role<HG>(a, sm, kv, head0, n_tiles, w, g, i16, tid);
+    score_role<HG>(a, sm, kv, head0, n_tiles, t_first, w, g, i16, tid);
   else
-    value_role<HG>(a, sm, kv, head0, pair, split, hg, n_tiles, w - 4, g, i16, tid - 256);
+    value_role<HG>(a, sm, kv, head0, pair, split, hg, n_tiles, t_first, w - 4, g, i16, tid - 256);
 }
 
 // Merge the split partials of one (layer, request, head) per wavefront.
