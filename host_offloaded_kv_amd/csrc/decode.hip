@@ -58,7 +58,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+typedef const __attribute__((address_space(1))) u32x2 gu32x2;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
@@ -76,27 +78,68 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
   return r;
 }
 
-// Tile loads go through VGPRs: each loading thread fetches 9 16-byte chunks
-// of a tile with ordinary global loads two tiles ahead, and writes them to
-// LDS after the current tile's work.  On MI355X this sustains ~7.3 TB/s for a random
-// 1152-byte row gather, where direct-to-LDS loads stayed under 3 TB/s.  The
-// loads use global-address-space pointers: flat loads would also count
-// against the LDS wait counter and be drained by every lds_barrier().
-// Loader thread t (0..255) owns row t / 8 of the tile and its chunks
-// t % 8 + 8 k, k = 0..8: eight threads cover 128 contiguous bytes of a row
-// per k, and every address is one base plus an immediate k * 128.
-__device__ __forceinline__ void load_tile(u32x4* st, const uint16_t* kv, const int* rowid, int t) {
-  const int rid = rowid[t >> 3];
-  gu32x4* src = (gu32x4*)(kv + (size_t)(rid < 0 ? 0 : rid) * kLatent + (t & 7) * 8);
+// Tile loads go through VGPRs: each loading thread fetches its part of a
+// tile with ordinary global loads two tiles ahead, and writes it to LDS
+// after the current tile's work.  On MI355X this sustains ~7.3 TB/s for a
+// random 1152-byte row gather, where direct-to-LDS loads stayed under
+// 3 TB/s.  The loads use global-address-space pointers: flat loads would
+// also count against the LDS wait counter and be drained by every
+// lds_barrier().  Loader thread t (0..255) owns row t / 8 of the tile and
+// its 8-value groups t % 8 + 8 k, k = 0..8 (LDS chunk t % 8 + 8 k of the
+// row): eight threads cover contiguous bytes of a row per k, and every
+// address is one base plus an immediate.
+//
+// The LDS tile is always bf16.  FP8 E4M3 rows are widened while staging:
+// every E4M3 value (at most 4 significant bits, exponent within bf16's
+// range) converts to fp32 and then to bf16 exactly; the layer's scale is
+// applied to the scores and to O instead.
+template <bool FP8>
+struct TileStage;
+
+template <>
+struct TileStage<false> {
+  u32x4 v[kStage];
+  __device__ __forceinline__ void load(const unsigned char* kv, const int* rowid, int t) {
+    const int rid = rowid[t >> 3];
+    gu32x4* src = (gu32x4*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytes + (t & 7) * 16);
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) st[k] = src[8 * k];
+    for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
+  }
+  __device__ __forceinline__ void store(unsigned char* xs, int t) const {
+    u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) dst[8 * k] = v[k];
+  }
+};
+
+// Two fp32 values that are exact in bf16 -> their bf16 pair (upper halves).
+__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-__device__ __forceinline__ void store_tile(const u32x4* st, unsigned char* xs, int t) {
-  u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
+template <>
+struct TileStage<true> {
+  u32x2 v[kStage];
+  __device__ __forceinline__ void load(const unsigned char* kv, const int* rowid, int t) {
+    const int rid = rowid[t >> 3];
+    gu32x2* src = (gu32x2*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytesFp8 + (t & 7) * 8);
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) dst[8 * k] = st[k];
-}
+    for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
+  }
+  __device__ __forceinline__ void store(unsigned char* xs, int t) const {
+    u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+      const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][0], false);
+      const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][0], true);
+      const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], false);
+      const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], true);
+      const u32x4 w = {bf16_pair_exact(a0[0], a0[1]), bf16_pair_exact(a1[0], a1[1]), bf16_pair_exact(b0[0], b0[1]),
+                       bf16_pair_exact(b1[0], b1[1])};
+      dst[8 * k] = w;
+    }
+  }
+};
 
 // Workgroup barrier for LDS traffic only: unlike __syncthreads() it does
 // not wait for outstanding global loads, so tile loads stay in flight.
@@ -171,13 +214,14 @@ struct DecodeSmem {
 // starting the load of tile it+3 into the same registers.  The value waves
 // stage the even tiles and the score waves the odd ones, so two tiles'
 // loads are in flight while a third is consumed.
-template <int HG>
-__device__ __forceinline__ void stage_next(u32x4* st, DecodeSmem<HG>& sm, const uint16_t* kv, int it, int n_tiles,
+template <int HG, bool FP8>
+__device__ __forceinline__ void stage_next(TileStage<FP8>& st, DecodeSmem<HG>& sm, const unsigned char* kv, int it,
+                                           int n_tiles,
                                            int parity, int lt) {
   const int nx = it + 1;
   if (nx < n_tiles && (nx & 1) == parity) {
-    store_tile(st, sm.xs[nx % kNBuf], lt);
-    if (nx + 2 < n_tiles) load_tile(st, kv, sm.rowid + (nx + 2) * kT, lt);
+    st.store(sm.xs[nx % kNBuf], lt);
+    if (nx + 2 < n_tiles) st.load(kv, sm.rowid + (nx + 2) * kT, lt);
   }
 }
 
@@ -188,10 +232,10 @@ __device__ __forceinline__ void stage_next(u32x4* st, DecodeSmem<HG>& sm, const 
 // all instead of once each.  Each role runs its own loop with the same
 // barriers, so the registers of one role (Q here, the O accumulators there)
 // are never live in the other.
-template <int HG>
-__device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
-                                           size_t head0, int n_tiles, int t_first, int w, int g, int i16,
-                                           int tid) {
+template <int HG, bool FP8>
+__device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
+                                           float kvs, size_t head0, int n_tiles, int t_first, int w, int g,
+                                           int i16, int tid) {
   constexpr int QB = HG >= 32 ? 2 : 1;     // 16-head blocks per score wave
   constexpr int NHB = HG / (16 * QB);      // head-block groups (wave pairs with heads)
   const int rb = w & 1, hb = w >> 1;
@@ -211,7 +255,9 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
 #pragma unroll
       for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[qb][s]), "+v"(q[qb][s + 1]));
   }
-  u32x4 st[kStage];
+  TileStage<FP8> st;
+  // Scores in log2 units; FP8 rows carry the layer's scale.
+  const float score_scale = a.scale_log2 * kvs;
   // m: reference max per head (log2 units), shared by the two waves of a
   // head; m_seen: the largest score this wave saw; l: sum of the unrounded
   // weights of this wave's rows.
@@ -227,7 +273,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
   // is recomputed once with m = the true maximum, which no tile can exceed.
   // Both passes give the exact softmax.
   for (int pass = 0; pass < 2; ++pass) {
-    if (n_tiles > 1) load_tile(st, kv, sm.rowid + kT, tid);
+    if (n_tiles > 1) st.load(kv, sm.rowid + kT, tid);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_exact[qb] = 0.f;
     lds_barrier();
@@ -260,7 +306,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
           mx[qb] = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            sacc[qb][v] = valid[v] ? sacc[qb][v] * a.scale_log2 : -INFINITY;
+            sacc[qb][v] = valid[v] ? sacc[qb][v] * score_scale : -INFINITY;
             mx[qb] = fmaxf(mx[qb], sacc[qb][v]);
           }
           mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 16, 64));
@@ -336,13 +382,13 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
 
 // Value waves 4-7: wave 4+cw owns output columns 128cw .. 128cw+127 of every
 // head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
-template <int HG>
-__device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const uint16_t* kv,
-                                           size_t head0, int pair, int split, int hg, int n_tiles, int t_first,
-                                           int cw, int g, int i16, int lt) {
+template <int HG, bool FP8>
+__device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
+                                           float kvs, size_t head0, int pair, int split, int hg, int n_tiles,
+                                           int t_first, int cw, int g, int i16, int lt) {
   constexpr int NBP = HG / 16;  // 16-head blocks
   f32x4 acc[8 * NBP];           // acc[mb * NBP + nb]: columns 16 mb.., heads 16 nb..
-  u32x4 st[kStage];
+  TileStage<FP8> st;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
@@ -351,10 +397,10 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
     // Tile 0 goes straight to LDS; tile 2 stays in flight in registers
     // (tile 1 is the score waves').
     if (n_tiles > 0) {
-      load_tile(st, kv, sm.rowid, lt);
-      store_tile(st, sm.xs[0], lt);
+      st.load(kv, sm.rowid, lt);
+      st.store(sm.xs[0], lt);
     }
-    if (n_tiles > 2) load_tile(st, kv, sm.rowid + 2 * kT, lt);
+    if (n_tiles > 2) st.load(kv, sm.rowid + 2 * kT, lt);
     lds_barrier();
     // Iteration it multiplies tile it-1 (the score waves score tile it).
     for (int it = 0; it <= n_tiles; ++it) {
@@ -411,7 +457,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
     const float lex = lsum;
     const float m = sm.mfin[h];
     if (a.splits == 1) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const float inv = lsum > 0.f ? kvs / lsum : 0.f;
       float* out = a.out + (head0 + h) * kVDim + 128 * cw + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
@@ -426,7 +472,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) po[16 * mb + v] = acc[mb * NBP + nb][v];
+        for (int v = 0; v < 4; ++v) po[16 * mb + v] = acc[mb * NBP + nb][v] * kvs;
         __builtin_amdgcn_sched_barrier(0);
       }
       if (cw == 0 && g == 0) {
@@ -438,7 +484,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
   }
 }
 
-template <int HG>
+template <int HG, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   __shared__ __align__(16) DecodeSmem<HG> sm;
   const int H = a.num_heads, R = a.num_requests, K = a.top_k;
@@ -451,7 +497,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   const int hg = li % nhg;
   const int pair = li / nhg;
   const int l = a.layer_begin + pair / R;
-  const uint16_t* kv = a.kv[l];
+  const unsigned char* kv = a.kv[l];
+  const float kvs = FP8 ? a.kv_scale[l] : 1.f;  // x = decode(code) * kvs for FP8 rows
   const int32_t* rows = a.rows + (size_t)pair * K;
 
   const int tid = threadIdx.x;
@@ -481,9 +528,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
 
   const size_t head0 = (size_t)pair * H + hg * HG;
   if (w < 4)
-    score_role<HG>(a, sm, kv, head0, n_tiles, t_first, w, g, i16, tid);
+    score_role<HG, FP8>(a, sm, kv, kvs, head0, n_tiles, t_first, w, g, i16, tid);
   else
-    value_role<HG>(a, sm, kv, head0, pair, split, hg, n_tiles, t_first, w - 4, g, i16, tid - 256);
+    value_role<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, n_tiles, t_first, w - 4, g, i16, tid - 256);
 }
 
 // Merge the split partials of one (layer, request, head) per wavefront.
@@ -572,12 +619,18 @@ hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s) {
   const int nhg = a.num_heads / hgs;
   const int grid = a.n_layers * a.num_requests * nhg * a.splits;
   prof_begin(p, kKDecode, s);
-  if (hgs == 64)
-    hipLaunchKernelGGL(decode_ws<64>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
-  else if (hgs == 32)
-    hipLaunchKernelGGL(decode_ws<32>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
-  else
-    hipLaunchKernelGGL(decode_ws<16>, dim3(grid), dim3(kThreads), 0, s, a, nhg);
+  const bool fp8 = a.kv_dtype == HISPARSE_KV_FP8_E4M3;
+  const dim3 gd(grid), bd(kThreads);
+  if (hgs == 64) {
+    if (fp8) hipLaunchKernelGGL((decode_ws<64, true>), gd, bd, 0, s, a, nhg);
+    else hipLaunchKernelGGL((decode_ws<64, false>), gd, bd, 0, s, a, nhg);
+  } else if (hgs == 32) {
+    if (fp8) hipLaunchKernelGGL((decode_ws<32, true>), gd, bd, 0, s, a, nhg);
+    else hipLaunchKernelGGL((decode_ws<32, false>), gd, bd, 0, s, a, nhg);
+  } else {
+    if (fp8) hipLaunchKernelGGL((decode_ws<16, true>), gd, bd, 0, s, a, nhg);
+    else hipLaunchKernelGGL((decode_ws<16, false>), gd, bd, 0, s, a, nhg);
+  }
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   if (e != hipSuccess || a.splits == 1) return e;

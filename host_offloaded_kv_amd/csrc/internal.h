@@ -11,10 +11,11 @@
 
 namespace hs {
 
-constexpr int kLatent = 576;         // bf16 values per KV row
+constexpr int kLatent = 576;         // values per KV row
 constexpr int kVDim = 512;           // value width (the "nope" part)
-constexpr int kRowBytes = kLatent * 2;
-constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per row (72)
+constexpr int kRowBytes = kLatent * 2;      // bf16 row
+constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per bf16 row (72)
+constexpr int kRowBytesFp8 = kLatent;       // FP8 E4M3 row (36 chunks)
 constexpr int kPartW = kVDim + 4;           // split partial: o[512], m, l (rounded weights), l (exact), pad
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHotSlots = 8192;
@@ -39,7 +40,7 @@ struct FetchArgs {
   const int32_t* miss_count;   // [n_pairs]
   const int2* fetch;           // [n_pairs][K] (position, slot)
   const uint64_t* host_rows;   // [L*R] device-visible address of pool rows of (l, r)
-  uint16_t* const* kv;         // [L] device pointers of the KV tensors (device array)
+  unsigned char* const* kv;    // [L] device pointers of the KV tensors (device array)
   const int32_t* hv;           // [L][R] positions below hv[l][r] are held by the host pool
   uint32_t* err;
   int32_t layer_begin;
@@ -49,13 +50,14 @@ struct FetchArgs {
   int32_t total_requests;      // R of the pool
   int32_t top_k;
   int32_t hot_slots;
+  int32_t row_chunks;          // 16-byte chunks per row (72 bf16, 36 FP8)
   int64_t resident_rows;
 };
 
 // Append of one token per request (all layers) into the tail page.
 struct AppendArgs {
-  const uint16_t* rows;        // [L][R][576] new rows
-  uint16_t* const* kv;         // [L] device array of KV tensor pointers
+  const unsigned char* rows;   // [L][R] new rows
+  unsigned char* const* kv;    // [L] device array of KV tensor pointers
   int32_t* ctx;                // [R] current context lengths (advanced)
   const int32_t* capacity;     // [R]
   const int32_t* bt;           // concatenated block tables
@@ -64,11 +66,12 @@ struct AppendArgs {
   int32_t num_layers;
   int32_t num_requests;
   int32_t page_shift;
+  int32_t row_chunks;
 };
 
 // Copy of completed pages from their resident blocks to the host pool.
 struct WritebackArgs {
-  uint16_t* const* kv;         // [L]
+  unsigned char* const* kv;    // [L]
   const uint64_t* host_rows;   // [L*R] device-visible address of the pool rows of (l, r)
   const int32_t* ctx;          // [R]
   int32_t* hv;                 // [L][R] (advanced)
@@ -78,6 +81,7 @@ struct WritebackArgs {
   int32_t num_layers;
   int32_t num_requests;
   int32_t page_shift;
+  int32_t row_chunks;
 };
 
 struct ResolveArgs {
@@ -112,7 +116,8 @@ struct ResolveArgs {
 struct DecodeArgs {
   const uint16_t* q;       // [n_layers][R][H][576]
   const int32_t* rows;     // [n_layers][R][K]
-  uint16_t* const* kv;     // [L] device array of KV tensor pointers
+  const unsigned char* const* kv;  // [L] device array of KV tensor pointers
+  const float* kv_scale;   // [L] FP8 row scales (device)
   float* out;              // [n_layers][R][H][512]
   float* lse;              // [n_layers][R][H]
   float* partial;          // [n_layers][R][splits][H][kPartW] when splits > 1
@@ -125,12 +130,13 @@ struct DecodeArgs {
   int32_t splits;
   int64_t kv_rows;         // rows per KV tensor
   float scale_log2;        // scale * log2(e)
+  int32_t kv_dtype;        // HISPARSE_KV_BF16 or HISPARSE_KV_FP8_E4M3
 };
 
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
-  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, cap, hv, host_rows, kv_ptrs, err,
-      partial, posmap, map_off, total;
+  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, cap, hv, host_rows, kv_ptrs, kv_scale,
+      err, partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
   int32_t splits_max;      // largest split count any decode launch uses
@@ -163,10 +169,12 @@ struct hisparse_pool {
   hs::Layout lay;
   char* ws = nullptr;
   std::vector<void*> host_alloc;        // one pinned allocation per request
-  std::vector<uint16_t*> host_rows;     // [L*R] host addresses (index l*R + r)
+  std::vector<unsigned char*> host_rows;  // [L*R] host addresses (index l*R + r)
   std::vector<uint64_t> host_rows_dev;  // [L*R] device-visible addresses
-  std::vector<uint16_t*> kv;            // [L]
+  std::vector<unsigned char*> kv;       // [L]
+  std::vector<float> kv_scale;          // [L] FP8 row scales (1 for bf16)
   int64_t kv_rows = 0;
+  int32_t row_bytes = hs::kRowBytes;    // bytes per KV row (1152 bf16, 576 FP8)
   size_t resolve_lds = 0;
   int32_t policy = HISPARSE_POLICY_LRU;
   uint64_t policy_seed = 0;
@@ -176,7 +184,8 @@ struct hisparse_pool {
   int64_t* map_off;
   int2* fetch;
   uint64_t* host_rows_d;
-  uint16_t** kv_d;
+  unsigned char** kv_d;
+  float* kv_scale_d;
   uint32_t* err;
   float* partial;
   // Overlapped step: per-layer miss fetches run on fetch_stream (default

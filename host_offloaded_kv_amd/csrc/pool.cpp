@@ -50,6 +50,21 @@ hisparse_status check_config(const hisparse_config* c) {
     set_error("latent_dim must be 576 and v_dim 512");
     return HISPARSE_EINVAL;
   }
+  if (c->kv_dtype != HISPARSE_KV_BF16 && c->kv_dtype != HISPARSE_KV_FP8_E4M3) {
+    set_error("kv_dtype must be HISPARSE_KV_BF16 or HISPARSE_KV_FP8_E4M3");
+    return HISPARSE_EINVAL;
+  }
+  if (c->num_verify < 0 || c->num_verify > 1) {
+    set_error("num_verify must be 0 or 1");
+    return HISPARSE_EINVAL;
+  }
+  if (c->kv_scale && c->kv_dtype == HISPARSE_KV_FP8_E4M3) {
+    for (int l = 0; l < c->num_layers; ++l)
+      if (!(std::isfinite(c->kv_scale[l]) && c->kv_scale[l] > 0.f)) {
+        set_error("kv_scale[" + std::to_string(l) + "] must be finite and positive");
+        return HISPARSE_EINVAL;
+      }
+  }
   if (c->top_k < 1 || c->top_k > kMaxTopK) {
     set_error("top_k must be in [1, 4096]");
     return HISPARSE_EINVAL;
@@ -126,6 +141,7 @@ Layout make_layout(const hisparse_config* c) {
   L.hv = off; off = align256(off + NL * R * 4);
   L.host_rows = off; off = align256(off + NL * R * 8);
   L.kv_ptrs = off; off = align256(off + NL * 8);
+  L.kv_scale = off; off = align256(off + NL * 4);
   L.err = off; off = align256(off + 4);
   L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
   int64_t ctx_sum = 0;
@@ -244,7 +260,12 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->lay = lay;
   p->ws = (char*)d_workspace;
   p->kv.resize(NL);
-  for (int l = 0; l < NL; ++l) p->kv[l] = (uint16_t*)d_kv[l];
+  for (int l = 0; l < NL; ++l) p->kv[l] = (unsigned char*)d_kv[l];
+  p->row_bytes = cfg->kv_dtype == HISPARSE_KV_FP8_E4M3 ? kRowBytesFp8 : kRowBytes;
+  p->kv_scale.assign(NL, 1.f);
+  if (cfg->kv_scale && cfg->kv_dtype == HISPARSE_KV_FP8_E4M3)
+    for (int l = 0; l < NL; ++l) p->kv_scale[l] = cfg->kv_scale[l];
+  p->cfg.kv_scale = p->kv_scale.data();
   p->kv_rows = cfg->resident_rows_per_layer + (int64_t)R * cfg->hot_slots;
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) {
@@ -279,7 +300,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->host_rows.assign((size_t)NL * R, nullptr);
   p->host_rows_dev.assign((size_t)NL * R, 0);
   for (int r = 0; r < R; ++r) {
-    const size_t per_layer = (size_t)p->cap[r] * kRowBytes;
+    const size_t per_layer = (size_t)p->cap[r] * p->row_bytes;
     void* h = nullptr;
     e = hipHostMalloc(&h, per_layer * NL, flags);
     if (e != hipSuccess || !h) {
@@ -297,7 +318,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
       return hip_fail(e, "hipHostGetDevicePointer");
     }
     for (int l = 0; l < NL; ++l) {
-      p->host_rows[(size_t)l * R + r] = (uint16_t*)((char*)h + per_layer * l);
+      p->host_rows[(size_t)l * R + r] = (unsigned char*)h + per_layer * l;
       p->host_rows_dev[(size_t)l * R + r] = (uint64_t)((char*)dptr + per_layer * l);
     }
   }
@@ -316,7 +337,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->cap_d = (int32_t*)(w + lay.cap);
   p->hv_d = (int32_t*)(w + lay.hv);
   p->host_rows_d = (uint64_t*)(w + lay.host_rows);
-  p->kv_d = (uint16_t**)(w + lay.kv_ptrs);
+  p->kv_d = (unsigned char**)(w + lay.kv_ptrs);
+  p->kv_scale_d = (float*)(w + lay.kv_scale);
   p->err = (uint32_t*)(w + lay.err);
   p->partial = (float*)(w + lay.partial);
   p->posmap = (int16_t*)(w + lay.posmap);
@@ -350,6 +372,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
       (e = hipMemcpyAsync(p->host_rows_d, p->host_rows_dev.data(), (size_t)NL * R * 8, hipMemcpyHostToDevice, s)) !=
           hipSuccess ||
       (e = hipMemcpyAsync(p->kv_d, kvp.data(), (size_t)NL * 8, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(p->kv_scale_d, p->kv_scale.data(), (size_t)NL * 4, hipMemcpyHostToDevice, s)) !=
+          hipSuccess ||
       (e = launch_workspace_init(p, s)) != hipSuccess || (e = hipStreamSynchronize(s)) != hipSuccess) {
     hisparse_destroy_pool(p);
     return hip_fail(e, "workspace initialisation");
@@ -384,7 +408,7 @@ void hisparse_destroy_pool(hisparse_pool* p) {
   delete p;
 }
 
-uint16_t* hisparse_host_rows(hisparse_pool* p, int32_t r, int32_t l) {
+void* hisparse_host_rows(hisparse_pool* p, int32_t r, int32_t l) {
   if (!p || r < 0 || r >= p->cfg.num_requests || l < 0 || l >= p->cfg.num_layers) {
     set_error("hisparse_host_rows: bad argument");
     return nullptr;
@@ -472,6 +496,7 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
   f.total_requests = R;
   f.top_k = p->cfg.top_k;
   f.hot_slots = p->cfg.hot_slots;
+  f.row_chunks = p->row_bytes / 16;
   f.resident_rows = p->cfg.resident_rows_per_layer;
   f.hv = p->hv_d;
   f.err = p->err;
@@ -490,6 +515,8 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.q = d_q;
   a.rows = d_rows;
   a.kv = p->kv_d;
+  a.kv_scale = p->kv_scale_d;
+  a.kv_dtype = p->cfg.kv_dtype;
   a.out = d_out;
   a.lse = d_lse;
   a.partial = p->partial;
@@ -653,7 +680,7 @@ hisparse_status hisparse_reset_state(hisparse_pool* p, void* stream) {
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_reset_state");
 }
 
-hisparse_status hisparse_append(hisparse_pool* p, const uint16_t* d_rows, void* stream) {
+hisparse_status hisparse_append(hisparse_pool* p, const void* d_rows, void* stream) {
   if (!p || !d_rows) {
     set_error("hisparse_append: NULL argument");
     return HISPARSE_EINVAL;
@@ -663,7 +690,8 @@ hisparse_status hisparse_append(hisparse_pool* p, const uint16_t* d_rows, void* 
     return HISPARSE_EINVAL;
   }
   AppendArgs a;
-  a.rows = d_rows;
+  a.rows = (const unsigned char*)d_rows;
+  a.row_chunks = p->row_bytes / 16;
   a.kv = p->kv_d;
   a.ctx = p->ctx_d;
   a.capacity = p->cap_d;
@@ -683,6 +711,7 @@ hisparse_status hisparse_writeback(hisparse_pool* p, void* stream) {
     return HISPARSE_EINVAL;
   }
   WritebackArgs a;
+  a.row_chunks = p->row_bytes / 16;
   a.kv = p->kv_d;
   a.host_rows = p->host_rows_d;
   a.ctx = p->ctx_d;

@@ -43,10 +43,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows(AppendArgs a) {
     return;
   }
   const int64_t row = ((int64_t)blk << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
-  for (int i = threadIdx.x; i < a.num_layers * kRowChunks; i += kAppendThreads) {
-    const int l = i / kRowChunks, c = i - l * kRowChunks;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.rows + ((size_t)l * R + r) * kLatent) + c;
-    u32x4* dst = reinterpret_cast<u32x4*>(a.kv[l] + row * kLatent) + c;
+  const int rc = a.row_chunks;
+  for (int i = threadIdx.x; i < a.num_layers * rc; i += kAppendThreads) {
+    const int l = i / rc, c = i - l * rc;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.rows + ((size_t)l * R + r) * rc * 16) + c;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.kv[l] + row * rc * 16) + c;
     *dst = *src;
   }
   __syncthreads();
@@ -64,19 +65,20 @@ __global__ __launch_bounds__(kWritebackThreads) void writeback_rows(WritebackArg
   if (to <= from) return;
   const int32_t* bt = a.bt + a.bt_off[r];
   u32x4* host = reinterpret_cast<u32x4*>(a.host_rows[(size_t)l * R + r]);
-  const uint16_t* kv = a.kv[l];
+  const unsigned char* kv = a.kv[l];
+  const int rc = a.row_chunks;
   bool bad = false;
-  const int64_t n = (int64_t)(to - from) * kRowChunks;
+  const int64_t n = (int64_t)(to - from) * rc;
   for (int64_t i = threadIdx.x; i < n; i += kWritebackThreads) {
-    const int p = from + (int)(i / kRowChunks);
-    const int c = (int)(i - (int64_t)(p - from) * kRowChunks);
+    const int p = from + (int)(i / rc);
+    const int c = (int)(i - (int64_t)(p - from) * rc);
     const int blk = bt[p >> pshift];
     if (blk < 0) {
       bad = true;
       continue;
     }
-    const u32x4 v = reinterpret_cast<const u32x4*>(kv + (((int64_t)blk << pshift) + (p & pmask)) * kLatent)[c];
-    __builtin_nontemporal_store(v, host + (size_t)p * kRowChunks + c);
+    const u32x4 v = reinterpret_cast<const u32x4*>(kv + (((int64_t)blk << pshift) + (p & pmask)) * rc * 16)[c];
+    __builtin_nontemporal_store(v, host + (size_t)p * rc + c);
   }
   if (__syncthreads_or(bad)) {
     if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);

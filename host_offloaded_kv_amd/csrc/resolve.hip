@@ -23,7 +23,8 @@
 //  * fetch_rows: a fan-out copy over the whole GPU.  Each workgroup scans
 //    the per-(request, layer) miss counts in LDS, then the grid walks a flat
 //    index of 16-byte chunks over every missed row (72 chunks per 1152-byte
-//    row), so a wavefront's loads cover 1 KiB of contiguous host memory.
+//    bf16 row, 36 per 576-byte FP8 row), so a wavefront's loads cover 1 KiB
+//    of contiguous host memory.
 //    Loads are zero-copy reads of the pinned, device-mapped pool over the
 //    host link.
 #include "internal.h"
@@ -495,7 +496,8 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
   }
   if (tid == kFetchThreads - 1) pre_s[n] = acc;
   __syncthreads();
-  const int64_t total_chunks = (int64_t)pre_s[n] * kRowChunks;
+  const int rc = a.row_chunks;
+  const int64_t total_chunks = (int64_t)pre_s[n] * rc;
   const int R = a.num_requests, RT = a.total_requests;
 
   for (int64_t base = (int64_t)blockIdx.x * kFetchThreads * kFetchUnroll; base < total_chunks;
@@ -507,8 +509,8 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
       const int64_t q = base + (int64_t)u * kFetchThreads + tid;
       dst[u] = nullptr;
       if (q < total_chunks) {
-        const int gi = (int)(q / kRowChunks);
-        const int c = (int)(q - (int64_t)gi * kRowChunks);
+        const int gi = (int)(q / rc);
+        const int c = (int)(q - (int64_t)gi * rc);
         int lo = 0, hi = n;  // largest pair with pre_s[pair] <= gi
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
@@ -524,9 +526,9 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_rows(FetchArgs a, const i
         if (!held && c == 0) atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
         if ((unsigned)e.y < (unsigned)a.hot_slots && e.x >= 0 && e.x < ctx[r] && held) {
           const u32x4* src = reinterpret_cast<const u32x4*>(
-              reinterpret_cast<const char*>(a.host_rows[(size_t)l * RT + r]) + (size_t)e.x * kRowBytes) + c;
+              reinterpret_cast<const char*>(a.host_rows[(size_t)l * RT + r]) + (size_t)e.x * rc * 16) + c;
           const int64_t row = a.resident_rows + (int64_t)r * a.hot_slots + e.y;
-          dst[u] = reinterpret_cast<u32x4*>(a.kv[l] + row * kLatent) + c;
+          dst[u] = reinterpret_cast<u32x4*>(a.kv[l] + row * rc * 16) + c;
           v[u] = __builtin_nontemporal_load(src);
         }
       }

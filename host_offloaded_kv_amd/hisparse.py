@@ -33,6 +33,12 @@ HISPARSE_ERR_ROW = 8
 HISPARSE_ERR_APPEND = 16
 HISPARSE_ERR_UNMATERIALIZED = 32
 
+# KV row formats (hisparse_config.kv_dtype)
+HISPARSE_KV_BF16 = 0
+HISPARSE_KV_FP8_E4M3 = 1
+KV_DTYPES = {"bf16": HISPARSE_KV_BF16, "fp8": HISPARSE_KV_FP8_E4M3}
+ROW_BYTES = {HISPARSE_KV_BF16: 1152, HISPARSE_KV_FP8_E4M3: 576}
+
 # replacement policies (hisparse_set_replacement)
 HISPARSE_POLICY_LRU = 0
 HISPARSE_POLICY_FIFO = 1
@@ -67,6 +73,8 @@ class hisparse_config(ctypes.Structure):
         ("resident_rows_per_layer", ctypes.c_int64),
         ("ctx_len", ctypes.POINTER(ctypes.c_int64)),
         ("ctx_capacity", ctypes.POINTER(ctypes.c_int64)),
+        ("kv_dtype", ctypes.c_int32), ("num_verify", ctypes.c_int32),
+        ("kv_scale", ctypes.POINTER(ctypes.c_float)),
     ]
 
 
@@ -146,6 +154,9 @@ def make_config(cfg: dict) -> tuple[hisparse_config, object]:
     cap = None
     if cfg.get("ctx_capacity") is not None:
         cap = (ctypes.c_int64 * len(cfg["ctx_capacity"]))(*[int(c) for c in cfg["ctx_capacity"]])
+    scl = None
+    if cfg.get("kv_scale") is not None:
+        scl = (ctypes.c_float * len(cfg["kv_scale"]))(*[float(v) for v in cfg["kv_scale"]])
     c = hisparse_config(
         num_requests=cfg["num_requests"], num_layers=cfg["num_layers"],
         index_share=cfg.get("index_share", 1), latent_dim=cfg.get("latent_dim", 576),
@@ -155,8 +166,14 @@ def make_config(cfg: dict) -> tuple[hisparse_config, object]:
         resident_rows_per_layer=cfg.get("resident_rows_per_layer", 0),
         ctx_len=ctypes.cast(ctx, ctypes.POINTER(ctypes.c_int64)),
         ctx_capacity=ctypes.cast(cap, ctypes.POINTER(ctypes.c_int64)) if cap is not None else None,
+        kv_dtype=kv_dtype_code(cfg.get("kv_dtype", "bf16")), num_verify=cfg.get("num_verify", 1),
+        kv_scale=ctypes.cast(scl, ctypes.POINTER(ctypes.c_float)) if scl is not None else None,
     )
-    return c, (ctx, cap)
+    return c, (ctx, cap, scl)
+
+
+def kv_dtype_code(v) -> int:
+    return KV_DTYPES[v] if isinstance(v, str) else int(v)
 
 
 def hisparse_last_error() -> str:
@@ -313,7 +330,11 @@ class HiSparse:
         self.ws_bytes = hisparse_workspace_bytes(self._c)
         self.kv_rows = hisparse_kv_rows_per_layer(self._c)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
-        self.kv = [torch.zeros((self.kv_rows, 576), dtype=torch.bfloat16, device=self.device)
+        self.kv_dtype = kv_dtype_code(self.cfg.get("kv_dtype", "bf16"))
+        self.row_bytes = ROW_BYTES[self.kv_dtype]
+        # bf16 rows: [rows, 576] bfloat16; FP8 rows: [rows, 576] uint8 codes
+        kv_torch_dtype = torch.bfloat16 if self.kv_dtype == HISPARSE_KV_BF16 else torch.uint8
+        self.kv = [torch.zeros((self.kv_rows, 576), dtype=kv_torch_dtype, device=self.device)
                    for _ in range(self.cfg["num_layers"])]
         self.pool = hisparse_create_pool(self._c, self.workspace.data_ptr(), self.ws_bytes,
                                          [t.data_ptr() for t in self.kv], self.stream)
@@ -326,9 +347,11 @@ class HiSparse:
         return hisparse_host_rows(self.pool, r, l)
 
     def host_rows(self, r: int, l: int) -> np.ndarray:
-        """NumPy view of the host pool rows of (r, l): [capacity_r][576] bf16 bits."""
+        """NumPy view of the host pool rows of (r, l): [capacity_r][576] bf16 bits
+        (uint16) or FP8 E4M3 codes (uint8)."""
         cap = self.cfg.get("ctx_capacity") or self.cfg["ctx_len"]
-        return host_array(self.host_rows_ptr(r, l), (int(cap[r]), 576))
+        dt = np.uint16 if self.kv_dtype == HISPARSE_KV_BF16 else np.uint8
+        return host_array(self.host_rows_ptr(r, l), (int(cap[r]), 576), dt)
 
     def set_block_table(self, r: int, bt) -> None:
         hisparse_set_block_table(self.pool, r, bt, self.stream)

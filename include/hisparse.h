@@ -21,8 +21,9 @@
  * Row ids index one KV tensor per layer: rows [0, resident_rows_per_layer)
  * hold resident pages (block b = rows [b*page_size, (b+1)*page_size)), and
  * rows [resident_rows_per_layer + r*B, ... + B) are the hot rows of request
- * r.  A KV row is latent_dim = 576 bf16 values (512 "nope" + 64 rope); the
- * value vector is its first v_dim = 512 values.
+ * r.  A KV row is latent_dim = 576 values (512 "nope" + 64 rope), stored
+ * as bf16 or as FP8 E4M3 codes with a per-layer scale (kv_dtype); the value
+ * vector is its first v_dim = 512 values.
  *
  * Replacement rule (exact; the pages say only that LRU metadata drives
  * replacement and that the current selection must be served): every slot
@@ -74,6 +75,15 @@ typedef int32_t hisparse_status;
 #define HISPARSE_ERR_APPEND 16u /* append with the tail page not resident or the context full (not appended) */
 #define HISPARSE_ERR_UNMATERIALIZED 32u /* a row was needed from the host pool before it was written there */
 
+/* KV row formats (hisparse_config.kv_dtype).  The vLLM Hybrid HiSparse blog
+ * (measurements section) runs its benchmark with an FP8 KV cache; the blog
+ * does not describe the format, so the reading here is the plainest one:
+ * every latent value is one OCP FP8 E4M3 code (bias 7, no infinities, 0x7F
+ * and 0xFF are NaN, largest finite 448), and the row of layer l stands for
+ * x = decode(code) * kv_scale[l]. */
+#define HISPARSE_KV_BF16 0     /* 576 bf16 values per row, 1152 bytes */
+#define HISPARSE_KV_FP8_E4M3 1 /* 576 FP8 E4M3 codes per row, 576 bytes */
+
 /* Replacement policies (hisparse_set_replacement). */
 #define HISPARSE_POLICY_LRU 0    /* victims: least recently used first (default) */
 #define HISPARSE_POLICY_FIFO 1   /* victims: earliest filled first; a hit does not refresh */
@@ -97,6 +107,12 @@ typedef struct {
   const int64_t* ctx_capacity; /* [R] host array or NULL (= ctx_len): the length the context may
                                   grow to by hisparse_append; sizes the host pool, the block
                                   table and the position map; copied */
+  int32_t kv_dtype;      /* HISPARSE_KV_BF16 (0) or HISPARSE_KV_FP8_E4M3 (1): format of the
+                            host pool rows and of the KV tensors */
+  int32_t num_verify;    /* T >= 1 query tokens per request per step (1 + speculative tokens);
+                            0 is read as 1.  T > 1 is multi-token verification (see below) */
+  const float* kv_scale; /* [L] host array or NULL (= 1.0): scale of each layer's FP8 rows
+                            (finite, > 0); ignored for bf16 rows; copied */
 } hisparse_config;
 
 /* Message describing the calling thread's last failure ("" if none). */
@@ -112,11 +128,12 @@ hisparse_status hisparse_kv_rows_per_layer(const hisparse_config* cfg, int64_t* 
 /* Create a pool on the current device.
  *   d_workspace: device buffer of at least hisparse_workspace_bytes bytes,
  *                256-byte aligned; owned by the caller, must outlive the pool.
- *   d_kv:        host array of L device pointers; d_kv[l] is a bf16 tensor
- *                [kv_rows_per_layer][576], 16-byte aligned, caller-owned.
+ *   d_kv:        host array of L device pointers; d_kv[l] is a tensor of
+ *                [kv_rows_per_layer] rows in the pool's row format (576 bf16
+ *                or 576 FP8 codes), 16-byte aligned, caller-owned.
  *   stream:      used to initialise the workspace (synchronised before return).
  * Allocates the pinned, device-mapped host pool: request r, layer l holds
- * ctx_r rows of 576 bf16 (filled by the caller via hisparse_host_rows).
+ * capacity_r rows (filled by the caller via hisparse_host_rows).
  * Every slot starts empty and every page host-only.
  * Errors: EINVAL (bad config, null or misaligned pointers, workspace too
  * small), ENOMEM (pinned allocation failed), EHIP, EDEVICE. */
@@ -127,10 +144,11 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
  * Synchronises the device first.  NULL is ignored. */
 void hisparse_destroy_pool(hisparse_pool* pool);
 
-/* Host address of the pool rows of (request r, layer l): bf16 bits
- * [ctx_r][576], row-major, for the caller to fill before resolving.
- * NULL on a bad argument. */
-uint16_t* hisparse_host_rows(hisparse_pool* pool, int32_t r, int32_t l);
+/* Host address of the pool rows of (request r, layer l), [capacity_r] rows
+ * in the pool's row format (bf16 bits [576] or FP8 E4M3 codes [576]),
+ * row-major, for the caller to fill before resolving.  NULL on a bad
+ * argument. */
+void* hisparse_host_rows(hisparse_pool* pool, int32_t r, int32_t l);
 
 /* Set the block table of request r: host_bt[page] is the resident block id
  * of that page, or -1 (host-only placeholder); n_pages must equal
@@ -219,7 +237,8 @@ hisparse_status hisparse_reset_state(hisparse_pool* pool, void* stream);
  * RESOLVE and decode read ctx_r on the device, so a step after appends
  * accepts the new positions. */
 
-/* Append one token per request: d_rows [L][R][576] bf16 (16-byte aligned)
+/* Append one token per request: d_rows [L][R] rows in the pool's row
+ * format (16-byte aligned)
  * is the new token's latent row of every layer, written to the resident
  * block of the request's tail page (page ctx_r / page_size) at row ctx_r %
  * page_size; then ctx_r += 1.  The caller leases the tail block with
@@ -227,7 +246,7 @@ hisparse_status hisparse_reset_state(hisparse_pool* pool, void* stream);
  * whose tail page is a placeholder, or whose context is at capacity, is
  * left unchanged and sets HISPARSE_ERR_APPEND.  Enqueue only
  * (graph-capturable). */
-hisparse_status hisparse_append(hisparse_pool* pool, const uint16_t* d_rows, void* stream);
+hisparse_status hisparse_append(hisparse_pool* pool, const void* d_rows, void* stream);
 
 /* Materialise completed pages: for every (layer, request), copy the rows
  * [held_lr, floor(ctx_r / page_size) * page_size) from their resident

@@ -28,15 +28,20 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def attend(q_bits: np.ndarray, x_bits: np.ndarray, scale: float, v_dim: int = 512):
-    """q_bits: uint16 [H, D]; x_bits: uint16 [n, D] (valid rows only).
+    """q_bits: uint16 [H, D]; x_bits: uint16 [n, D] bf16 rows (valid rows only).
 
     Returns (O float64 [H, v_dim], lse float64 [H]).
     """
-    q = bf16_bits_to_f64(q_bits)
+    x = bf16_bits_to_f64(x_bits) if x_bits.shape[0] else np.zeros((0, q_bits.shape[1]))
+    return attend_f64(bf16_bits_to_f64(q_bits), x, scale, v_dim)
+
+
+def attend_f64(q: np.ndarray, x: np.ndarray, scale: float, v_dim: int = 512):
+    """The same with the query and the rows already widened to float64
+    (FP8 rows: their decoded values times the layer scale)."""
     H = q.shape[0]
-    if x_bits.shape[0] == 0:
+    if x.shape[0] == 0:
         return np.zeros((H, v_dim)), np.full(H, -np.inf)
-    x = bf16_bits_to_f64(x_bits)
     s = float(scale) * (q @ x.T)  # [H, n]
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)

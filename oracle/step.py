@@ -20,7 +20,8 @@ import numpy as np
 
 from tracegen import kv_rows, q_block
 
-from .attention import attend
+from .attention import attend, attend_f64, bf16_bits_to_f64
+from .fp8 import e4m3_to_f64
 from .resolve import LruState, resolve
 
 
@@ -48,8 +49,12 @@ class OracleDecoder:
         """fp64 (O [H, 512], lse [H]) of (request r, layer l) at step t."""
         w = self.w
         pos = [int(p) for p in sel if p >= 0]
-        x = kv_rows(w.seed, r, l, pos, w.latent_dim) if pos else np.zeros((0, w.latent_dim), np.uint16)
         q = q_block(w.seed, t, l, r, w.num_heads, w.latent_dim)
+        if w.kv_dtype == "fp8":
+            codes = kv_rows(w.seed, r, l, pos, w.latent_dim, fp8_scale=w.fp8_scale(l)) if pos else \
+                np.zeros((0, w.latent_dim), np.uint8)
+            return attend_f64(bf16_bits_to_f64(q), row_values(w, l, codes), w.scale, w.v_dim)
+        x = kv_rows(w.seed, r, l, pos, w.latent_dim) if pos else np.zeros((0, w.latent_dim), np.uint16)
         return attend(q, x, w.scale, w.v_dim)
 
     def step(self, t: int, sel_t: np.ndarray, attend_pairs=None):
@@ -69,6 +74,14 @@ class OracleDecoder:
         return res, att
 
 
+def row_values(w, l: int, rows: np.ndarray) -> np.ndarray:
+    """float64 values of stored rows of layer l: bf16 bits, or FP8 E4M3 codes
+    times the layer's scale."""
+    if w.kv_dtype == "fp8":
+        return e4m3_to_f64(rows) * w.fp8_scale(l)
+    return bf16_bits_to_f64(rows)
+
+
 class SimulatedKV:
     """Mirror of the device KV tensor of every layer, for small workloads."""
 
@@ -83,19 +96,19 @@ class SimulatedKV:
                 lo = page * w.page_size
                 hi = min(lo + w.page_size, w.ctx_len[r])
                 for l in range(w.num_layers):
-                    data = kv_rows(w.seed, r, l, list(range(lo, hi)), w.latent_dim)
+                    data = kv_rows(w.seed, r, l, list(range(lo, hi)), w.latent_dim, fp8_scale=w.fp8_scale(l))
                     for i, p in enumerate(range(lo, hi)):
                         self.rows[(l, int(blk) * w.page_size + (p - lo))] = data[i]
 
     def apply_fetches(self, l: int, r: int, fetches, hot_base: int) -> None:
         if not fetches:
             return
-        data = kv_rows(self.w.seed, r, l, [p for p, _ in fetches], self.w.latent_dim)
+        data = kv_rows(self.w.seed, r, l, [p for p, _ in fetches], self.w.latent_dim, fp8_scale=self.w.fp8_scale(l))
         for i, (_, s) in enumerate(fetches):
             self.rows[(l, hot_base + s)] = data[i]
 
     def gather(self, l: int, row_ids) -> np.ndarray:
         ids = [int(x) for x in row_ids if x >= 0]
         if not ids:
-            return np.zeros((0, self.w.latent_dim), np.uint16)
+            return np.zeros((0, self.w.latent_dim), np.uint8 if self.w.kv_dtype == "fp8" else np.uint16)
         return np.stack([self.rows[(l, i)] for i in ids])

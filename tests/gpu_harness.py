@@ -77,10 +77,15 @@ def check_hot_bytes(hs, w, dec, pairs, t):
             continue
         owners = np.array([st.owner[s] for s in slots], dtype=np.int64)
         base = dec.hot_base(r)
-        got = hs.kv[l][torch.from_numpy(base + slots).to(hs.device)].view(torch.int16).cpu().numpy().view(np.uint16)
         from tracegen.values import kv_key
 
-        want = fill.rows(kv_key(w.seed, r, l), owners, w.latent_dim)
+        idx = torch.from_numpy(base + slots).to(hs.device)
+        if w.kv_dtype == "fp8":
+            got = hs.kv[l][idx].cpu().numpy()
+            want = fill.rows_fp8(kv_key(w.seed, r, l), owners, w.latent_dim, w.fp8_scale(l))
+        else:
+            got = hs.kv[l][idx].view(torch.int16).cpu().numpy().view(np.uint16)
+            want = fill.rows(kv_key(w.seed, r, l), owners, w.latent_dim)
         assert np.array_equal(got, want), f"hot row bytes t={t} l={l} r={r}"
 
 

@@ -33,6 +33,12 @@ def _load():
         lib.tg_fill_rows.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int64]
         lib.tg_fill_rows.restype = None
+        lib.tg_fill_fp8.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_float]
+        lib.tg_fill_fp8.restype = None
+        lib.tg_fill_rows_fp8.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_float]
+        lib.tg_fill_rows_fp8.restype = None
         _lib = lib
     return _lib
 
@@ -52,4 +58,17 @@ def rows(key: int, positions, dim: int) -> np.ndarray:
     out = np.empty((pos.shape[0], dim), dtype=np.uint16)
     _load().tg_fill_rows(ctypes.c_void_p(out.ctypes.data), key, ctypes.c_void_p(pos.ctypes.data),
                          pos.shape[0], dim)
+    return out
+
+
+def fill_ptr_fp8(ptr: int, key: int, e0: int, n: int, scale: float) -> None:
+    """Write n FP8 E4M3 codes (elements e0..e0+n of stream ``key`` / scale) at ptr."""
+    _load().tg_fill_fp8(ctypes.c_void_p(ptr), key, e0, n, scale)
+
+
+def rows_fp8(key: int, positions, dim: int, scale: float) -> np.ndarray:
+    pos = np.ascontiguousarray(positions, dtype=np.int64).reshape(-1)
+    out = np.empty((pos.shape[0], dim), dtype=np.uint8)
+    _load().tg_fill_rows_fp8(ctypes.c_void_p(out.ctypes.data), key, ctypes.c_void_p(pos.ctypes.data),
+                             pos.shape[0], dim, scale)
     return out

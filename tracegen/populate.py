@@ -2,7 +2,8 @@
 
 Works on any object that exposes ``host_rows_ptr(r, l)`` (host address of
 the pinned pool rows of request r, layer l), ``set_block_table(r, bt)``,
-``kv`` (list of per-layer device tensors [rows, 576] bf16) and ``device``;
+``kv`` (list of per-layer device tensors [rows, 576], bf16 or uint8 FP8
+codes) and ``device``;
 it does not import the decode library.  Resident pages are copies of the
 host rows they mirror.
 """
@@ -19,7 +20,10 @@ def fill_host_pool(hs, w) -> None:
     for r in range(w.num_requests):
         n = int(w.ctx_len[r]) * w.latent_dim
         for l in range(w.num_layers):
-            fill.fill_ptr(hs.host_rows_ptr(r, l), kv_key(w.seed, r, l), 0, n)
+            if w.kv_dtype == "fp8":
+                fill.fill_ptr_fp8(hs.host_rows_ptr(r, l), kv_key(w.seed, r, l), 0, n, w.fp8_scale(l))
+            else:
+                fill.fill_ptr(hs.host_rows_ptr(r, l), kv_key(w.seed, r, l), 0, n)
 
 
 def upload_residency(hs, w) -> None:
@@ -39,8 +43,11 @@ def upload_residency(hs, w) -> None:
         idx = torch.from_numpy(rows).to(hs.device)
         for l in range(w.num_layers):
             host = hs.host_rows(r, l)
-            data = torch.from_numpy(np.ascontiguousarray(host[pos]).view(np.int16)).to(hs.device)
-            hs.kv[l].view(torch.int16)[idx] = data
+            if w.kv_dtype == "fp8":
+                hs.kv[l][idx] = torch.from_numpy(np.ascontiguousarray(host[pos])).to(hs.device)
+            else:
+                data = torch.from_numpy(np.ascontiguousarray(host[pos]).view(np.int16)).to(hs.device)
+                hs.kv[l].view(torch.int16)[idx] = data
 
 
 def populate(hs, w) -> None:

@@ -22,7 +22,10 @@ Definition (the same in the NumPy code below and in ``fill.c``):
   the sum minus 6 has mean 0 and variance ~1).  Every step is integer or
   exact, so the float32 value is identical on any machine and in any
   language.
-* That float32 is rounded to bfloat16 with round-to-nearest-even.
+* That float32 is rounded to bfloat16 with round-to-nearest-even.  For
+  FP8 pools the float32 is first divided by the layer's scale (float32
+  division) and rounded to an OCP FP8 E4M3 code, nearest with ties to the
+  even code.
 
 KV element (seed, request r, layer l, position p, dim d) uses stream words
 ``(seed, TAG_KV, r, l)`` and element index ``p * dim + d``.  Query element
@@ -103,10 +106,49 @@ def bf16_values(key: int, elems: np.ndarray) -> np.ndarray:
     return f32_to_bf16_bits(float_values(key, elems))
 
 
-def kv_rows(seed: int, r: int, l: int, positions, dim: int = 576) -> np.ndarray:
-    """bf16 bits [len(positions), dim] of the host KV rows at ``positions``."""
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 to OCP FP8 E4M3 codes (nearest, ties to the even code;
+    magnitudes past 448 saturate to 448).  Returns uint8 codes.
+
+    Works on the float32 bit fields: a normal E4M3 keeps the top 3 stored
+    mantissa bits of float32 (exponent -6..8, bias 7); below 2^-6 the code
+    counts multiples of 2^-9 (subnormals).  Either way the kept bits are the
+    float32 significand (with its leading 1) shifted right, and the dropped
+    bits decide the rounding.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.int64)
+    sign = ((b >> 31) & 1).astype(np.uint8) << np.uint8(7)
+    e32 = (b >> 23) & 0xFF
+    sig = np.where(e32 > 0, (b & 0x7FFFFF) | (1 << 23), 0)  # float32 subnormals are far below 2^-10: -> 0
+    E = e32 - 127
+    # value = sig * 2^(E - 23); in units of the target quantum 2^(max(E, -6) - 3):
+    qexp = np.maximum(E, -6) - 3
+    shift = np.clip(qexp - (E - 23), 0, 62)  # >= 20 for normals, more for subnormals
+    q = sig >> shift
+    rem = sig - (q << shift)
+    half = np.where(shift > 0, np.int64(1) << np.maximum(shift - 1, 0), 0)
+    up = (rem > half) | ((rem == half) & (shift > 0) & ((q & 1) == 1))
+    q = q + up.astype(np.int64)
+    # assemble: q counts quanta 2^qexp; for E >= -6, q in [8, 16] (16 = carry into the next binade)
+    mag = np.where(E >= -6, ((np.maximum(E, -6) + 7) << 3) + (q - 8), q)  # subnormal/min-normal: code = q
+    mag = np.where(e32 == 0, 0, mag)
+    mag = np.minimum(mag, 0x7E)  # saturate at 448
+    return (sign | mag.astype(np.uint8)).astype(np.uint8)
+
+
+def fp8_values(key: int, elems: np.ndarray, scale: float) -> np.ndarray:
+    """FP8 E4M3 codes of the stream's values divided by ``scale`` (float32)."""
+    v = float_values(key, elems) / np.float32(scale)
+    return f32_to_e4m3_codes(v.astype(np.float32))
+
+
+def kv_rows(seed: int, r: int, l: int, positions, dim: int = 576, fp8_scale: float | None = None) -> np.ndarray:
+    """Host KV rows at ``positions``: bf16 bits uint16 [n, dim], or, with
+    ``fp8_scale``, FP8 E4M3 codes uint8 [n, dim] of value / fp8_scale."""
     pos = np.asarray(positions, dtype=np.uint64).reshape(-1)
     e = pos[:, None] * np.uint64(dim) + np.arange(dim, dtype=np.uint64)[None, :]
+    if fp8_scale is not None:
+        return fp8_values(kv_key(seed, r, l), e, fp8_scale)
     return bf16_values(kv_key(seed, r, l), e)
 
 

@@ -52,6 +52,8 @@ class Workload:
     v_dim: int = V_DIM
     block_tables: list = field(default_factory=list)  # per request int32 [n_pages]
     resident_blocks: int = 0
+    kv_dtype: str = "bf16"  # "bf16" or "fp8" (OCP FP8 E4M3 codes with a per-layer scale)
+    kv_scale: list | None = None  # [L] FP8 row scales
 
     @property
     def groups(self) -> int:
@@ -64,6 +66,10 @@ class Workload:
     @property
     def resident_rows_per_layer(self) -> int:
         return self.resident_blocks * self.page_size
+
+    def fp8_scale(self, l: int) -> float | None:
+        """Scale of layer l's FP8 rows, or None for bf16 rows."""
+        return float(self.kv_scale[l]) if self.kv_dtype == "fp8" else None
 
     def n_pages(self, r: int) -> int:
         return -(-int(self.ctx_len[r]) // self.page_size)
@@ -80,7 +86,8 @@ class Workload:
                     v_dim=self.v_dim, top_k=self.top_k, hot_slots=self.hot_slots,
                     page_size=self.page_size, num_heads=self.num_heads,
                     resident_rows_per_layer=self.resident_rows_per_layer,
-                    ctx_len=[int(c) for c in self.ctx_len])
+                    ctx_len=[int(c) for c in self.ctx_len], kv_dtype=self.kv_dtype,
+                    kv_scale=list(self.kv_scale) if self.kv_dtype == "fp8" else None)
 
 
 def _assign_residency(w: Workload) -> None:
@@ -142,3 +149,18 @@ def named_workload(name: str) -> Workload:
 
 
 NAMED = ("tiny", "r8_ctx32k", "r32_ctx128k_l4", "mixed_r64", "miss_1m")
+
+
+def default_fp8_scales(num_layers: int) -> list:
+    """Per-layer FP8 scales of the synthetic pools: 2^-5 * (1 + l/4) (float32).
+    The generated values lie in [-6, 6], so value / scale stays inside E4M3's
+    +-448; layer 0's scale is a power of two, the others are not."""
+    return [float(np.float32(2.0 ** -5 * (1 + l / 4))) for l in range(num_layers)]
+
+
+def with_fp8(w: Workload, scales=None) -> Workload:
+    """The same workload with FP8 E4M3 host and device rows."""
+    w.kv_dtype = "fp8"
+    w.kv_scale = list(scales) if scales is not None else default_fp8_scales(w.num_layers)
+    w.name = w.name + "_fp8"
+    return w
