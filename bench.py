@@ -25,7 +25,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, published
-ROW_BYTES = 1152
 
 
 def pmc_bytes(workload: str, kernel: str):
@@ -101,14 +100,15 @@ def residency_probe(torch, H, w, dev, ctx=8192):
     R, L, page = w.num_requests, w.num_layers, w.page_size
     cfg = dict(num_requests=R, num_layers=L, index_share=w.index_share, top_k=w.top_k, hot_slots=w.hot_slots,
                page_size=page, num_heads=w.num_heads, resident_rows_per_layer=R * page,
-               ctx_len=[ctx] * R, ctx_capacity=[ctx + page] * R)
+               ctx_len=[ctx] * R, ctx_capacity=[ctx + page] * R, kv_dtype=w.kv_dtype, kv_scale=w.kv_scale)
     hs = H.HiSparse(cfg, dev)
+    row_bytes = hs.row_bytes
     try:
         for r in range(R):
             bt = np.full((ctx + page + page - 1) // page, -1, np.int32)
             bt[ctx // page] = r
             hs.set_block_table(r, bt)
-        rows = torch.zeros((L, R, 576), dtype=torch.int16, device=dev)
+        rows = torch.zeros((L, R, 576), dtype=torch.int16 if row_bytes == 1152 else torch.uint8, device=dev)
         stream = torch.cuda.current_stream(dev)
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         hs.append(rows)  # warm
@@ -124,10 +124,10 @@ def residency_probe(torch, H, w, dev, ctx=8192):
         n_ctx, held = hs.get_lengths()
         if not (np.all(n_ctx == ctx + page) and np.all(held == ctx + page)):
             return None
-        wb_bytes = R * L * page * ROW_BYTES
+        wb_bytes = R * L * page * row_bytes
         wb_ms = e1.elapsed_time(e2)
         return {"append_us": round(e0.elapsed_time(e1) * 1e3 / (page - 1), 2),
-                "append_bytes": R * L * ROW_BYTES,
+                "append_bytes": R * L * row_bytes,
                 "writeback_us": round(wb_ms * 1e3, 2), "writeback_bytes": wb_bytes,
                 "writeback_GBs": round(wb_bytes / (wb_ms * 1e-3) / 1e9, 2),
                 "writeback_us_per_step_amortised": round(wb_ms * 1e3 / page, 2)}
@@ -187,6 +187,8 @@ def main() -> int:
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
     ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="KV row format: bf16 (the named workloads) or FP8 E4M3 codes with a per-layer scale")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -201,7 +203,7 @@ def main() -> int:
     import torch
 
     from host_offloaded_kv_amd import hisparse as H
-    from tracegen import named_workload
+    from tracegen import named_workload, with_fp8
     from tracegen.populate import populate, queries
 
     if not torch.cuda.is_available():
@@ -210,6 +212,8 @@ def main() -> int:
     H.load()
     dev = torch.device("cuda:0")
     w = named_workload(args.workload)
+    if args.kv_dtype == "fp8":
+        w = with_fp8(w)
     n_steps = args.warmup + args.steps
     L, R, K, Hh, B = w.num_layers, w.num_requests, w.top_k, w.num_heads, w.hot_slots
 
@@ -221,7 +225,8 @@ def main() -> int:
     cfg["host_coherent"] = args.host_coherent
     t0 = time.time()
     hs = H.HiSparse(cfg, dev)
-    log(f"pool created ({sum(w.ctx_len) * L * ROW_BYTES / 1e9:.2f} GB pinned) in {time.time() - t0:.1f}s")
+    row_bytes = hs.row_bytes
+    log(f"pool created ({sum(w.ctx_len) * L * row_bytes / 1e9:.2f} GB pinned) in {time.time() - t0:.1f}s")
     t0 = time.time()
     populate(hs, w)
     log(f"host pool filled and residency uploaded in {time.time() - t0:.1f}s")
@@ -377,14 +382,14 @@ def main() -> int:
 
     # algorithmic bytes per step (split partials and repeated reads are
     # overhead, not counted)
-    host_bytes = misses.sum(axis=(1, 2)) * ROW_BYTES  # per step
-    attn_bytes = (valid.sum(axis=(1, 2)) * ROW_BYTES
+    host_bytes = misses.sum(axis=(1, 2)) * row_bytes  # per step
+    attn_bytes = (valid.sum(axis=(1, 2)) * row_bytes
                   + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4))
     attn_flops = valid.sum(axis=(1, 2)) * 2 * Hh * (576 + 512)
     meta_bytes = L * R * (2 * 3 * B * 4 + 2 * K * 4 + 12) + misses.sum(axis=(1, 2)) * 8
     hbm_step_bytes = attn_bytes + host_bytes + meta_bytes  # hot-row writes counted once in host_bytes
     last_valid = valid[-1].sum()
-    dec_bytes = last_valid * ROW_BYTES + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4)
+    dec_bytes = last_valid * row_bytes + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4)
 
     kern = {}
     for name, (n, tot_ms) in prof.items():
@@ -408,6 +413,16 @@ def main() -> int:
                       "achieved": round(ach, 2) if ach is not None else None, "bound": bound, "peak": peak,
                       "unit": unit, "frac": round(ach / peak, 4) if (peak and ach is not None) else None,
                       "busy_share_of_step": round(tot_ms / ms_total, 4)}
+    if "sparse_mla_decode" in kern:
+        kern["sparse_mla_decode"]["in_step_note"] = (
+            "in-step launches: every layer of an index-share group but the last is decoded without key splits "
+            "on few CUs while the next layer's miss fetch streams; the group's last layer is split over the "
+            "whole GPU; full_gpu_launch: one launch over all layers of a group on all CUs")
+        if dec_us:
+            ach_full = dec_bytes / (dec_us * 1e-6) / 1e9
+            kern["sparse_mla_decode"]["full_gpu_launch"] = {
+                "us": round(dec_us, 2), "alg_bytes": int(dec_bytes), "achieved": round(ach_full, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_full / HBM_PEAK_GBS, 4)}
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kern[dom]
     pmc = pmc_bytes(w.name, dom)
@@ -467,7 +482,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "requests": R, "ctx": int(w.ctx_len[0]), "layers": L,
                    "index_share": w.index_share, "heads": Hh, "top_k": K, "hot_slots": B,
-                   "seed": w.seed, "host_coherent": args.host_coherent, "policy": args.policy},
+                   "seed": w.seed, "host_coherent": args.host_coherent, "policy": args.policy,
+                   "kv_dtype": w.kv_dtype},
         "roofline": roofline,
         "kernels": kern,
         "step": {"us": round(ms_step * 1e3, 2),
