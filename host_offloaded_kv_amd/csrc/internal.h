@@ -102,7 +102,8 @@ struct ResolveArgs {
   int32_t layer_begin;
   int32_t n_layers;
   int32_t num_requests;
-  int32_t top_k;
+  int32_t top_k;            // selection width: num_verify * K
+  int32_t tok_k;            // K: entries per verify token (a repeat inside one token's list is an error)
   int32_t hot_slots;
   int32_t page_shift;
   int64_t resident_rows;
@@ -178,6 +179,8 @@ struct hisparse_pool {
   size_t resolve_lds = 0;
   int32_t policy = HISPARSE_POLICY_LRU;
   uint64_t policy_seed = 0;
+  int32_t T = 1;                        // verify tokens per request per step
+  int32_t W = 0;                        // resolve selection width T * K
   // device views into the workspace
   int32_t *owner, *stamp, *lru, *last_t, *miss_count, *bt, *bt_off, *ctx_d, *cap_d, *hv_d;
   int16_t* posmap;

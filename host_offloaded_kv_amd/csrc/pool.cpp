@@ -54,8 +54,9 @@ hisparse_status check_config(const hisparse_config* c) {
     set_error("kv_dtype must be HISPARSE_KV_BF16 or HISPARSE_KV_FP8_E4M3");
     return HISPARSE_EINVAL;
   }
-  if (c->num_verify < 0 || c->num_verify > 1) {
-    set_error("num_verify must be 0 or 1");
+  const int T = c->num_verify < 1 ? 1 : c->num_verify;
+  if (c->num_verify < 0 || (int64_t)T * c->top_k > kMaxTopK) {
+    set_error("num_verify must be >= 0 and num_verify * top_k <= 4096");
     return HISPARSE_EINVAL;
   }
   if (c->kv_scale && c->kv_dtype == HISPARSE_KV_FP8_E4M3) {
@@ -69,8 +70,8 @@ hisparse_status check_config(const hisparse_config* c) {
     set_error("top_k must be in [1, 4096]");
     return HISPARSE_EINVAL;
   }
-  if (c->hot_slots < c->top_k || c->hot_slots > kMaxHotSlots) {
-    set_error("hot_slots must satisfy top_k <= hot_slots <= 8192");
+  if (c->hot_slots < c->top_k * (c->num_verify < 1 ? 1 : c->num_verify) || c->hot_slots > kMaxHotSlots) {
+    set_error("hot_slots must satisfy num_verify * top_k <= hot_slots <= 8192");
     return HISPARSE_EINVAL;
   }
   if (c->page_size < 1 || ilog2_exact(c->page_size) < 0 || c->page_size > (1 << 20)) {
@@ -111,29 +112,32 @@ hisparse_status check_config(const hisparse_config* c) {
   return HISPARSE_OK;
 }
 
+int verify_tokens(const hisparse_config* c) { return c->num_verify < 1 ? 1 : c->num_verify; }
+
 Layout make_layout(const hisparse_config* c) {
   Layout L{};
-  const size_t R = c->num_requests, NL = c->num_layers, B = c->hot_slots, K = c->top_k;
+  const size_t R = c->num_requests, NL = c->num_layers, B = c->hot_slots;
+  const size_t T = verify_tokens(c), W = T * c->top_k;  // decode sees R * T query sets
   int64_t bt_entries = 0;
   for (size_t r = 0; r < R; ++r) bt_entries += (capacity_of(c, (int)r) + c->page_size - 1) / c->page_size;
   L.bt_entries = bt_entries;
   L.layers_batched = c->index_share;
-  const int s1 = decode_splits(1, c->num_requests, c->num_heads, c->top_k);
-  const int sg = decode_splits(c->index_share, c->num_requests, c->num_heads, c->top_k);
+  const int s1 = decode_splits(1, (int)(R * T), c->num_heads, c->top_k);
+  const int sg = decode_splits(c->index_share, (int)(R * T), c->num_heads, c->top_k);
   L.splits_max = s1 > sg ? s1 : sg;
   size_t part_1 = 0;  // one layer, any request count up to R (pipelined chunks)
   for (size_t nreq = 1; nreq <= R; ++nreq) {
-    const int sn = decode_splits(1, (int)nreq, c->num_heads, c->top_k);
-    if (sn > 1) part_1 = std::max(part_1, (size_t)sn * nreq * c->num_heads * kPartW);
+    const int sn = decode_splits(1, (int)(nreq * T), c->num_heads, c->top_k);
+    if (sn > 1) part_1 = std::max(part_1, (size_t)sn * nreq * T * c->num_heads * kPartW);
   }
-  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * c->num_heads * kPartW : 0;
+  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * T * c->num_heads * kPartW : 0;
   size_t off = 0;
   L.owner = off; off = align256(off + NL * R * B * 4);
   L.stamp = off; off = align256(off + NL * R * B * 4);
   L.lru = off; off = align256(off + NL * R * B * 4);
   L.last_t = off; off = align256(off + NL * R * 4);
   L.miss_count = off; off = align256(off + NL * R * 4);
-  L.fetch = off; off = align256(off + NL * R * K * 8);
+  L.fetch = off; off = align256(off + NL * R * W * 8);
   L.bt = off; off = align256(off + (size_t)bt_entries * 4);
   L.bt_off = off; off = align256(off + R * 4);
   L.ctx = off; off = align256(off + R * 4);
@@ -267,12 +271,14 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     for (int l = 0; l < NL; ++l) p->kv_scale[l] = cfg->kv_scale[l];
   p->cfg.kv_scale = p->kv_scale.data();
   p->kv_rows = cfg->resident_rows_per_layer + (int64_t)R * cfg->hot_slots;
+  p->T = verify_tokens(cfg);
+  p->W = p->T * cfg->top_k;
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) {
     delete p;
     return hip_fail(e, "hipGetDevice");
   }
-  p->resolve_lds = resolve_lds_bytes(cfg->top_k, cfg->hot_slots);
+  p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots);
   int max_lds = 0;
   e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
   if (e != hipSuccess) {
@@ -455,7 +461,7 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.lru = p->lru;
   a.last_t = p->last_t;
   a.miss_count = p->miss_count + (size_t)layer_begin * p->cfg.num_requests;
-  a.fetch = p->fetch + (size_t)layer_begin * p->cfg.num_requests * p->cfg.top_k;
+  a.fetch = p->fetch + (size_t)layer_begin * p->cfg.num_requests * p->W;
   a.bt = p->bt;
   a.bt_off = p->bt_off;
   a.ctx = p->ctx_d;
@@ -463,7 +469,8 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.layer_begin = layer_begin;
   a.n_layers = n_layers;
   a.num_requests = p->cfg.num_requests;
-  a.top_k = p->cfg.top_k;
+  a.top_k = p->W;
+  a.tok_k = p->cfg.top_k;
   a.hot_slots = p->cfg.hot_slots;
   int ps = 0;
   while ((1 << ps) < p->cfg.page_size) ++ps;
@@ -486,7 +493,7 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
   const int R = p->cfg.num_requests;
   FetchArgs f;
   f.miss_count = p->miss_count + (size_t)layer * R + r0;
-  f.fetch = p->fetch + ((size_t)layer * R + r0) * p->cfg.top_k;
+  f.fetch = p->fetch + ((size_t)layer * R + r0) * p->W;
   f.host_rows = p->host_rows_d;
   f.kv = p->kv_d;
   f.layer_begin = layer;
@@ -494,7 +501,7 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
   f.num_requests = nreq;
   f.request_begin = r0;
   f.total_requests = R;
-  f.top_k = p->cfg.top_k;
+  f.top_k = p->W;
   f.hot_slots = p->cfg.hot_slots;
   f.row_chunks = p->row_bytes / 16;
   f.resident_rows = p->cfg.resident_rows_per_layer;
@@ -506,8 +513,9 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
 
 // splits: key-range splits per (layer, request, head group); 0 picks the
 // count that fills the GPU (decode_splits).
-// nreq: requests per layer covered by the pointers (a chunk of the pool's
-// requests when decoding one layer piecewise).
+// nreq: query sets per layer covered by the pointers -- requests times
+// verify tokens, for all requests or a chunk of them when one layer is
+// decoded piecewise.
 hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, int32_t nreq,
                                const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out, float* d_lse,
                                hipStream_t s, int splits = 0) {
@@ -571,7 +579,8 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, cons
     set_error("hisparse_sparse_mla_decode: scale must be finite");
     return HISPARSE_EINVAL;
   }
-  return enqueue_decode(p, layer, 1, p->cfg.num_requests, d_q, d_rows, scale, d_out, d_lse, (hipStream_t)stream);
+  return enqueue_decode(p, layer, 1, p->cfg.num_requests * p->T, d_q, d_rows, scale, d_out, d_lse,
+                        (hipStream_t)stream);
 }
 
 hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
@@ -595,7 +604,7 @@ hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* p, int32_t laye
     set_error("hisparse_sparse_mla_decode_layers: scale must be finite");
     return HISPARSE_EINVAL;
   }
-  return enqueue_decode(p, layer_begin, n_layers, p->cfg.num_requests, d_q, d_rows, scale, d_out, d_lse,
+  return enqueue_decode(p, layer_begin, n_layers, p->cfg.num_requests * p->T, d_q, d_rows, scale, d_out, d_lse,
                         (hipStream_t)stream);
 }
 
@@ -612,6 +621,7 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
   }
   const auto& c = p->cfg;
   const size_t R = c.num_requests, K = c.top_k, H = c.num_heads;
+  const size_t T = p->T, W = p->W;  // verify tokens; the decode sees R * T query sets per layer
   const int G = c.index_share;
   hipStream_t s = (hipStream_t)stream;
   hipStream_t fs = p->fetch_stream;
@@ -627,16 +637,16 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
     // chunks, so that only the last chunk's decode is exposed.  A whole
     // layer decoded under a later fetch runs unsplit (64 CUs or fewer, no
     // partials); chunks of the last layer are split to fill the GPU.
-    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * K, d_rows + (size_t)l0 * R * K,
+    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
                                          d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
     if (G == 1 && C == 1) {
       // One layer, one unit: nothing to overlap, so no fork; the fetch takes
       // the whole-group launch shape.
-      const size_t pr = (size_t)l0 * R;
+      const size_t pr = (size_t)l0 * R * T;  // first query set of the layer
       if ((st = enqueue_fetch(p, l0, 1, 0, (int)R, p->fetch_wg_all, s))) return st;
-      st = enqueue_decode(p, l0, 1, (int)R, d_q + pr * H * kLatent, d_rows + pr * K, scale, d_out + pr * H * kVDim,
-                          d_lse + pr * H, s);
+      st = enqueue_decode(p, l0, 1, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                          d_out + pr * H * kVDim, d_lse + pr * H, s);
       if (st) return st;
       continue;
     }
@@ -658,9 +668,9 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
     }
     for (int u = 0; u < nu; ++u) {
       const Unit& un = units[u];
-      const size_t pr = (size_t)un.layer * R + un.r0;  // first (layer, request) of the unit
+      const size_t pr = ((size_t)un.layer * R + un.r0) * T;  // first query set of the unit
       if ((e = hipStreamWaitEvent(s, p->ev_fetch[u], 0)) != hipSuccess) return hip_fail(e, "hisparse_step: join");
-      st = enqueue_decode(p, un.layer, 1, un.nreq, d_q + pr * H * kLatent, d_rows + pr * K, scale,
+      st = enqueue_decode(p, un.layer, 1, (int)(un.nreq * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
                           d_out + pr * H * kVDim, d_lse + pr * H, s, un.splits);
       if (st) return st;
     }

@@ -65,7 +65,7 @@ constexpr int kSelChunks = kMaxTopK / kMetaThreads;       // 64-entry chunks of 
 constexpr int kSlotChunks = kMaxHotSlots / kMetaThreads;  // 64-entry chunks of the order array per wave (max)
 
 struct LdsMap {
-  size_t sel, mpos, mj, vic, tflag, region, total;
+  size_t sel, mpos, mj, vic, rows, tflag, region, total;
 };
 
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -82,7 +82,8 @@ __host__ __device__ inline LdsMap lds_map(int K, int B) {
   m.mpos = m.sel + 4 * (size_t)K;
   m.mj = m.mpos + 4 * (size_t)K;
   m.vic = m.mj + 4 * (size_t)K;
-  m.tflag = m.vic + 4 * (size_t)K;
+  m.rows = m.vic + 4 * (size_t)K;
+  m.tflag = m.rows + 4 * (size_t)K;
   m.region = m.tflag + round16((size_t)B);
   // sort keys: (position, index) on the unsorted-input path, (priority,
   // slot) of the random replacement policy
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   int32_t* mpos_s = (int32_t*)(smem + M.mpos);
   int32_t* mj_s = (int32_t*)(smem + M.mj);
   int32_t* vic_s = (int32_t*)(smem + M.vic);
+  int32_t* row_s = (int32_t*)(smem + M.rows);  // row of every resolved entry (copies read it)
   unsigned char* tflag_s = smem + M.tflag;
   unsigned long long* key_s = (unsigned long long*)(smem + M.region);
 
@@ -251,8 +253,11 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   const int KP = next_pow2(K);
 
   if (!fast) {
-    // Repeated positions: sort (position, index) and keep the earliest
-    // index of each position.
+    // Repeated positions: sort (position, index); the earliest index of
+    // each position is the one resolved.  A later entry in the same
+    // verify token's list as the entry before it is an error (padding); an
+    // entry of a later token shares the row of the earliest entry, which it
+    // names as sel = -2 - index (padding to the classification below).
     for (int i = tid; i < KP; i += kMetaThreads) {
       const int p = i < K ? sel_s[i] : -1;
       key_s[i] = p >= 0 ? (((unsigned long long)(uint32_t)p << 32) | (uint32_t)i) : ~0ull;
@@ -261,9 +266,15 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     bitonic_sort(key_s, KP, tid);
     for (int i = tid + 1; i < KP; i += kMetaThreads) {
       const unsigned long long x = key_s[i];
-      if (x != ~0ull && (x >> 32) == (key_s[i - 1] >> 32)) {
-        sel_s[(uint32_t)x] = -1;
+      if (x == ~0ull || (x >> 32) != (key_s[i - 1] >> 32)) continue;
+      const int j = (int)(uint32_t)x, jp = (int)(uint32_t)key_s[i - 1];
+      if (j / a.tok_k == jp / a.tok_k) {
+        sel_s[j] = -1;
         errbits |= HISPARSE_ERR_DUP;
+      } else {
+        int f = i - 1;
+        while (f > 0 && (key_s[f - 1] >> 32) == (x >> 32)) --f;
+        sel_s[j] = -2 - (int)(uint32_t)key_s[f];
       }
     }
     __syncthreads();
@@ -307,7 +318,10 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
           miss = true;
         }
       }
-      if (!miss) rows_out[j] = row;
+      if (!miss) {
+        rows_out[j] = row;
+        row_s[j] = row;
+      }
     }
     mb[c] = __ballot(miss);
     mloc += __popcll(mb[c]);
@@ -402,9 +416,17 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     stamp_g[v] = t;
     tflag_s[v] |= 5;
     rows_out[j] = (int)(hot_base + v);
+    row_s[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
   __syncthreads();
+  if (!fast) {
+    // Entries that repeat a position of an earlier verify token take its row.
+    for (int j = tid; j < K; j += kMetaThreads) {
+      const int p = sel_s[j];
+      if (p <= -2) rows_out[j] = row_s[-2 - p];
+    }
+  }
 
   // New order: slots with stamp < t (untouched; old order), then every slot
   // stamped t, by slot index.

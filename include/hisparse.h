@@ -69,7 +69,7 @@ typedef int32_t hisparse_status;
 
 /* Device error flag bits (hisparse_check_errors). */
 #define HISPARSE_ERR_RANGE 1u /* a selected position outside [-1, ctx_r) */
-#define HISPARSE_ERR_DUP 2u   /* a position repeated within one selection (later copies dropped) */
+#define HISPARSE_ERR_DUP 2u   /* a position repeated within one token's selection (later copies dropped) */
 #define HISPARSE_ERR_STEP 4u  /* step index negative or below the last one seen by a (request, layer) */
 #define HISPARSE_ERR_ROW 8u   /* decode saw a row id outside the KV tensor (treated as padding) */
 #define HISPARSE_ERR_APPEND 16u /* append with the tail page not resident or the context full (not appended) */
@@ -114,6 +114,22 @@ typedef struct {
   const float* kv_scale; /* [L] host array or NULL (= 1.0): scale of each layer's FP8 rows
                             (finite, > 0); ignored for bf16 rows; copied */
 } hisparse_config;
+
+/* Multi-token verification (num_verify = T > 1).  The vLLM Hybrid HiSparse
+ * blog says that speculative decoding runs through a per-step replayable
+ * resolver plan whose verification steps share the request's hot state, and
+ * that the hot buffer must hold every verification token at once.  Reading:
+ * each step carries T query tokens per request (1 + speculative tokens),
+ * each with its own K-entry selection; one RESOLVE per (request, layer)
+ * covers the T selections concatenated (token-major, width T*K): a position
+ * selected by several tokens is resolved once, at its earliest entry, and
+ * every copy gets that row; a repeat inside one token's list is an error
+ * (HISPARSE_ERR_DUP, padding).  Counts are over the distinct positions.
+ * Requires T*K <= 4096 and B >= T*K (the blog sizes B = (T + 1) * K).
+ * Selections, row ids, queries and outputs then carry a token axis after
+ * the request axis: d_topk [..][R][T][K], d_rows [..][R][T][K],
+ * d_q [..][R][T][H][576], d_out [..][R][T][H][512], d_lse [..][R][T][H];
+ * d_counts stays [..][R][3]. */
 
 /* Message describing the calling thread's last failure ("" if none). */
 const char* hisparse_last_error(void);

@@ -23,6 +23,7 @@ from tracegen import kv_rows, q_block
 from .attention import attend, attend_f64, bf16_bits_to_f64
 from .fp8 import e4m3_to_f64
 from .resolve import LruState, resolve
+from .verify import resolve_verify
 
 
 class OracleDecoder:
@@ -35,21 +36,27 @@ class OracleDecoder:
         return self.w.resident_rows_per_layer + r * self.w.hot_slots
 
     def resolve_step(self, t: int, sel_t: np.ndarray):
-        """sel_t: int32 [groups][R][K].  Returns {(l, r): ResolveResult}."""
+        """sel_t: int32 [groups][R][K] ([groups][R][T][K] with T verify
+        tokens).  Returns {(l, r): ResolveResult}."""
         w = self.w
         out = {}
         for g in range(w.groups):
             for l in range(g * w.index_share, (g + 1) * w.index_share):
                 for r in self.requests:
-                    out[(l, r)] = resolve(self.states[(l, r)], sel_t[g][r], t, w.ctx_len[r],
-                                          w.block_tables[r], w.page_size, self.hot_base(r))
+                    if w.num_verify > 1:
+                        out[(l, r)] = resolve_verify(self.states[(l, r)], sel_t[g][r], t, w.ctx_len[r],
+                                                     w.block_tables[r], w.page_size, self.hot_base(r))
+                    else:
+                        out[(l, r)] = resolve(self.states[(l, r)], sel_t[g][r], t, w.ctx_len[r],
+                                              w.block_tables[r], w.page_size, self.hot_base(r))
         return out
 
-    def attend_one(self, t: int, l: int, r: int, sel: np.ndarray):
-        """fp64 (O [H, 512], lse [H]) of (request r, layer l) at step t."""
+    def attend_one(self, t: int, l: int, r: int, sel: np.ndarray, token: int = 0):
+        """fp64 (O [H, 512], lse [H]) of (request r, layer l, verify token)
+        at step t; ``sel`` is that token's selection."""
         w = self.w
-        pos = [int(p) for p in sel if p >= 0]
-        q = q_block(w.seed, t, l, r, w.num_heads, w.latent_dim)
+        pos = list(dict.fromkeys(int(p) for p in sel if p >= 0))  # a repeat inside one list is padding
+        q = q_block(w.seed, w.query_step(t, token), l, r, w.num_heads, w.latent_dim)
         if w.kv_dtype == "fp8":
             codes = kv_rows(w.seed, r, l, pos, w.latent_dim, fp8_scale=w.fp8_scale(l)) if pos else \
                 np.zeros((0, w.latent_dim), np.uint8)

@@ -1,0 +1,106 @@
+"""GPU parity of multi-token verification (num_verify = T > 1): one RESOLVE
+over the T verify tokens' selections per (request, layer), then decode of
+every (request, token) with its own query.
+
+Bit-exact: row ids of every entry (copies across tokens share a row),
+counts over distinct positions, LRU state and hot-row bytes; attention per
+token within the usual bound.
+"""
+
+import numpy as np
+import pytest
+
+from tests.gpu_harness import LSE_TOL, O_TOL, check_hot_bytes, check_state, log, make_pool
+from oracle.step import OracleDecoder
+from tracegen import fill, make_workload, named_workload, with_fp8
+from tracegen.populate import queries
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from host_offloaded_kv_amd import hisparse
+
+    hisparse.load()
+    fill.build(force=False)
+
+
+def _run(w, steps, attend_every=1, attend_pairs=None, dup_step=None):
+    import torch
+
+    T, L, R, K, H = w.num_verify, w.num_layers, w.num_requests, w.top_k, w.num_heads
+    tr = w.trace(steps)  # [steps][G][R][T][K]
+    if dup_step is not None:
+        tr[dup_step, 0, 0, T - 1, 1] = tr[dup_step, 0, 0, T - 1, 0]  # a repeat inside one token's list
+    hs = make_pool(w)
+    dev = hs.device
+    rows = torch.empty((L, R, T, K), dtype=torch.int32, device=dev)
+    counts = torch.empty((L, R, 3), dtype=torch.int32, device=dev)
+    out = torch.empty((L, R, T, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((L, R, T, H), dtype=torch.float32, device=dev)
+    d_step = torch.zeros(1, dtype=torch.int32, device=dev)
+    dec = OracleDecoder(w)
+    pairs = [(l, r) for l in range(L) for r in range(R)]
+    worst = 0.0
+    for t in range(steps):
+        d_step.fill_(t)
+        topk = torch.from_numpy(np.ascontiguousarray(tr[t])).to(dev)
+        q = torch.from_numpy(queries(w, t).view(np.int16)).to(dev)
+        hs.step(d_step, topk, q, w.scale, rows, counts, out, lse)
+        torch.cuda.synchronize(dev)
+        g_rows, g_counts = rows.cpu().numpy(), counts.cpu().numpy()
+        res = dec.resolve_step(t, tr[t])
+        for (l, r), rr in res.items():
+            assert np.array_equal(g_rows[l, r].reshape(-1), np.asarray(rr.rows, np.int32)), f"rows t={t} l={l} r={r}"
+            assert tuple(int(x) for x in g_counts[l, r]) == (rr.n_resident, rr.n_hit, rr.n_miss), \
+                f"counts t={t} l={l} r={r}"
+        check_state(hs, dec, pairs, t)
+        check_hot_bytes(hs, w, dec, pairs, t)
+        if t % attend_every == 0 or t == steps - 1:
+            g_out, g_lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+            for (l, r) in (attend_pairs or pairs):
+                g = l // w.index_share
+                for i in range(T):
+                    o_ref, lse_ref = dec.attend_one(t, l, r, tr[t][g][r][i], token=i)
+                    err = np.abs(g_out[l, r, i] - o_ref).max() / np.abs(o_ref).max()
+                    worst = max(worst, err)
+                    assert err <= O_TOL, f"O t={t} l={l} r={r} token={i} err {err:.3e}"
+                    assert np.abs(g_lse[l, r, i] - lse_ref).max() <= LSE_TOL
+    flags = hs.check_errors()
+    hs.close()
+    log(f"{w.name}: T={T} {steps} steps ok, worst O rel err {worst:.3e}, flags {flags:#x}")
+    return flags
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_verify_small_configs(case):
+    rng = np.random.default_rng(900 + case)
+    T = int(rng.choice([2, 3, 4]))
+    K = int(rng.choice([16, 50, 128]))
+    B = T * K + int(rng.integers(0, K + 1))
+    R, L = int(rng.integers(1, 4)), int(rng.choice([1, 2, 4]))
+    share = int(rng.choice([s for s in (1, 2, 4) if L % s == 0]))
+    ctx = [int(rng.integers(T * K, 8 * T * K)) for _ in range(R)]
+    w = make_workload(f"verify{case}", 950 + case, R, L, share, ctx, 16 * int(rng.integers(1, 5)), K, B, 8,
+                      float(rng.choice([0.5, 0.8])), 0.8, str(rng.choice(["none", "tail", "tail+half"])),
+                      page_size=int(rng.choice([16, 64])))
+    w.num_verify = T
+    if case == 3:
+        w = with_fp8(w)
+    log(f"verify config {case}: T={T} R={R} L={L} g={share} K={K} B={B} ctx={ctx} res={w.residency} {w.kv_dtype}")
+    flags = _run(w, w.steps, dup_step=3 if case == 1 else None)
+    from host_offloaded_kv_amd.hisparse import HISPARSE_ERR_DUP
+
+    assert flags == (HISPARSE_ERR_DUP if case == 1 else 0)
+
+
+def test_verify_mtp1_r8_ctx32k():
+    """One speculative token on the 8 x 32K workload: T*K = 4096 = B."""
+    w = named_workload("r8_ctx32k")
+    w.num_verify = 2
+    w.name = "r8_ctx32k_mtp1"
+    assert _run(w, 8, attend_every=3, attend_pairs=[(0, 0), (0, 5)]) == 0

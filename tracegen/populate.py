@@ -56,9 +56,12 @@ def populate(hs, w) -> None:
 
 
 def queries(w, t: int) -> np.ndarray:
-    """bf16 bits [L][R][H][576] of step t's queries."""
-    out = np.empty((w.num_layers, w.num_requests, w.num_heads, w.latent_dim), np.uint16)
+    """bf16 bits [L][R][H][576] of step t's queries ([L][R][T][H][576] with
+    T = num_verify > 1 verify tokens, token i using query counter t*T + i)."""
+    T = w.num_verify
+    out = np.empty((w.num_layers, w.num_requests, T, w.num_heads, w.latent_dim), np.uint16)
     for l in range(w.num_layers):
         for r in range(w.num_requests):
-            fill.fill_array(out[l, r], q_key(w.seed, t, l, r))
-    return out
+            for i in range(T):
+                fill.fill_array(out[l, r, i], q_key(w.seed, w.query_step(t, i), l, r))
+    return out[:, :, 0] if T == 1 else out

@@ -54,6 +54,7 @@ class Workload:
     resident_blocks: int = 0
     kv_dtype: str = "bf16"  # "bf16" or "fp8" (OCP FP8 E4M3 codes with a per-layer scale)
     kv_scale: list | None = None  # [L] FP8 row scales
+    num_verify: int = 1  # T query tokens per request per step (multi-token verification)
 
     @property
     def groups(self) -> int:
@@ -75,10 +76,20 @@ class Workload:
         return -(-int(self.ctx_len[r]) // self.page_size)
 
     def trace(self, steps: int | None = None) -> np.ndarray:
-        """int32 [steps][groups][R][K] selections."""
-        return selection_trace(self.seed, self.ctx_len, self.top_k,
-                               self.steps if steps is None else steps,
-                               self.groups, self.retain, self.alpha)
+        """int32 [steps][groups][R][K] selections; with T = num_verify > 1,
+        [steps][groups][R][T][K], where token i of step t is step t*T + i of
+        the single-token drift trace (consecutive tokens overlap)."""
+        n = self.steps if steps is None else steps
+        T = self.num_verify
+        tr = selection_trace(self.seed, self.ctx_len, self.top_k, n * T, self.groups, self.retain, self.alpha)
+        if T == 1:
+            return tr
+        G, R, K = tr.shape[1], tr.shape[2], tr.shape[3]
+        return np.ascontiguousarray(tr.reshape(n, T, G, R, K).transpose(0, 2, 3, 1, 4))
+
+    def query_step(self, t: int, token: int = 0) -> int:
+        """Counter of the query of verify token ``token`` at step t."""
+        return t * self.num_verify + token
 
     def config_dict(self) -> dict:
         return dict(num_requests=self.num_requests, num_layers=self.num_layers,
@@ -87,7 +98,8 @@ class Workload:
                     page_size=self.page_size, num_heads=self.num_heads,
                     resident_rows_per_layer=self.resident_rows_per_layer,
                     ctx_len=[int(c) for c in self.ctx_len], kv_dtype=self.kv_dtype,
-                    kv_scale=list(self.kv_scale) if self.kv_dtype == "fp8" else None)
+                    kv_scale=list(self.kv_scale) if self.kv_dtype == "fp8" else None,
+                    num_verify=self.num_verify)
 
 
 def _assign_residency(w: Workload) -> None:
