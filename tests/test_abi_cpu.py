@@ -54,6 +54,12 @@ def test_sizes():
     dict(resident_rows_per_layer=100),
     dict(ctx_len=[0, 5]),
     dict(latent_dim=512),
+    dict(kv_dtype=2),                        # unknown row format
+    dict(num_verify=-1),
+    dict(num_verify=3),                      # T * K = 6144 > 4096
+    dict(num_verify=2, hot_slots=4095),      # B < T * K
+    dict(kv_dtype="fp8", kv_scale=[1.0, 0.0, 1.0, 1.0]),
+    dict(kv_dtype="fp8", kv_scale=[1.0, float("nan"), 1.0, 1.0]),
 ])
 def test_bad_configs_rejected(bad):
     c, keep = _cfg(**bad)
@@ -61,6 +67,17 @@ def test_bad_configs_rejected(bad):
         H.hisparse_workspace_bytes(c)
     assert ei.value.status == H.HISPARSE_EINVAL
     assert H.hisparse_last_error()
+
+
+def test_row_formats_and_verify_tokens_size_the_workspace():
+    c1, k1 = _cfg()
+    c8, k8 = _cfg(kv_dtype="fp8", kv_scale=[0.5, 0.25, 1.0, 2.0])
+    assert H.hisparse_workspace_bytes(c8) == H.hisparse_workspace_bytes(c1)  # device metadata does not depend on it
+    assert H.hisparse_kv_rows_per_layer(c8) == H.hisparse_kv_rows_per_layer(c1)
+    c2, k2 = _cfg(num_verify=2)  # miss lists and partials grow with the token axis
+    assert H.hisparse_workspace_bytes(c2) > H.hisparse_workspace_bytes(c1)
+    c0, k0 = _cfg(num_verify=0)  # 0 reads as 1
+    assert H.hisparse_workspace_bytes(c0) == H.hisparse_workspace_bytes(c1)
 
 
 def test_null_arguments_rejected():
