@@ -10,7 +10,7 @@ import pytest
 from tests.gpu_harness import LSE_TOL, O_TOL, check_attention, check_hot_bytes, check_state, log, make_pool
 from oracle.step import OracleDecoder
 from tracegen.populate import queries
-from tracegen.workloads import make_workload
+from tracegen.workloads import make_workload, with_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -22,25 +22,28 @@ def _grouped_workload():
 
 
 class _Buffers:
+    """Step inputs and outputs; with T verify tokens the request axis of
+    rows, queries and outputs carries R*T query sets (token-minor)."""
+
     def __init__(self, w, dev):
         import torch
 
-        L, R, K, H = w.num_layers, w.num_requests, w.top_k, w.num_heads
-        self.rows = torch.full((L, R, K), -7, dtype=torch.int32, device=dev)
+        L, R, K, H, T = w.num_layers, w.num_requests, w.top_k, w.num_heads, w.num_verify
+        self.rows = torch.full((L, R, T * K), -7, dtype=torch.int32, device=dev)
         self.counts = torch.full((L, R, 3), -7, dtype=torch.int32, device=dev)
-        self.out = torch.full((L, R, H, 512), float("nan"), dtype=torch.float32, device=dev)
-        self.lse = torch.full((L, R, H), float("nan"), dtype=torch.float32, device=dev)
+        self.out = torch.full((L, R * T, H, 512), float("nan"), dtype=torch.float32, device=dev)
+        self.lse = torch.full((L, R * T, H), float("nan"), dtype=torch.float32, device=dev)
         self.d_step = torch.zeros(1, dtype=torch.int32, device=dev)
         G = L // w.index_share
-        self.topk = torch.empty((G, R, K), dtype=torch.int32, device=dev)
-        self.q = torch.empty((L, R, H, 576), dtype=torch.int16, device=dev)
+        self.topk = torch.empty((G, R, T * K), dtype=torch.int32, device=dev)
+        self.q = torch.empty((L, R * T, H, 576), dtype=torch.int16, device=dev)
 
     def load(self, w, t, sel_t):
         import torch
 
         self.d_step.fill_(t)
-        self.topk.copy_(torch.from_numpy(np.ascontiguousarray(sel_t, dtype=np.int32)))
-        self.q.copy_(torch.from_numpy(queries(w, t).view(np.int16)))
+        self.topk.copy_(torch.from_numpy(np.ascontiguousarray(sel_t, dtype=np.int32)).reshape(self.topk.shape))
+        self.q.copy_(torch.from_numpy(queries(w, t).view(np.int16)).reshape(self.q.shape))
 
     def snapshot(self):
         return tuple(x.cpu().numpy().copy() for x in (self.rows, self.counts, self.out, self.lse))
@@ -152,12 +155,17 @@ def test_overlapped_step_matches_oracle_and_sync_path():
     hs.close()
 
 
-def test_captured_step_graph_replays():
+@pytest.mark.parametrize("variant", ["bf16", "fp8_verify2"])
+def test_captured_step_graph_replays(variant):
     """A captured hisparse_step, replayed once per step with fresh inputs
-    copied in between, matches eager steps of a second pool bit for bit."""
+    copied in between, matches eager steps of a second pool bit for bit
+    (bf16 rows, and FP8 rows with two verify tokens per request)."""
     import torch
 
     w = _grouped_workload()
+    if variant == "fp8_verify2":
+        w = with_fp8(w)
+        w.num_verify = 2
     tr = w.trace(w.steps)
     eager = make_pool(w)
     ebuf = _Buffers(w, eager.device)
