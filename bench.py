@@ -161,7 +161,7 @@ def cpu_baseline(w, trace, budget_s=20.0):
         if time.time() - t0 > budget_s:
             break
     el = time.time() - t0
-    tokens = len(reqs) * steps
+    tokens = len(reqs) * steps * w.num_verify
     return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"requests {reqs} x all {w.num_layers} layers x steps 0..{steps - 1} "
                       f"(resolve + fp64 attention), {el:.1f} s"}
@@ -187,6 +187,9 @@ def main() -> int:
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
     ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
+    ap.add_argument("--num-verify", type=int, default=1,
+                    help="query tokens per request per step (multi-token verification); the value "
+                         "then counts verified query tokens")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="KV row format: bf16 (the named workloads) or FP8 E4M3 codes with a per-layer scale")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -214,8 +217,10 @@ def main() -> int:
     w = named_workload(args.workload)
     if args.kv_dtype == "fp8":
         w = with_fp8(w)
+    w.num_verify = args.num_verify
     n_steps = args.warmup + args.steps
     L, R, K, Hh, B = w.num_layers, w.num_requests, w.top_k, w.num_heads, w.hot_slots
+    T = w.num_verify
 
     log(f"workload {w.name}: R={R} L={L} g={w.index_share} ctx={w.ctx_len[0]} H={Hh} K={K} B={B}")
     t0 = time.time()
@@ -234,11 +239,11 @@ def main() -> int:
     d_steps = torch.arange(n_steps, dtype=torch.int32, device=dev)
     d_topk = torch.from_numpy(trace).to(dev)  # [T][G][R][K]
     q_all = np.stack([queries(w, t) for t in range(n_steps)])
-    d_q = torch.from_numpy(q_all.view(np.int16)).to(dev)  # [T][L][R][H][576]
-    d_rows = torch.empty((n_steps, L, R, K), dtype=torch.int32, device=dev)
+    d_q = torch.from_numpy(q_all.view(np.int16)).to(dev)  # [steps][L][R]([T])[H][576]
+    d_rows = torch.empty((n_steps, L, R, T * K), dtype=torch.int32, device=dev)
     d_counts = torch.empty((n_steps, L, R, 3), dtype=torch.int32, device=dev)
-    d_out = torch.empty((L, R, Hh, 512), dtype=torch.float32, device=dev)
-    d_lse = torch.empty((L, R, Hh), dtype=torch.float32, device=dev)
+    d_out = torch.empty((L, R * T, Hh, 512), dtype=torch.float32, device=dev)
+    d_lse = torch.empty((L, R * T, Hh), dtype=torch.float32, device=dev)
     torch.cuda.synchronize(dev)
     log("inputs staged in HBM")
 
@@ -375,21 +380,22 @@ def main() -> int:
     use_graph = graph_ms is not None and prof_graph is not None and graph_ms <= eager_ms
     ms_total = graph_ms if use_graph else eager_ms
     prof = prof_graph if use_graph else prof_eager
-    valid = counts.sum(axis=3)  # valid selections per (step, l, r)
+    valid = counts.sum(axis=3)  # distinct valid positions per (step, l, r)
+    entries = (d_rows[args.warmup:] >= 0).sum(dim=3).cpu().numpy().astype(np.int64)  # rows attended
     misses = counts[..., 2]
     ms_step = ms_total / args.steps
-    tokens_per_s = R * args.steps / (ms_total * 1e-3)
+    tokens_per_s = R * T * args.steps / (ms_total * 1e-3)
 
     # algorithmic bytes per step (split partials and repeated reads are
     # overhead, not counted)
     host_bytes = misses.sum(axis=(1, 2)) * row_bytes  # per step
-    attn_bytes = (valid.sum(axis=(1, 2)) * row_bytes
-                  + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4))
-    attn_flops = valid.sum(axis=(1, 2)) * 2 * Hh * (576 + 512)
+    attn_bytes = (entries.sum(axis=(1, 2)) * row_bytes
+                  + L * R * T * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4))
+    attn_flops = entries.sum(axis=(1, 2)) * 2 * Hh * (576 + 512)
     meta_bytes = L * R * (2 * 3 * B * 4 + 2 * K * 4 + 12) + misses.sum(axis=(1, 2)) * 8
     hbm_step_bytes = attn_bytes + host_bytes + meta_bytes  # hot-row writes counted once in host_bytes
-    last_valid = valid[-1].sum()
-    dec_bytes = last_valid * row_bytes + L * R * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4)
+    last_valid = entries[-1].sum()
+    dec_bytes = last_valid * row_bytes + L * R * T * (Hh * (576 * 2 + 512 * 4 + 4) + K * 4)
 
     kern = {}
     for name, (n, tot_ms) in prof.items():
@@ -483,7 +489,7 @@ def main() -> int:
         "config": {"workload": w.name, "requests": R, "ctx": int(w.ctx_len[0]), "layers": L,
                    "index_share": w.index_share, "heads": Hh, "top_k": K, "hot_slots": B,
                    "seed": w.seed, "host_coherent": args.host_coherent, "policy": args.policy,
-                   "kv_dtype": w.kv_dtype},
+                   "kv_dtype": w.kv_dtype, "num_verify": T},
         "roofline": roofline,
         "kernels": kern,
         "step": {"us": round(ms_step * 1e3, 2),
@@ -497,7 +503,7 @@ def main() -> int:
                    "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
-                        "sync_path_tokens_per_s": round(R * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
+                        "sync_path_tokens_per_s": round(R * T * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
         "decode_only": {"alg_bytes": int(dec_bytes),
                         "per_group_launch": {"us_per_step": round(dec_us, 2), "launches": w.groups,
                                              "achieved_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 2),

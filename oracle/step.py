@@ -68,7 +68,8 @@ class OracleDecoder:
         """Resolve every layer of every group, then attend.
 
         ``attend_pairs``: iterable of (l, r) to attend (default: all).
-        Returns (resolve results, {(l, r): (O, lse)}).
+        Returns (resolve results, {(l, r): (O, lse)}), keyed (l, r, token)
+        with T > 1 verify tokens.
         """
         res = self.resolve_step(t, sel_t)
         w = self.w
@@ -77,7 +78,11 @@ class OracleDecoder:
         att = {}
         for (l, r) in attend_pairs:
             g = l // w.index_share
-            att[(l, r)] = self.attend_one(t, l, r, sel_t[g][r])
+            if w.num_verify > 1:
+                for i in range(w.num_verify):
+                    att[(l, r, i)] = self.attend_one(t, l, r, sel_t[g][r][i], token=i)
+            else:
+                att[(l, r)] = self.attend_one(t, l, r, sel_t[g][r])
         return res, att
 
 
