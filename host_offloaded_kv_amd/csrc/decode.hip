@@ -11,24 +11,21 @@
 // same as attention over the full KV with the same selection.
 //
 // Work split: a workgroup handles (layer, request, group of up to 64 heads,
-// K split) with 8 wavefronts, two per SIMD, specialised by role:
-//  * score waves 0-3: wave 2 hb + rb keeps the Q of 32 heads (16 when the
-//    group has 16) in registers and scores rows 16 rb .. 16 rb + 15 of each
-//    32-row tile on 16x16x32 bf16 MFMA, one LDS read of the rows feeding
-//    both 16-head blocks; it applies the softmax with a reference max that
-//    the two row halves of a head agree on once, and writes the
+// K split) with 12 wavefronts, three per SIMD, specialised by role:
+//  * score waves 0-3: wave w keeps the Q of heads 16w .. 16w+15 in
+//    registers and scores all 32 rows of each tile on 16x16x32 bf16 MFMA;
+//    it applies the softmax with a reference max per head and writes the
 //    probabilities P to LDS as two bf16 planes, P = P_hi + P_lo;
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
 //    every head of the group (fp32 accumulators in registers); it multiplies
-//    the transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo
-//    (one tile read, two MFMAs).
-// Both roles stage the row tiles: the value waves gather the even tiles and
-// the score waves the odd ones, each through registers two tiles ahead, so
-// two tiles' loads are in flight per workgroup while a third is consumed.
-// The value waves run one tile behind the score waves, so each tile costs a
-// single workgroup barrier and the two waves sharing a SIMD overlap each
-// other's LDS and softmax latency with MFMA work.  Split partials are merged
-// by a second kernel.
+//    the transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo,
+//    one tile read feeding both MFMAs of two 16-head blocks;
+//  * loader waves 8-11: gather the row tiles through registers, two tiles
+//    ahead, and write them to LDS.
+// The value waves run one tile behind the score waves and the loaders one
+// tile ahead, so each tile costs a single workgroup barrier, and no compute
+// wave waits on a global load or an LDS store.  Split partials are merged by
+// a second kernel.
 //
 // Precision: a single bf16 P carries a relative rounding error up to 2^-8
 // per weight, which for near-uniform softmax weights shows up in O at the
@@ -42,11 +39,14 @@ namespace hs {
 namespace {
 
 constexpr int kT = 32;                        // rows per tile
-constexpr int kPitchChunks = kRowChunks + 1;  // LDS row pitch: 72 data + 1 pad chunk (1168 bytes)
+// LDS row pitch: 72 data + 2 pad chunks (1184 bytes).  With this pitch the
+// score waves' 16-row b128 reads run at the contiguous-read rate on gfx950;
+// a 1168-byte pitch costs them 1.5x and 1152 bytes 3x (measured).
+constexpr int kPitchChunks = kRowChunks + 2;
 constexpr int kPitch = kPitchChunks * 16;
-constexpr int kTileBytes = kT * kPitch;       // 37376
+constexpr int kTileBytes = kT * kPitch;       // 37888
 constexpr int kNBuf = 3;                      // tiles in LDS: scored, multiplied, being stored
-constexpr int kThreads = 512;                 // 8 wavefronts
+constexpr int kThreads = 768;                 // 12 wavefronts: 4 score, 4 value, 4 loader
 constexpr int kPPitch = kT + 8;               // bf16 per P row (80 bytes)
 constexpr float kMaxGrowLog2 = 64.f;          // P = 2^(s - m) may reach 2^64 before a second pass
 constexpr int kStage = kRowChunks / 8;        // 9 chunks per loading thread per tile
@@ -78,9 +78,9 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
   return r;
 }
 
-// Tile loads go through VGPRs: each loading thread fetches its part of a
-// tile with ordinary global loads two tiles ahead, and writes it to LDS
-// after the current tile's work.  On MI355X this sustains ~7.3 TB/s for a
+// Tile loads go through VGPRs: each loader thread fetches its part of a
+// tile with ordinary global loads two tiles ahead and writes it to LDS one
+// tile ahead of the score waves.  On MI355X this sustains ~7.3 TB/s for a
 // random 1152-byte row gather, where direct-to-LDS loads stayed under
 // 3 TB/s.  The loads use global-address-space pointers: flat loads would
 // also count against the LDS wait counter and be drained by every
@@ -203,138 +203,93 @@ struct DecodeSmem {
   unsigned char xs[kNBuf][kTileBytes];  // row tiles: scored, multiplied, being stored
   uint16_t ps[2][2][HG][kPPitch];       // [tile parity][hi, lo][head][row]
   int rowid[kMaxTopK];                  // row ids of the workgroup's K range
-  float mx[2][HG];                      // per-head maxima of the two row halves (exchange)
-  float lexact[2][HG], mfin[HG];        // weight sums of the two row halves, reference max
+  float lexact[HG], mfin[HG];           // weight sum and reference max per head
   int overflow;
-  int first_valid;                      // first valid index of the K range
 };
 
-// Iteration it of either role ends by moving tile it+1 from registers to its
-// LDS slot (last read in iteration it-1), if this role stages it, and then
-// starting the load of tile it+3 into the same registers.  The value waves
-// stage the even tiles and the score waves the odd ones, so two tiles'
-// loads are in flight while a third is consumed.
+// Score waves 0-3: wave w scores all 32 rows of each tile against heads
+// 16w .. 16w+15 (waves past the group's heads idle through the barriers).
+// The A operand (16 rows x 32 dims) comes from LDS, the B operand (Q) from
+// registers, and the two 16-row blocks of a tile give two accumulators, so
+// each wave sees every row of its heads and needs no exchange with another.
 template <int HG, bool FP8>
-__device__ __forceinline__ void stage_next(TileStage<FP8>& st, DecodeSmem<HG>& sm, const unsigned char* kv, int it,
-                                           int n_tiles,
-                                           int parity, int lt) {
-  const int nx = it + 1;
-  if (nx < n_tiles && (nx & 1) == parity) {
-    st.store(sm.xs[nx % kNBuf], lt);
-    if (nx + 2 < n_tiles) st.load(kv, sm.rowid + (nx + 2) * kT, lt);
-  }
-}
-
-// Score waves 0-3: wave w = 2 hb + rb scores rows 16 rb .. 16 rb + 15 of
-// each tile against QB blocks of 16 heads, heads 16 QB hb ..  (QB = 2 when
-// the group has 32 or more heads).  One A operand (16 rows x 32 dims, read
-// from LDS) feeds QB MFMAs, so the four score waves read the tile twice in
-// all instead of once each.  Each role runs its own loop with the same
-// barriers, so the registers of one role (Q here, the O accumulators there)
-// are never live in the other.
-template <int HG, bool FP8>
-__device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
-                                           float kvs, size_t head0, int n_tiles, int t_first, int w, int g,
-                                           int i16, int tid) {
-  constexpr int QB = HG >= 32 ? 2 : 1;     // 16-head blocks per score wave
-  constexpr int NHB = HG / (16 * QB);      // head-block groups (wave pairs with heads)
-  const int rb = w & 1, hb = w >> 1;
-  const bool active = hb < NHB;            // waves past the group's heads only stage tiles
-  // Q of the wave's heads as MFMA B operands: lane (g, i16) holds
-  // dims 32 s + 8 g .. +7 of head 16 (QB hb + qb) + i16.
-  f32x4 q[QB][kLatent / 32];
+__device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
+                                           int n_tiles, int w, int g, int i16) {
+  const bool active = 16 * w < HG;
+  // Q as MFMA B operands: lane (g, i16) holds dims 32 s + 8 g .. +7 of head 16 w + i16.
+  f32x4 q[kLatent / 32];
   if (active) {
+    gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * w + i16) * kLatent + 8 * g);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * (QB * hb + qb) + i16) * kLatent + 8 * g);
+    for (int s = 0; s < kLatent / 32; ++s) q[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
 #pragma unroll
-      for (int s = 0; s < kLatent / 32; ++s) q[qb][s] = __builtin_bit_cast(f32x4, qp[4 * s]);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[qb][s]), "+v"(q[qb][s + 1]));
+    for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[s]), "+v"(q[s + 1]));
   }
-  TileStage<FP8> st;
   // Scores in log2 units; FP8 rows carry the layer's scale.
   const float score_scale = a.scale_log2 * kvs;
-  // m: reference max per head (log2 units), shared by the two waves of a
-  // head; m_seen: the largest score this wave saw; l: sum of the unrounded
-  // weights of this wave's rows.
-  float m_run[QB], m_seen[QB], l_exact[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) m_run[qb] = m_seen[qb] = -INFINITY;
+  // m_run: reference max of this lane's head; m_seen: the largest score
+  // seen; l_exact: sum of the unrounded weights.
+  float m_run = -INFINITY, m_seen = -INFINITY, l_exact = 0.f;
 
   // Softmax with a fixed reference max per head: the first tile with a
-  // valid row sets m (the two waves of a head exchange their maxima once,
-  // through LDS), and P = 2^(s*scale*log2e - m) accumulates unnormalised, so
-  // the O accumulators are never rescaled inside the loop.  If a later tile
-  // exceeds m by more than 2^64 (never for ordinary scores), the whole range
-  // is recomputed once with m = the true maximum, which no tile can exceed.
-  // Both passes give the exact softmax.
+  // valid row sets m, and P = 2^(s*scale*log2e - m) accumulates
+  // unnormalised, so the O accumulators are never rescaled inside the loop.
+  // If a later tile exceeds m by more than 2^64 (never for ordinary scores),
+  // the whole range is recomputed once with m = the true maximum, which no
+  // tile can exceed.  Both passes give the exact softmax.
   for (int pass = 0; pass < 2; ++pass) {
-    if (n_tiles > 1) st.load(kv, sm.rowid + kT, tid);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_exact[qb] = 0.f;
-    lds_barrier();
+    l_exact = 0.f;
+    lds_barrier();  // tile 0 is in LDS
     for (int it = 0; it <= n_tiles; ++it) {
-      const bool xchg = pass == 0 && it == t_first;  // uniform: every wave takes the extra barrier
       if (active && it < n_tiles) {
         const unsigned char* xb = sm.xs[it % kNBuf];
-        f32x4 sacc[QB];
-        // A operand: lane (g, i16) reads row 16 rb + i16, dims 32 s + 8 g .. +7.
-        const unsigned char* xrow = xb + (16 * rb + i16) * kPitch + 16 * g;
+        f32x4 sacc[2];
+        // A operands: lane (g, i16) reads rows i16 and 16 + i16, dims 32 s + 8 g .. +7.
+        const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
 #pragma unroll
         for (int s = 0; s < kLatent / 32; ++s) {
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            if (s == 0)
-              mfma_score_first(sacc[qb], a0, q[qb][0]);
-            else
-              mfma_score(sacc[qb], a0, q[qb][s]);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
+          if (s == 0) {
+            mfma_score_first(sacc[0], a0, q[0]);
+            mfma_score_first(sacc[1], a1, q[0]);
+          } else {
+            mfma_score(sacc[0], a0, q[s]);
+            mfma_score(sacc[1], a1, q[s]);
           }
           if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
         }
         score_drain(sacc);
-        // lane (g, i16): head 16 (QB hb + qb) + i16, rows 16 rb + 4 g + v
-        const int4 rid = *reinterpret_cast<const int4*>(sm.rowid + it * kT + 16 * rb + 4 * g);
-        const bool valid[4] = {rid.x >= 0, rid.y >= 0, rid.z >= 0, rid.w >= 0};
-        float mx[QB];
+        // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
+        bool valid[2][4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          mx[qb] = -INFINITY;
+        for (int rb = 0; rb < 2; ++rb) {
+          const int4 rid = *reinterpret_cast<const int4*>(sm.rowid + it * kT + 16 * rb + 4 * g);
+          valid[rb][0] = rid.x >= 0;
+          valid[rb][1] = rid.y >= 0;
+          valid[rb][2] = rid.z >= 0;
+          valid[rb][3] = rid.w >= 0;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            sacc[qb][v] = valid[v] ? sacc[qb][v] * score_scale : -INFINITY;
-            mx[qb] = fmaxf(mx[qb], sacc[qb][v]);
+            sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * score_scale : -INFINITY;
+            mx = fmaxf(mx, sacc[rb][v]);
           }
-          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 16, 64));
-          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32, 64));
-          m_seen[qb] = fmaxf(m_seen[qb], mx[qb]);
         }
-        if (xchg) {
-          // first tile with a valid row: both waves of a head take the max
-          // over all 32 rows as the reference
-          if (g == 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_seen = fmaxf(m_seen, mx);
+        if (m_run == -INFINITY)
+          m_run = mx;  // first tile with a valid row (stays -inf while none is)
+        else if (mx > m_run + kMaxGrowLog2)
+          sm.overflow = 1;  // this pass is discarded
+        const int head = 16 * w + i16;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sm.mx[rb][16 * (QB * hb + qb) + i16] = mx[qb];
-          }
-          lds_barrier();
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(mx[qb], sm.mx[rb ^ 1][16 * (QB * hb + qb) + i16]);
-        } else {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (mx[qb] > m_run[qb] + kMaxGrowLog2) sm.overflow = 1;  // this pass is discarded
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int head = 16 * (QB * hb + qb) + i16;
+        for (int rb = 0; rb < 2; ++rb) {
           float p[4], r[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) p[v] = valid[v] ? __builtin_amdgcn_exp2f(sacc[qb][v] - m_run[qb]) : 0.f;
-          l_exact[qb] += (p[0] + p[1]) + (p[2] + p[3]);
+          for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
+          l_exact += (p[0] + p[1]) + (p[2] + p[3]);
           const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
           const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
                               __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
@@ -344,37 +299,22 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
           *reinterpret_cast<u32x2*>(&sm.ps[it & 1][0][head][16 * rb + 4 * g]) = hi;
           *reinterpret_cast<u32x2*>(&sm.ps[it & 1][1][head][16 * rb + 4 * g]) = lo;
         }
-      } else if (xchg) {
-        lds_barrier();
       }
-      stage_next(st, sm, kv, it, n_tiles, 1, tid);
       lds_barrier();
     }
     if (!sm.overflow) break;
-    // Recompute with the true maximum of each head over both waves' rows.
-    if (active && g == 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sm.mx[rb][16 * (QB * hb + qb) + i16] = m_seen[qb];
-    }
+    m_run = m_seen;  // recompute with the true maximum of the head
     lds_barrier();
-    if (active) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(m_seen[qb], sm.mx[rb ^ 1][16 * (QB * hb + qb) + i16]);
-    }
   }
 
-  // Reference max and partial weight sums per head for the value waves.
+  // Reference max and weight sum per head for the value waves.
   if (active) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float le = l_exact[qb];
-      le += __shfl_xor(le, 16, 64);
-      le += __shfl_xor(le, 32, 64);
-      if (g == 0) {
-        const int head = 16 * (QB * hb + qb) + i16;
-        sm.lexact[rb][head] = le;
-        if (rb == 0) sm.mfin[head] = m_run[qb];
-      }
+    float le = l_exact;
+    le += __shfl_xor(le, 16, 64);
+    le += __shfl_xor(le, 32, 64);
+    if (g == 0) {
+      sm.lexact[16 * w + i16] = le;
+      sm.mfin[16 * w + i16] = m_run;
     }
   }
   __syncthreads();
@@ -383,62 +323,54 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
 // Value waves 4-7: wave 4+cw owns output columns 128cw .. 128cw+127 of every
 // head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
 template <int HG, bool FP8>
-__device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
-                                           float kvs, size_t head0, int pair, int split, int hg, int n_tiles,
-                                           int t_first, int cw, int g, int i16, int lt) {
-  constexpr int NBP = HG / 16;  // 16-head blocks
-  f32x4 acc[8 * NBP];           // acc[mb * NBP + nb]: columns 16 mb.., heads 16 nb..
-  TileStage<FP8> st;
+__device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
+                                           int pair, int split, int hg, int n_tiles, int cw, int g, int i16) {
+  constexpr int NBP = HG / 16;             // 16-head blocks
+  constexpr int NBH = NBP > 2 ? 2 : NBP;   // head blocks per sweep over the tile (P operands in registers)
+  // acc[mb * NBP + nb]: columns 128 cw + 16 mb + 4 g + v, head 16 nb + i16
+  f32x4 acc[8 * NBP];
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NBP; ++nb) zero_acc(acc[mb * NBP + nb]);
-    // Tile 0 goes straight to LDS; tile 2 stays in flight in registers
-    // (tile 1 is the score waves').
-    if (n_tiles > 0) {
-      st.load(kv, sm.rowid, lt);
-      st.store(sm.xs[0], lt);
-    }
-    if (n_tiles > 2) st.load(kv, sm.rowid + 2 * kT, lt);
     lds_barrier();
-    // Iteration it multiplies tile it-1 (the score waves score tile it).
     for (int it = 0; it <= n_tiles; ++it) {
-      if (pass == 0 && it == t_first) lds_barrier();  // the score waves' max exchange
       if (it >= 1) {
         const int tp = it - 1;
         const unsigned char* xb = sm.xs[tp % kNBuf];
-        u32x4 bp[NBP], bq[NBP];  // P_hi, P_lo operands
-#pragma unroll
-        for (int nb = 0; nb < NBP; ++nb) {
-          bp[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][0][16 * nb + i16][8 * g]);
-          bq[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][1][16 * nb + i16][8 * g]);
-        }
-        // Transposed A operand: lane i16 of each 16-lane group supplies row
-        // j0 + i16/4, columns c0 + 4 (i16 % 4) .. +3, and receives column
-        // c0 + i16 of rows j0 .. j0+3 (j0 = 8 g, then 8 g + 4).  The
-        // transposed-read builtin takes no immediate offset, so an opaque
-        // per-iteration base keeps the compiler from hoisting 16
-        // precomputed addresses out of the loop.
+        // A operand (X^T, 16 cols x 32 rows) by two transposed reads: lane
+        // (g, i16) addresses row 8 g + i16 / 4 (+4), columns 128 cw + 16 mb +
+        // 4 (i16 % 4) .. +3, and receives column 128 cw + 16 mb + i16 of rows
+        // 8 g .. 8 g + 7.
         uint32_t xoff = (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
         asm volatile("" : "+v"(xoff));
         const lds_u8* xl = (const lds_u8*)xb + xoff;
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const s16x4 lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
-          const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          mfma_acc_after_valu(acc[mb * NBP], av, bp[0]);
+        for (int h0 = 0; h0 < NBP; h0 += NBH) {
+          // B operands: P_hi and P_lo of rows 8 g .. 8 g + 7, head 16 (h0 + nb) + i16.
+          u32x4 bp[NBH], bq[NBH];
 #pragma unroll
-          for (int nb = 1; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bp[nb]);
+          for (int nb = 0; nb < NBH; ++nb) {
+            bp[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][0][16 * (h0 + nb) + i16][8 * g]);
+            bq[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][1][16 * (h0 + nb) + i16][8 * g]);
+          }
 #pragma unroll
-          for (int nb = 0; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bq[nb]);
-          if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+          for (int mb = 0; mb < 8; ++mb) {
+            const s16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
+            const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            mfma_acc_after_valu(acc[mb * NBP + h0], av, bp[0]);
+#pragma unroll
+            for (int nb = 1; nb < NBH; ++nb) mfma_acc(acc[mb * NBP + h0 + nb], av, bp[nb]);
+#pragma unroll
+            for (int nb = 0; nb < NBH; ++nb) mfma_acc(acc[mb * NBP + h0 + nb], av, bq[nb]);
+            if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-      stage_next(st, sm, kv, it, n_tiles, 0, lt);
       lds_barrier();
     }
     if (!sm.overflow) break;
@@ -453,8 +385,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
     const int h = nb * 16 + i16;
     // O is normalised by the sum of the unrounded weights; P_hi + P_lo
     // carries each weight to about 2^-17 relative, far inside the tolerance.
-    const float lsum = sm.lexact[0][h] + sm.lexact[1][h];
-    const float lex = lsum;
+    const float lsum = sm.lexact[h];
     const float m = sm.mfin[h];
     if (a.splits == 1) {
       const float inv = lsum > 0.f ? kvs / lsum : 0.f;
@@ -465,7 +396,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
         __builtin_amdgcn_sched_barrier(0);  // few accumulators in VGPRs at a time
       }
       if (cw == 0 && g == 0)
-        a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lex)) * 0.69314718055994531f : -INFINITY;
+        a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
     } else {
       float* part = a.partial + (((size_t)pair * a.splits + split) * H + hg * HG + h) * kPartW;
       float* po = part + 128 * cw + 4 * g;
@@ -478,12 +409,50 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
       if (cw == 0 && g == 0) {
         part[kVDim] = m;
         part[kVDim + 1] = lsum;
-        part[kVDim + 2] = lex;
+        part[kVDim + 2] = lsum;
       }
     }
   }
 }
 
+// Loader waves 8-11: tile n is held in registers set n % 2 from two
+// iterations before it is needed.  Iteration it writes tile it+1 to its LDS
+// slot (last read in iteration it-2) and starts the load of tile it+3 into
+// the registers just freed, so two tiles' loads are in flight while the
+// compute waves work on tiles it and it-1.
+template <int HG, bool FP8>
+__device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned char* kv, int n_tiles, int lt) {
+  TileStage<FP8> s0, s1;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (n_tiles > 0) s0.load(kv, sm.rowid, lt);
+    if (n_tiles > 1) s1.load(kv, sm.rowid + kT, lt);
+    if (n_tiles > 0) {
+      s0.store(sm.xs[0], lt);
+      if (n_tiles > 2) s0.load(kv, sm.rowid + 2 * kT, lt);
+    }
+    lds_barrier();
+    for (int it = 0; it <= n_tiles; ++it) {
+      const int nx = it + 1;
+      if (nx < n_tiles) {
+        if (nx & 1) {
+          s1.store(sm.xs[nx % kNBuf], lt);
+          if (nx + 2 < n_tiles) s1.load(kv, sm.rowid + (nx + 2) * kT, lt);
+        } else {
+          s0.store(sm.xs[nx % kNBuf], lt);
+          if (nx + 2 < n_tiles) s0.load(kv, sm.rowid + (nx + 2) * kT, lt);
+        }
+      }
+      lds_barrier();
+    }
+    if (!sm.overflow) break;
+    lds_barrier();
+  }
+  __syncthreads();
+}
+
+// Every role passes the same barriers: one before the loop, one per
+// iteration (n_tiles + 1), one more before a second pass, and the final
+// __syncthreads().
 template <int HG, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   __shared__ __align__(16) DecodeSmem<HG> sm;
@@ -511,26 +480,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   const int k1 = min(K, k0 + per);
   const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
 
-  // Row ids of the whole K range, validated once, and the tile holding the
-  // first valid one (n_tiles if there is none).
-  if (tid == 0) {
-    sm.overflow = 0;
-    sm.first_valid = n_tiles * kT;
-  }
+  // Row ids of the whole K range, validated once.
+  if (tid == 0) sm.overflow = 0;
+  for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
   __syncthreads();
-  for (int k = tid; k < n_tiles * kT; k += kThreads) {
-    const int rid = load_row_id(a, rows, k0 + k, k1);
-    sm.rowid[k] = rid;
-    if (rid >= 0) atomicMin(&sm.first_valid, k);
-  }
-  __syncthreads();
-  const int t_first = sm.first_valid / kT;
 
   const size_t head0 = (size_t)pair * H + hg * HG;
   if (w < 4)
-    score_role<HG, FP8>(a, sm, kv, kvs, head0, n_tiles, t_first, w, g, i16, tid);
+    score_role<HG, FP8>(a, sm, kvs, head0, n_tiles, w, g, i16);
+  else if (w < 8)
+    value_role<HG, FP8>(a, sm, kvs, head0, pair, split, hg, n_tiles, w - 4, g, i16);
   else
-    value_role<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, n_tiles, t_first, w - 4, g, i16, tid - 256);
+    loader_role<HG, FP8>(sm, kv, n_tiles, tid - 512);
 }
 
 // Merge the split partials of one (layer, request, head) per wavefront.

@@ -49,7 +49,7 @@ def kernels(tmp_path_factory):
     text = out.read_text()
     found = {}
     for name in re.findall(r"^(_Z\w*decode_ws\w*):", text, re.M):
-        body = text.split(f"\n{name}:", 1)[1].split("s_endpgm", 1)[0]
+        body = text.split(f"\n{name}:", 1)[1].split(".Lfunc_end", 1)[0]
         found[name] = body.split("\n")
     assert len(found) >= 3, "expected the 16-, 32- and 64-head instantiations"
     return found
