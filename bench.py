@@ -374,6 +374,9 @@ def main() -> int:
     if flags:
         log(f"device error flags {flags:#x} after the replays")
         return 1
+    # decode workgroups that left the fp16 path for the exact fp32 one (0
+    # for these inputs; the timings above would not be of the fast path)
+    fallbacks = hs.decode_fallback_count()
 
     # the headline is the faster of the two timed modes, with the kernel
     # times recorded in that same mode
@@ -420,6 +423,7 @@ def main() -> int:
                       "unit": unit, "frac": round(ach / peak, 4) if (peak and ach is not None) else None,
                       "busy_share_of_step": round(tot_ms / ms_total, 4)}
     if "sparse_mla_decode" in kern:
+        kern["sparse_mla_decode"]["fp32_fallback_workgroups"] = int(fallbacks)
         kern["sparse_mla_decode"]["in_step_note"] = (
             "in-step launches: every layer of an index-share group but the last is decoded without key splits "
             "on few CUs while the next layer's miss fetch streams; the group's last layer is split over the "

@@ -13,24 +13,31 @@
 // Work split: a workgroup handles (layer, request, group of up to 64 heads,
 // K split) with 12 wavefronts, three per SIMD, specialised by role:
 //  * score waves 0-3: wave w keeps the Q of heads 16w .. 16w+15 in
-//    registers and scores all 32 rows of each tile on 16x16x32 bf16 MFMA;
+//    registers and scores all 32 rows of each tile on 16x16x32 fp16 MFMA;
 //    it applies the softmax with a reference max per head and writes the
-//    probabilities P to LDS as two bf16 planes, P = P_hi + P_lo;
+//    probabilities P to LDS;
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
 //    every head of the group (fp32 accumulators in registers); it multiplies
-//    the transposed tile (read with ds_read_b64_tr_b16) by P_hi and by P_lo,
-//    one tile read feeding both MFMAs of two 16-head blocks;
-//  * loader waves 8-11: gather the row tiles through registers, two tiles
-//    ahead, and write them to LDS.
+//    the transposed tile (read with ds_read_b64_tr_b16) by P;
+//  * loader waves 8-11: gather the row tiles through registers, three tiles
+//    ahead, convert them to fp16 and write them to LDS.
 // The value waves run one tile behind the score waves and the loaders one
 // tile ahead, so each tile costs a single workgroup barrier, and no compute
 // wave waits on a global load or an LDS store.  Split partials are merged by
 // a second kernel.
 //
-// Precision: a single bf16 P carries a relative rounding error up to 2^-8
-// per weight, which for near-uniform softmax weights shows up in O at the
-// 1e-3 level.  The hi/lo pair represents P to about 2^-16, so O keeps the
-// accuracy of fp32 accumulation over exact bf16 inputs.
+// Precision.  Rows and Q are converted from bf16 to fp16, which is exact for
+// magnitudes in [2^-14, 2^16); smaller ones become fp16 subnormals (absolute
+// error below 2^-25).  The scores are therefore those of the bf16 inputs
+// with fp32 accumulation.  P is one fp16 plane: 11 significant bits, a
+// relative rounding error of at most 2^-11 per weight, while O and lse are
+// normalised by the sum of the unrounded fp32 weights.  (A single bf16
+// plane, 8 bits, gave O errors above 2e-3 of max|O| for near-uniform
+// weights.)  A value of magnitude 2^16 or more (or inf, NaN) becomes inf in
+// fp16 and makes every score of its row or head non-finite; the score waves
+// detect that, and the workgroup then computes its result again in plain
+// fp32 arithmetic on the values as given (exact_fallback), a slow path for
+// inputs that KV caches do not hold.  FP8 rows always fit fp16.
 #include "internal.h"
 
 #include <cmath>
@@ -47,25 +54,32 @@ constexpr int kPitch = kPitchChunks * 16;
 constexpr int kTileBytes = kT * kPitch;       // 37888
 constexpr int kNBuf = 3;                      // tiles in LDS: scored, multiplied, being stored
 constexpr int kThreads = 768;                 // 12 wavefronts: 4 score, 4 value, 4 loader
-constexpr int kPPitch = kT + 8;               // bf16 per P row (80 bytes)
-constexpr float kMaxGrowLog2 = 64.f;          // P = 2^(s - m) may reach 2^64 before a second pass
+constexpr int kPPitch = kT + 8;               // fp16 per P row (80 bytes)
+constexpr float kMaxGrowLog2 = 15.f;          // P = 2^(s - m) <= 2^15 stays finite in fp16
+constexpr int kMaxPasses = 2;
 constexpr int kStage = kRowChunks / 8;        // 9 chunks per loading thread per tile
 static_assert(kT * 8 == 256 && kRowChunks % 8 == 0, "8 loader threads per row, 256 loaders per tile");
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) u32x4 gu32x4;
 typedef const __attribute__((address_space(1))) u32x2 gu32x2;
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return a | (b << 16);
+// Two fp32 values -> their fp16 pair, rounded to nearest even (overflow
+// gives +-inf).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// A bf16 pair -> the fp16 pair of the same values.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
+  return pack_f16(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* rows, int k, int k1) {
@@ -79,8 +93,8 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
 }
 
 // Tile loads go through VGPRs: each loader thread fetches its part of a
-// tile with ordinary global loads two tiles ahead and writes it to LDS one
-// tile ahead of the score waves.  On MI355X this sustains ~7.3 TB/s for a
+// tile with ordinary global loads three tiles ahead and writes it to LDS
+// one tile ahead of the score waves.  On MI355X this sustains ~7.3 TB/s for a
 // random 1152-byte row gather, where direct-to-LDS loads stayed under
 // 3 TB/s.  The loads use global-address-space pointers: flat loads would
 // also count against the LDS wait counter and be drained by every
@@ -89,9 +103,9 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
 // row): eight threads cover contiguous bytes of a row per k, and every
 // address is one base plus an immediate.
 //
-// The LDS tile is always bf16.  FP8 E4M3 rows are widened while staging:
-// every E4M3 value (at most 4 significant bits, exponent within bf16's
-// range) converts to fp32 and then to bf16 exactly; the layer's scale is
+// The LDS tile is fp16.  FP8 E4M3 rows are widened while staging: every
+// E4M3 value (at most 4 significant bits, magnitude at most 448, smallest
+// 2^-9) converts to fp32 and then to fp16 exactly; the layer's scale is
 // applied to the scores and to O instead.
 template <bool FP8>
 struct TileStage;
@@ -108,14 +122,13 @@ struct TileStage<false> {
   __device__ __forceinline__ void store(unsigned char* xs, int t) const {
     u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
 #pragma unroll
-    for (int k = 0; k < kStage; ++k) dst[8 * k] = v[k];
+    for (int k = 0; k < kStage; ++k) {
+      const u32x4 w = {bf16x2_to_f16x2(v[k][0]), bf16x2_to_f16x2(v[k][1]), bf16x2_to_f16x2(v[k][2]),
+                       bf16x2_to_f16x2(v[k][3])};
+      dst[8 * k] = w;
+    }
   }
 };
-
-// Two fp32 values that are exact in bf16 -> their bf16 pair (upper halves).
-__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
 
 template <>
 struct TileStage<true> {
@@ -134,8 +147,8 @@ struct TileStage<true> {
       const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][0], true);
       const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], false);
       const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], true);
-      const u32x4 w = {bf16_pair_exact(a0[0], a0[1]), bf16_pair_exact(a1[0], a1[1]), bf16_pair_exact(b0[0], b0[1]),
-                       bf16_pair_exact(b1[0], b1[1])};
+      const u32x4 w = {pack_f16(a0[0], a0[1]), pack_f16(a1[0], a1[1]), pack_f16(b0[0], b0[1]),
+                       pack_f16(b1[0], b1[1])};
       dst[8 * k] = w;
     }
   }
@@ -146,10 +159,10 @@ struct TileStage<true> {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // All MFMAs are written as inline asm with every operand in VGPRs (the
-// kernel uses no AGPRs, so both roles may use up to 256 VGPRs at two waves
-// per SIMD); with the builtin the register allocator moves accumulators
-// between register files around the MFMAs.  The compiler does not see
-// these as MFMAs, so the hazards they can meet are covered by hand:
+// kernel uses no AGPRs, so every role may use all of a wave's 168 VGPRs at
+// three waves per SIMD); with the builtin the register allocator moves
+// accumulators between register files around the MFMAs.  The compiler does
+// not see these as MFMAs, so the hazards they can meet are covered by hand:
 //  * an operand written by a VALU instruction just before: two wait states
 //    in front of the first MFMA that reads a freshly assembled operand;
 //  * reading results afterwards: score_drain() and acc_drain() insert wait
@@ -159,22 +172,22 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 //    access could meet an MFMA still writing them.
 // Back-to-back MFMAs that chain through srcC need no wait states.
 __device__ __forceinline__ void mfma_acc(f32x4& d, const u32x4& a, const u32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_acc_after_valu(f32x4& d, const u32x4& a, const u32x4& b) {
-  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void zero_acc(f32x4& d) {
   const u32x4 z = {0u, 0u, 0u, 0u};
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=&v"(d) : "v"(z));
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %1, 0" : "=&v"(d) : "v"(z));
 }
 // Score MFMAs: A (tile rows) and B (Q) in VGPRs; the first k-step starts
 // from srcC = 0.
 __device__ __forceinline__ void mfma_score_first(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_score(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 // The drains name the registers they protect as read-write operands of the
 // wait-state asm itself, so the MFMAs writing them stay above it and no
@@ -201,27 +214,117 @@ __device__ __forceinline__ void acc_drain(f32x4 (&acc)[N]) {
 template <int HG>
 struct DecodeSmem {
   unsigned char xs[kNBuf][kTileBytes];  // row tiles: scored, multiplied, being stored
-  uint16_t ps[2][2][HG][kPPitch];       // [tile parity][hi, lo][head][row]
+  uint16_t ps[2][HG][kPPitch];          // P by tile parity: [head][row], fp16
   int rowid[kMaxTopK];                  // row ids of the workgroup's K range
   float lexact[HG], mfin[HG];           // weight sum and reference max per head
-  int overflow;
+  int overflow[kMaxPasses];             // a tile exceeded the reference max
+  int nonfinite;                        // a score was inf or NaN: exact_fallback takes over
 };
+
+// Passes over the K range: the first uses the reference max of the first
+// tile with a valid row; if a later tile exceeds it by more than 2^15 (the
+// range of an fp16 weight), the range is recomputed once with the true
+// maximum of every head, which no tile can exceed.  Read by every role after
+// the same barrier, so all take the same branch.
+template <int HG>
+__device__ __forceinline__ bool again(const DecodeSmem<HG>& sm, int p) {
+  return p + 1 < kMaxPasses && sm.overflow[p] && !sm.nonfinite;
+}
+
+// One pass of a score wave over the tiles (see score_role).
+template <int HG>
+__device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)[kLatent / 32], float score_scale,
+                                            int n_tiles, int p, int w, int g, int i16, float& m_run, float& m_seen,
+                                            float& l_exact) {
+  const bool active = 16 * w < HG;
+  for (int it = 0; it <= n_tiles; ++it) {
+    if (active && it < n_tiles) {
+      const unsigned char* xb = sm.xs[it % kNBuf];
+      f32x4 sacc[2];
+      // A operands: lane (g, i16) reads rows i16 and 16 + i16, dims 32 s + 8 g .. +7.
+      const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
+#pragma unroll
+      for (int s = 0; s < kLatent / 32; ++s) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
+        if (s == 0) {
+          mfma_score_first(sacc[0], a0, q[0]);
+          mfma_score_first(sacc[1], a1, q[0]);
+        } else {
+          mfma_score(sacc[0], a0, q[s]);
+          mfma_score(sacc[1], a1, q[s]);
+        }
+        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
+      }
+      score_drain(sacc);
+      // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
+      bool valid[2][4];
+      bool finite = true;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int4 rid = *reinterpret_cast<const int4*>(sm.rowid + it * kT + 16 * rb + 4 * g);
+        valid[rb][0] = rid.x >= 0;
+        valid[rb][1] = rid.y >= 0;
+        valid[rb][2] = rid.z >= 0;
+        valid[rb][3] = rid.w >= 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          // Every staged row counts, the filler rows of padding entries too:
+          // their zero weights must not meet an inf in the PV product.
+          finite = finite && __builtin_fabsf(sacc[rb][v]) <= 3.0e38f;
+          sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * score_scale : -INFINITY;
+          mx = fmaxf(mx, sacc[rb][v]);
+        }
+      }
+      if (!finite) sm.nonfinite = 1;  // the fp16 result is discarded
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_seen = fmaxf(m_seen, mx);
+      if (m_run == -INFINITY)
+        m_run = mx;  // first tile with a valid row (stays -inf while none is)
+      else if (mx > m_run + kMaxGrowLog2)
+        sm.overflow[p] = 1;  // this pass is discarded
+      const int head = 16 * w + i16;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float pr[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pr[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
+        l_exact += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const u32x2 pw = {pack_f16(pr[0], pr[1]), pack_f16(pr[2], pr[3])};
+        *reinterpret_cast<u32x2*>(&sm.ps[it & 1][head][16 * rb + 4 * g]) = pw;
+      }
+    }
+    lds_barrier();
+  }
+}
 
 // Score waves 0-3: wave w scores all 32 rows of each tile against heads
 // 16w .. 16w+15 (waves past the group's heads idle through the barriers).
 // The A operand (16 rows x 32 dims) comes from LDS, the B operand (Q) from
 // registers, and the two 16-row blocks of a tile give two accumulators, so
 // each wave sees every row of its heads and needs no exchange with another.
+//
+// Softmax with a fixed reference max per head: the first tile with a valid
+// row sets m, and P = 2^(s*scale*log2e - m) accumulates unnormalised, so
+// the O accumulators are never rescaled inside the loop.  Both passes give
+// the exact softmax.
 template <int HG, bool FP8>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
                                            int n_tiles, int w, int g, int i16) {
   const bool active = 16 * w < HG;
-  // Q as MFMA B operands: lane (g, i16) holds dims 32 s + 8 g .. +7 of head 16 w + i16.
+  // Q as MFMA B operands: lane (g, i16) holds dims 32 s + 8 g .. +7 of
+  // head 16 w + i16, in fp16.
   f32x4 q[kLatent / 32];
   if (active) {
     gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * w + i16) * kLatent + 8 * g);
 #pragma unroll
-    for (int s = 0; s < kLatent / 32; ++s) q[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
+    for (int s = 0; s < kLatent / 32; ++s) {
+      const u32x4 u = qp[4 * s];
+      const u32x4 h = {bf16x2_to_f16x2(u[0]), bf16x2_to_f16x2(u[1]), bf16x2_to_f16x2(u[2]), bf16x2_to_f16x2(u[3])};
+      q[s] = __builtin_bit_cast(f32x4, h);
+    }
 #pragma unroll
     for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[s]), "+v"(q[s + 1]));
   }
@@ -230,79 +333,11 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
   // m_run: reference max of this lane's head; m_seen: the largest score
   // seen; l_exact: sum of the unrounded weights.
   float m_run = -INFINITY, m_seen = -INFINITY, l_exact = 0.f;
-
-  // Softmax with a fixed reference max per head: the first tile with a
-  // valid row sets m, and P = 2^(s*scale*log2e - m) accumulates
-  // unnormalised, so the O accumulators are never rescaled inside the loop.
-  // If a later tile exceeds m by more than 2^64 (never for ordinary scores),
-  // the whole range is recomputed once with m = the true maximum, which no
-  // tile can exceed.  Both passes give the exact softmax.
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int p = 0; p < kMaxPasses; ++p) {
     l_exact = 0.f;
     lds_barrier();  // tile 0 is in LDS
-    for (int it = 0; it <= n_tiles; ++it) {
-      if (active && it < n_tiles) {
-        const unsigned char* xb = sm.xs[it % kNBuf];
-        f32x4 sacc[2];
-        // A operands: lane (g, i16) reads rows i16 and 16 + i16, dims 32 s + 8 g .. +7.
-        const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
-#pragma unroll
-        for (int s = 0; s < kLatent / 32; ++s) {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
-          if (s == 0) {
-            mfma_score_first(sacc[0], a0, q[0]);
-            mfma_score_first(sacc[1], a1, q[0]);
-          } else {
-            mfma_score(sacc[0], a0, q[s]);
-            mfma_score(sacc[1], a1, q[s]);
-          }
-          if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
-        }
-        score_drain(sacc);
-        // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
-        bool valid[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int4 rid = *reinterpret_cast<const int4*>(sm.rowid + it * kT + 16 * rb + 4 * g);
-          valid[rb][0] = rid.x >= 0;
-          valid[rb][1] = rid.y >= 0;
-          valid[rb][2] = rid.z >= 0;
-          valid[rb][3] = rid.w >= 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            sacc[rb][v] = valid[rb][v] ? sacc[rb][v] * score_scale : -INFINITY;
-            mx = fmaxf(mx, sacc[rb][v]);
-          }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        m_seen = fmaxf(m_seen, mx);
-        if (m_run == -INFINITY)
-          m_run = mx;  // first tile with a valid row (stays -inf while none is)
-        else if (mx > m_run + kMaxGrowLog2)
-          sm.overflow = 1;  // this pass is discarded
-        const int head = 16 * w + i16;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float p[4], r[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) p[v] = valid[rb][v] ? __builtin_amdgcn_exp2f(sacc[rb][v] - m_run) : 0.f;
-          l_exact += (p[0] + p[1]) + (p[2] + p[3]);
-          const u32x2 hi = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-          const float h[4] = {__uint_as_float(hi[0] << 16), __uint_as_float(hi[0] & 0xFFFF0000u),
-                              __uint_as_float(hi[1] << 16), __uint_as_float(hi[1] & 0xFFFF0000u)};
-#pragma unroll
-          for (int v = 0; v < 4; ++v) r[v] = p[v] - h[v];  // exact in fp32
-          const u32x2 lo = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-          *reinterpret_cast<u32x2*>(&sm.ps[it & 1][0][head][16 * rb + 4 * g]) = hi;
-          *reinterpret_cast<u32x2*>(&sm.ps[it & 1][1][head][16 * rb + 4 * g]) = lo;
-        }
-      }
-      lds_barrier();
-    }
-    if (!sm.overflow) break;
+    score_tiles<HG>(sm, q, score_scale, n_tiles, p, w, g, i16, m_run, m_seen, l_exact);
+    if (!again(sm, p)) break;
     m_run = m_seen;  // recompute with the true maximum of the head
     lds_barrier();
   }
@@ -320,138 +355,250 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
   __syncthreads();
 }
 
+// Where the output of head h of the group goes, from column c0 on: the O
+// row (scaled by kvs / l) or a split partial for combine_splits (scaled by
+// kvs, with m and l beside it).  The writer also stores lse or (m, l).
+struct OutSlot {
+  float scale;  // 0 when the head has no valid row
+  float* dst;
+};
+template <int HG>
+__device__ __forceinline__ OutSlot out_slot(const DecodeArgs& a, const DecodeSmem<HG>& sm, float kvs, size_t head0,
+                                            int pair, int split, int hg, int h, int c0, bool writer) {
+  // O and lse are normalised by the sum of the unrounded weights.
+  const float lsum = sm.lexact[h];
+  const float m = sm.mfin[h];
+  if (a.splits == 1) {
+    if (writer)
+      a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
+    return {lsum > 0.f ? kvs / lsum : 0.f, a.out + (head0 + h) * kVDim + c0};
+  }
+  float* part = a.partial + (((size_t)pair * a.splits + split) * a.num_heads + hg * HG + h) * kPartW;
+  if (writer) {
+    part[kVDim] = m;
+    part[kVDim + 1] = lsum;
+    part[kVDim + 2] = lsum;
+  }
+  return {kvs, part + c0};
+}
+
+// One pass of a value wave over the tiles (see value_role).  The P
+// operands of all head blocks are in registers, so the tile's columns are
+// read once per tile.
+template <int HG>
+__device__ __forceinline__ void value_tiles(DecodeSmem<HG>& sm, f32x4 (&acc)[HG / 2], int n_tiles, int cw, int g,
+                                            int i16) {
+  constexpr int NBP = HG / 16;  // 16-head blocks
+  for (int it = 0; it <= n_tiles; ++it) {
+    if (it >= 1) {
+      const int tp = it - 1;
+      const unsigned char* xb = sm.xs[tp % kNBuf];
+      // B operands: P of rows 8 g .. 8 g + 7, head 16 nb + i16.
+      u32x4 bp[NBP];
+#pragma unroll
+      for (int nb = 0; nb < NBP; ++nb) bp[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][16 * nb + i16][8 * g]);
+      // A operand (X^T, 16 cols x 32 rows) by two transposed reads: lane
+      // (g, i16) addresses row 8 g + i16 / 4 (+4), columns 128 cw + 16 mb +
+      // 4 (i16 % 4) .. +3, and receives column 128 cw + 16 mb + i16 of rows
+      // 8 g .. 8 g + 7.
+      uint32_t xoff = (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
+      asm volatile("" : "+v"(xoff));
+      const lds_u8* xl = (const lds_u8*)xb + xoff;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const s16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
+        const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        mfma_acc_after_valu(acc[mb * NBP], av, bp[0]);
+#pragma unroll
+        for (int nb = 1; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bp[nb]);
+        if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    lds_barrier();
+  }
+}
+
 // Value waves 4-7: wave 4+cw owns output columns 128cw .. 128cw+127 of every
 // head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
+// Writes nothing when the fp16 result is discarded.
 template <int HG, bool FP8>
 __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
                                            int pair, int split, int hg, int n_tiles, int cw, int g, int i16) {
-  constexpr int NBP = HG / 16;             // 16-head blocks
-  constexpr int NBH = NBP > 2 ? 2 : NBP;   // head blocks per sweep over the tile (P operands in registers)
+  constexpr int NBP = HG / 16;  // 16-head blocks
   // acc[mb * NBP + nb]: columns 128 cw + 16 mb + 4 g + v, head 16 nb + i16
   f32x4 acc[8 * NBP];
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int p = 0; p < kMaxPasses; ++p) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NBP; ++nb) zero_acc(acc[mb * NBP + nb]);
     lds_barrier();
-    for (int it = 0; it <= n_tiles; ++it) {
-      if (it >= 1) {
-        const int tp = it - 1;
-        const unsigned char* xb = sm.xs[tp % kNBuf];
-        // A operand (X^T, 16 cols x 32 rows) by two transposed reads: lane
-        // (g, i16) addresses row 8 g + i16 / 4 (+4), columns 128 cw + 16 mb +
-        // 4 (i16 % 4) .. +3, and receives column 128 cw + 16 mb + i16 of rows
-        // 8 g .. 8 g + 7.
-        uint32_t xoff = (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
-        asm volatile("" : "+v"(xoff));
-        const lds_u8* xl = (const lds_u8*)xb + xoff;
-#pragma unroll
-        for (int h0 = 0; h0 < NBP; h0 += NBH) {
-          // B operands: P_hi and P_lo of rows 8 g .. 8 g + 7, head 16 (h0 + nb) + i16.
-          u32x4 bp[NBH], bq[NBH];
-#pragma unroll
-          for (int nb = 0; nb < NBH; ++nb) {
-            bp[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][0][16 * (h0 + nb) + i16][8 * g]);
-            bq[nb] = *reinterpret_cast<const u32x4*>(&sm.ps[tp & 1][1][16 * (h0 + nb) + i16][8 * g]);
-          }
-#pragma unroll
-          for (int mb = 0; mb < 8; ++mb) {
-            const s16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
-            const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            mfma_acc_after_valu(acc[mb * NBP + h0], av, bp[0]);
-#pragma unroll
-            for (int nb = 1; nb < NBH; ++nb) mfma_acc(acc[mb * NBP + h0 + nb], av, bp[nb]);
-#pragma unroll
-            for (int nb = 0; nb < NBH; ++nb) mfma_acc(acc[mb * NBP + h0 + nb], av, bq[nb]);
-            if (mb & 1) __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      lds_barrier();
-    }
-    if (!sm.overflow) break;
+    value_tiles<HG>(sm, acc, n_tiles, cw, g, i16);
+    if (!again(sm, p)) break;
     lds_barrier();
   }
   __syncthreads();  // the score waves' normalisers are in LDS
+  if (sm.nonfinite) return;
 
   acc_drain(acc);
-  const int H = a.num_heads;
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
-    const int h = nb * 16 + i16;
-    // O is normalised by the sum of the unrounded weights; P_hi + P_lo
-    // carries each weight to about 2^-17 relative, far inside the tolerance.
-    const float lsum = sm.lexact[h];
-    const float m = sm.mfin[h];
-    if (a.splits == 1) {
-      const float inv = lsum > 0.f ? kvs / lsum : 0.f;
-      float* out = a.out + (head0 + h) * kVDim + 128 * cw + 4 * g;
+    const OutSlot o =
+        out_slot(a, sm, kvs, head0, pair, split, hg, nb * 16 + i16, 128 * cw + 4 * g, cw == 0 && g == 0);
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        *reinterpret_cast<f32x4*>(out + 16 * mb) = acc[mb * NBP + nb] * inv;
-        __builtin_amdgcn_sched_barrier(0);  // few accumulators in VGPRs at a time
-      }
-      if (cw == 0 && g == 0)
-        a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
-    } else {
-      float* part = a.partial + (((size_t)pair * a.splits + split) * H + hg * HG + h) * kPartW;
-      float* po = part + 128 * cw + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) po[16 * mb + v] = acc[mb * NBP + nb][v] * kvs;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (cw == 0 && g == 0) {
-        part[kVDim] = m;
-        part[kVDim + 1] = lsum;
-        part[kVDim + 2] = lsum;
-      }
+    for (int mb = 0; mb < 8; ++mb) {
+      *reinterpret_cast<f32x4*>(o.dst + 16 * mb) = acc[mb * NBP + nb] * o.scale;
+      __builtin_amdgcn_sched_barrier(0);  // few accumulators in VGPRs at a time
     }
   }
 }
 
-// Loader waves 8-11: tile n is held in registers set n % 2 from two
-// iterations before it is needed.  Iteration it writes tile it+1 to its LDS
-// slot (last read in iteration it-2) and starts the load of tile it+3 into
-// the registers just freed, so two tiles' loads are in flight while the
-// compute waves work on tiles it and it-1.
+// Loader waves 8-11: tile n is held in register set n % kLoadSets from
+// kLoadSets iterations before it is needed.  Iteration it writes tile it+1
+// to its LDS slot (last read in iteration it-2) and starts the load of tile
+// it+1+kLoadSets into the registers just freed, so three tiles' loads are in
+// flight while the compute waves work on tiles it and it-1 (two sets left
+// the gather waiting on HBM latency: 119 us instead of 102 us for one
+// launch over 4 layers of 32 requests; four sets gained nothing more).
+constexpr int kLoadSets = 3;
+
 template <int HG, bool FP8>
 __device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned char* kv, int n_tiles, int lt) {
-  TileStage<FP8> s0, s1;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (n_tiles > 0) s0.load(kv, sm.rowid, lt);
-    if (n_tiles > 1) s1.load(kv, sm.rowid + kT, lt);
+  TileStage<FP8> st[kLoadSets];
+  for (int p = 0; p < kMaxPasses; ++p) {
+#pragma unroll
+    for (int j = 0; j < kLoadSets; ++j)
+      if (j < n_tiles) st[j].load(kv, sm.rowid + j * kT, lt);
     if (n_tiles > 0) {
-      s0.store(sm.xs[0], lt);
-      if (n_tiles > 2) s0.load(kv, sm.rowid + 2 * kT, lt);
+      st[0].store(sm.xs[0], lt);
+      if (kLoadSets < n_tiles) st[0].load(kv, sm.rowid + kLoadSets * kT, lt);
     }
     lds_barrier();
     for (int it = 0; it <= n_tiles; ++it) {
       const int nx = it + 1;
       if (nx < n_tiles) {
-        if (nx & 1) {
-          s1.store(sm.xs[nx % kNBuf], lt);
-          if (nx + 2 < n_tiles) s1.load(kv, sm.rowid + (nx + 2) * kT, lt);
-        } else {
-          s0.store(sm.xs[nx % kNBuf], lt);
-          if (nx + 2 < n_tiles) s0.load(kv, sm.rowid + (nx + 2) * kT, lt);
+        const int j = nx % kLoadSets;
+#pragma unroll
+        for (int jj = 0; jj < kLoadSets; ++jj) {  // register sets need constant indices
+          if (jj == j) {
+            st[jj].store(sm.xs[nx % kNBuf], lt);
+            if (nx + kLoadSets < n_tiles) st[jj].load(kv, sm.rowid + (nx + kLoadSets) * kT, lt);
+          }
         }
       }
       lds_barrier();
     }
-    if (!sm.overflow) break;
+    if (!again(sm, p)) break;
     lds_barrier();
   }
   __syncthreads();
 }
 
-// Every role passes the same barriers: one before the loop, one per
-// iteration (n_tiles + 1), one more before a second pass, and the final
+// The result of a workgroup whose fp16 pass met a value beyond fp16, in
+// plain fp32 arithmetic on the values as given: a first sweep over the
+// rows finds each head's maximum score, a second forms the weights and O.
+// Rows are staged 16 at a time as fp32 in the tile buffers (with Q as
+// bf16); thread t < 8 HG owns O of head t / 8, columns 64 (t % 8) .. +63.
+constexpr int kFbRows = 16;
+constexpr int kFbPitch = kLatent + 4;  // floats per staged row
+
+template <int HG, bool FP8>
+__device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
+                                               float kvs, size_t head0, int pair, int split, int hg, int n_rows,
+                                               int tid) {
+  static_assert(HG * kLatent * 2 + kFbRows * kFbPitch * 4 <= kNBuf * kTileBytes, "fallback staging fits the tiles");
+  static_assert(HG * kFbRows * 4 <= sizeof(DecodeSmem<HG>::ps), "fallback scores fit the P buffers");
+  uint32_t* qs = reinterpret_cast<uint32_t*>(&sm.xs[0][0]);              // [HG][288] bf16 pairs
+  float* xf = reinterpret_cast<float*>(&sm.xs[0][0] + HG * kLatent * 2);  // [16][kFbPitch]
+  float* sp = reinterpret_cast<float*>(&sm.ps[0][0][0]);                   // [HG][16]
+  const float score_scale = a.scale_log2 * kvs;
+  __syncthreads();  // every role is done with the tile buffers
+  const uint32_t* qg = reinterpret_cast<const uint32_t*>(a.q + head0 * kLatent);
+  for (int i = tid; i < HG * kLatent / 2; i += kThreads) qs[i] = qg[i];
+  const int oh = tid >> 3, oc = (tid & 7) * 64;
+  const bool owner = tid < 8 * HG;
+  float acc[64];
+#pragma unroll
+  for (int c = 0; c < 64; ++c) acc[c] = 0.f;
+  float m = -INFINITY, l = 0.f;  // of head tid, in threads tid < HG
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c0 = 0; c0 < n_rows; c0 += kFbRows) {
+      __syncthreads();  // the previous chunk is consumed
+      for (int i = tid; i < kFbRows * kLatent / 2; i += kThreads) {
+        const int j = i / (kLatent / 2), d2 = i % (kLatent / 2);
+        const int rid = c0 + j < n_rows ? sm.rowid[c0 + j] : -1;
+        float x0 = 0.f, x1 = 0.f;
+        if (rid >= 0) {
+          if constexpr (FP8) {
+            const uint32_t w = *reinterpret_cast<const uint16_t*>(kv + (size_t)rid * kRowBytesFp8 + 2 * d2);
+            const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            x0 = v[0];
+            x1 = v[1];
+          } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(kv + (size_t)rid * kRowBytes + 4 * d2);
+            x0 = __uint_as_float(w << 16);
+            x1 = __uint_as_float(w & 0xFFFF0000u);
+          }
+        }
+        xf[j * kFbPitch + 2 * d2] = x0;
+        xf[j * kFbPitch + 2 * d2 + 1] = x1;
+      }
+      __syncthreads();
+      for (int pr = tid; pr < HG * kFbRows; pr += kThreads) {
+        const int h = pr / kFbRows, j = pr % kFbRows;
+        const bool valid = c0 + j < n_rows && sm.rowid[c0 + j] >= 0;
+        const uint32_t* qh = qs + h * (kLatent / 2);
+        const float* xj = xf + j * kFbPitch;
+        float dot = 0.f;
+        for (int d2 = 0; d2 < kLatent / 2; ++d2) {
+          const uint32_t w = qh[d2];
+          dot = fmaf(__uint_as_float(w << 16), xj[2 * d2], dot);
+          dot = fmaf(__uint_as_float(w & 0xFFFF0000u), xj[2 * d2 + 1], dot);
+        }
+        sp[h * kFbRows + j] = valid ? dot * score_scale : -INFINITY;
+      }
+      __syncthreads();
+      if (tid < HG) {
+        for (int j = 0; j < kFbRows; ++j) {
+          const float s = sp[tid * kFbRows + j];
+          if (pass == 0) {
+            m = fmaxf(m, s);
+          } else {
+            const float pw = s == -INFINITY ? 0.f : exp2f(s - m);
+            sp[tid * kFbRows + j] = pw;
+            l += pw;
+          }
+        }
+      }
+      if (pass == 1) {
+        __syncthreads();
+        if (owner) {
+          for (int j = 0; j < kFbRows; ++j) {
+            const float pw = sp[oh * kFbRows + j];
+            const float* xj = xf + j * kFbPitch + oc;
+#pragma unroll
+            for (int c = 0; c < 64; ++c) acc[c] = fmaf(pw, xj[c], acc[c]);
+          }
+        }
+      }
+    }
+  }
+  if (tid < HG) {
+    sm.lexact[tid] = l;
+    sm.mfin[tid] = m;
+  }
+  __syncthreads();
+  if (!owner) return;
+  const OutSlot o = out_slot(a, sm, kvs, head0, pair, split, hg, oh, oc, (tid & 7) == 0);
+#pragma unroll
+  for (int c = 0; c < 64; ++c) o.dst[c] = acc[c] * o.scale;
+}
+
+// Every role passes the same barriers: per pass one before the loop and one
+// per iteration (n_tiles + 1), one between passes, and the final
 // __syncthreads().
 template <int HG, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
@@ -481,7 +628,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
 
   // Row ids of the whole K range, validated once.
-  if (tid == 0) sm.overflow = 0;
+  if (tid < kMaxPasses) sm.overflow[tid] = 0;
+  if (tid == 0) sm.nonfinite = 0;
   for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
   __syncthreads();
 
@@ -492,6 +640,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
     value_role<HG, FP8>(a, sm, kvs, head0, pair, split, hg, n_tiles, w - 4, g, i16);
   else
     loader_role<HG, FP8>(sm, kv, n_tiles, tid - 512);
+  // nonfinite is final after every role's last barrier.
+  if (sm.nonfinite) {
+    exact_fallback<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, k1 > k0 ? k1 - k0 : 0, tid);
+    if (tid == 0) atomicAdd(a.fallback_count, 1u);
+  }
 }
 
 // Merge the split partials of one (layer, request, head) per wavefront.

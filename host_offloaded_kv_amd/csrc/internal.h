@@ -122,6 +122,7 @@ struct DecodeArgs {
   float* out;              // [n_layers][R][H][512]
   float* lse;              // [n_layers][R][H]
   float* partial;          // [n_layers][R][splits][H][kPartW] when splits > 1
+  uint32_t* fallback_count;  // workgroups that took the exact fp32 path (read and cleared by the host)
   uint32_t* err;
   int32_t layer_begin;
   int32_t n_layers;
@@ -137,7 +138,7 @@ struct DecodeArgs {
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
   size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, cap, hv, host_rows, kv_ptrs, kv_scale,
-      err, partial, posmap, map_off, total;
+      err, fallback_count, partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
   int32_t splits_max;      // largest split count any decode launch uses
@@ -191,6 +192,7 @@ struct hisparse_pool {
   float* kv_scale_d;
   uint32_t* err;
   float* partial;
+  uint32_t* fallback_count;
   // Overlapped step: per-layer miss fetches run on fetch_stream (default
   // priority) while the caller's stream decodes earlier layers.
   hipStream_t fetch_stream = nullptr;

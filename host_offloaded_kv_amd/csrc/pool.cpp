@@ -147,6 +147,7 @@ Layout make_layout(const hisparse_config* c) {
   L.kv_ptrs = off; off = align256(off + NL * 8);
   L.kv_scale = off; off = align256(off + NL * 4);
   L.err = off; off = align256(off + 4);
+  L.fallback_count = off; off = align256(off + 4);
   L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
   int64_t ctx_sum = 0;
   for (size_t r = 0; r < R; ++r) ctx_sum += capacity_of(c, (int)r);
@@ -347,6 +348,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->kv_scale_d = (float*)(w + lay.kv_scale);
   p->err = (uint32_t*)(w + lay.err);
   p->partial = (float*)(w + lay.partial);
+  p->fallback_count = (uint32_t*)(w + lay.fallback_count);
   p->posmap = (int16_t*)(w + lay.posmap);
   p->map_off = (int64_t*)(w + lay.map_off);
 
@@ -528,6 +530,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.out = d_out;
   a.lse = d_lse;
   a.partial = p->partial;
+  a.fallback_count = p->fallback_count;
   a.err = p->err;
   a.layer_begin = layer_begin;
   a.n_layers = n_layers;
@@ -844,6 +847,22 @@ hisparse_status hisparse_check_errors(hisparse_pool* p, void* stream, uint32_t* 
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hisparse_check_errors");
   *flags = v;
+  return HISPARSE_OK;
+}
+
+hisparse_status hisparse_decode_fallback_count(hisparse_pool* p, void* stream, int64_t* count) {
+  if (!p || !count) {
+    set_error("hisparse_decode_fallback_count: bad argument");
+    return HISPARSE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, p->fallback_count, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemsetAsync(p->fallback_count, 0, 4, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hisparse_decode_fallback_count");
+  *count = v;
   return HISPARSE_OK;
 }
 

@@ -610,6 +610,7 @@ hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
   hipError_t e;
   if ((e = hipMemsetAsync(p->bt, 0xFF, p->lay.bt_entries * 4, s)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(p->err, 0, 4, s)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(p->fallback_count, 0, 4, s)) != hipSuccess) return e;
   return launch_state_reset(p, s);
 }
 

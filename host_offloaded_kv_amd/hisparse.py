@@ -57,7 +57,7 @@ EXPORTED = (
     "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
     "hisparse_set_replacement",
-    "hisparse_export_state", "hisparse_check_errors",
+    "hisparse_export_state", "hisparse_check_errors", "hisparse_decode_fallback_count",
     "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
     "hisparse_profile_enable", "hisparse_profile_read",
 )
@@ -129,6 +129,7 @@ def load() -> ctypes.CDLL:
         "hisparse_get_lengths": (_I32, [_VP, _VP, _VP, _VP]),
         "hisparse_export_state": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
         "hisparse_check_errors": (_I32, [_VP, _VP, ctypes.POINTER(ctypes.c_uint32)]),
+        "hisparse_decode_fallback_count": (_I32, [_VP, _VP, ctypes.POINTER(ctypes.c_int64)]),
         "hisparse_host_alloc": (_I32, [ctypes.c_size_t, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP)]),
         "hisparse_host_free": (None, [_VP]),
         "hisparse_stream_copy": (_I32, [_VP, _VP, ctypes.c_size_t, _VP]),
@@ -279,6 +280,12 @@ def hisparse_check_errors(pool: int, stream: int) -> int:
     return v.value
 
 
+def hisparse_decode_fallback_count(pool: int, stream: int) -> int:
+    v = ctypes.c_int64()
+    _check(load().hisparse_decode_fallback_count(pool, stream, ctypes.byref(v)))
+    return v.value
+
+
 def hisparse_host_alloc(nbytes: int, coherent: int = 0) -> tuple[int, int]:
     h, d = _VP(), _VP()
     _check(load().hisparse_host_alloc(nbytes, coherent, ctypes.byref(h), ctypes.byref(d)))
@@ -399,6 +406,9 @@ class HiSparse:
 
     def check_errors(self) -> int:
         return hisparse_check_errors(self.pool, self.stream)
+
+    def decode_fallback_count(self) -> int:
+        return hisparse_decode_fallback_count(self.pool, self.stream)
 
     def close(self) -> None:
         if getattr(self, "pool", None):

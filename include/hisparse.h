@@ -328,6 +328,17 @@ hisparse_status hisparse_export_state(hisparse_pool* pool, int32_t r, int32_t l,
  * Synchronises the stream. */
 hisparse_status hisparse_check_errors(hisparse_pool* pool, void* stream, uint32_t* flags);
 
+/* Read and clear the number of decode workgroups (one per layer, query
+ * set, head group and key split) that took the exact fp32 path since the
+ * last call or pool creation.  The decode computes in fp16 (exact for bf16
+ * values of magnitude below 2^16); a workgroup whose rows or queries hold a
+ * value of magnitude 2^16 or more, an inf or a NaN (any staged row counts,
+ * also the filler row of a -1 entry) computes its result again in fp32 on
+ * the values as given, which is correct but far slower.  A nonzero count
+ * thus flags inputs outside the fast path; results do not depend on it
+ * beyond rounding.  Synchronises the stream.  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_decode_fallback_count(hisparse_pool* pool, void* stream, int64_t* count);
+
 /* ---- measurement helpers (not on the decode path) ---- */
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
