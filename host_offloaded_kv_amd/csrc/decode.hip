@@ -41,6 +41,7 @@
 #include "internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace hs {
 namespace {
@@ -113,8 +114,7 @@ struct TileStage;
 template <>
 struct TileStage<false> {
   u32x4 v[kStage];
-  __device__ __forceinline__ void load(const unsigned char* kv, const int* rowid, int t) {
-    const int rid = rowid[t >> 3];
+  __device__ __forceinline__ void load_row(const unsigned char* kv, int rid, int t) {
     gu32x4* src = (gu32x4*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytes + (t & 7) * 16);
 #pragma unroll
     for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
@@ -133,8 +133,7 @@ struct TileStage<false> {
 template <>
 struct TileStage<true> {
   u32x2 v[kStage];
-  __device__ __forceinline__ void load(const unsigned char* kv, const int* rowid, int t) {
-    const int rid = rowid[t >> 3];
+  __device__ __forceinline__ void load_row(const unsigned char* kv, int rid, int t) {
     gu32x2* src = (gu32x2*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytesFp8 + (t & 7) * 8);
 #pragma unroll
     for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
@@ -237,24 +236,43 @@ __device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)
                                             int n_tiles, int p, int w, int g, int i16, float& m_run, float& m_seen,
                                             float& l_exact) {
   const bool active = 16 * w < HG;
+  constexpr int GS = 3;                 // k-steps per operand group
+  constexpr int NG = kLatent / 32 / GS;  // 6 groups
   for (int it = 0; it <= n_tiles; ++it) {
     if (active && it < n_tiles) {
       const unsigned char* xb = sm.xs[it % kNBuf];
       f32x4 sacc[2];
-      // A operands: lane (g, i16) reads rows i16 and 16 + i16, dims 32 s + 8 g .. +7.
+      // A operands: lane (g, i16) reads rows i16 and 16 + i16, dims 32 s + 8 g .. +7;
+      // the group after the one being multiplied is already loading.
       const unsigned char* xrow = xb + i16 * kPitch + 16 * g;
+      u32x4 A[2][GS][2];
 #pragma unroll
-      for (int s = 0; s < kLatent / 32; ++s) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
-        if (s == 0) {
-          mfma_score_first(sacc[0], a0, q[0]);
-          mfma_score_first(sacc[1], a1, q[0]);
-        } else {
-          mfma_score(sacc[0], a0, q[s]);
-          mfma_score(sacc[1], a1, q[s]);
+      for (int s = 0; s < GS; ++s) {
+        A[0][s][0] = *reinterpret_cast<const u32x4*>(xrow + 64 * s);
+        A[0][s][1] = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * s);
+      }
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) {
+#pragma unroll
+          for (int s = 0; s < GS; ++s) {
+            const int ks = GS * (gi + 1) + s;
+            A[(gi + 1) & 1][s][0] = *reinterpret_cast<const u32x4*>(xrow + 64 * ks);
+            A[(gi + 1) & 1][s][1] = *reinterpret_cast<const u32x4*>(xrow + 16 * kPitch + 64 * ks);
+          }
         }
-        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch (registers)
+#pragma unroll
+        for (int s = 0; s < GS; ++s) {
+          const int ks = GS * gi + s;
+          if (ks == 0) {
+            mfma_score_first(sacc[0], A[gi & 1][s][0], q[0]);
+            mfma_score_first(sacc[1], A[gi & 1][s][1], q[0]);
+          } else {
+            mfma_score(sacc[0], A[gi & 1][s][0], q[ks]);
+            mfma_score(sacc[1], A[gi & 1][s][1], q[ks]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       score_drain(sacc);
       // lane (g, i16): head 16 w + i16, rows 16 rb + 4 g + v
@@ -278,13 +296,15 @@ __device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)
         }
       }
       if (!finite) sm.nonfinite = 1;  // the fp16 result is discarded
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_seen = fmaxf(m_seen, mx);
-      if (m_run == -INFINITY)
-        m_run = mx;  // first tile with a valid row (stays -inf while none is)
-      else if (mx > m_run + kMaxGrowLog2)
+      m_seen = fmaxf(m_seen, mx);  // this lane's rows only; reduced when needed
+      if (__builtin_amdgcn_readfirstlane(m_run == -INFINITY ? 1 : 0)) {
+        // first tile with a valid row (the same tile for every head)
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_run = mx;
+      } else if (mx > m_run + kMaxGrowLog2) {
         sm.overflow[p] = 1;  // this pass is discarded
+      }
       const int head = 16 * w + i16;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -338,7 +358,10 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
     lds_barrier();  // tile 0 is in LDS
     score_tiles<HG>(sm, q, score_scale, n_tiles, p, w, g, i16, m_run, m_seen, l_exact);
     if (!again(sm, p)) break;
-    m_run = m_seen;  // recompute with the true maximum of the head
+    // recompute with the true maximum of the head over all its lanes' rows
+    m_seen = fmaxf(m_seen, __shfl_xor(m_seen, 16, 64));
+    m_seen = fmaxf(m_seen, __shfl_xor(m_seen, 32, 64));
+    m_run = m_seen;
     lds_barrier();
   }
 
@@ -463,34 +486,54 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
 // flight while the compute waves work on tiles it and it-1 (two sets left
 // the gather waiting on HBM latency: 119 us instead of 102 us for one
 // launch over 4 layers of 32 requests; four sets gained nothing more).
+// For the wait before a store to name exactly that set's loads, the set
+// index must be a constant and every path must issue the same loads: the
+// loop runs three iterations per trip, and tiles past the range load row 0.
 constexpr int kLoadSets = 3;
 
 template <int HG, bool FP8>
 __device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned char* kv, int n_tiles, int lt) {
+  static_assert(kLoadSets == 3, "the loop below is unrolled for three register sets");
   TileStage<FP8> st[kLoadSets];
+  const int row = lt >> 3;
+  const int n_ids = n_tiles * kT;
+  // Row id of tile n for this thread; tiles past the range stage row 0
+  // (their loads are issued anyway, so that every path has the same loads
+  // in flight and the wait before a store names exactly its set's loads).
+  auto rid_of = [&](int n) {
+    const int i = n * kT + row;
+    const int r = sm.rowid[i < n_ids ? i : 0];
+    return i < n_ids ? r : -1;
+  };
+  int it = 0, rid = -1;
+  // Iteration it stores tile it + 1 (from set (it + 1) % 3) and loads tile
+  // it + 4 into the same set; stores past the range land in a buffer
+  // nobody reads.
+  auto step = [&](auto u) {
+    constexpr int U = decltype(u)::value;
+    const int nx = it + U + 1;
+    st[(U + 1) % kLoadSets].store(sm.xs[nx % kNBuf], lt);
+    st[(U + 1) % kLoadSets].load_row(kv, rid, lt);
+    rid = rid_of(nx + kLoadSets + 1);
+    lds_barrier();
+  };
   for (int p = 0; p < kMaxPasses; ++p) {
 #pragma unroll
-    for (int j = 0; j < kLoadSets; ++j)
-      if (j < n_tiles) st[j].load(kv, sm.rowid + j * kT, lt);
-    if (n_tiles > 0) {
-      st[0].store(sm.xs[0], lt);
-      if (kLoadSets < n_tiles) st[0].load(kv, sm.rowid + kLoadSets * kT, lt);
-    }
+    for (int j = 0; j < kLoadSets; ++j) st[j].load_row(kv, rid_of(j), lt);
+    rid = rid_of(kLoadSets);
+    st[0].store(sm.xs[0], lt);
+    st[0].load_row(kv, rid, lt);
+    rid = rid_of(kLoadSets + 1);
     lds_barrier();
-    for (int it = 0; it <= n_tiles; ++it) {
-      const int nx = it + 1;
-      if (nx < n_tiles) {
-        const int j = nx % kLoadSets;
-#pragma unroll
-        for (int jj = 0; jj < kLoadSets; ++jj) {  // register sets need constant indices
-          if (jj == j) {
-            st[jj].store(sm.xs[nx % kNBuf], lt);
-            if (nx + kLoadSets < n_tiles) st[jj].load(kv, sm.rowid + (nx + kLoadSets) * kT, lt);
-          }
-        }
-      }
-      lds_barrier();
+    // iterations 0 .. n_tiles, three per trip so that each step's register
+    // set is a constant, then the remaining one or two
+    for (it = 0; it + kLoadSets <= n_tiles + 1; it += kLoadSets) {
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
     }
+    if (it <= n_tiles) step(std::integral_constant<int, 0>{});
+    if (it + 1 <= n_tiles) step(std::integral_constant<int, 1>{});
     if (!again(sm, p)) break;
     lds_barrier();
   }
