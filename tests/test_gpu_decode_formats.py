@@ -147,3 +147,44 @@ def test_late_tile_growth_takes_a_second_fp16_pass():
     assert s0[70] - s0[:32].max() > 20  # the case is what it claims
     log("decode formats: late tile growth")
     assert _run(R, H, K, n, rows, q, sel) == 0
+
+
+def test_fp8_rows_with_query_beyond_fp16_take_the_fallback():
+    """FP8 rows always fit fp16; a query value beyond it still sends the
+    workgroup to the fallback, which decodes the codes itself (times the
+    layer scale).  The count is read and cleared: a second read gives 0."""
+    import torch
+
+    from host_offloaded_kv_amd.hisparse import HiSparse
+    from oracle.attention import attend_f64, bf16_bits_to_f64
+    from oracle.fp8 import e4m3_to_f64
+    from tracegen.values import fp8_values
+
+    R, H, K, n, scale, kvs = 1, 64, 80, 160, 1 / 24.0, 0.25
+    e = np.arange(n * 576, dtype=np.uint64).reshape(n, 576)
+    codes = fp8_values(91, e, kvs)
+    q = q_block(26, 0, 0, 0, H)[None]
+    d = 9
+    codes[:, d] = 0  # code 0 is +0: the exact scores do not see the planted query value
+    q[0, 3, d] = _bits(70000.0)
+    sel = np.random.default_rng(26).permutation(n)[:K].astype(np.int32)[None]
+    cfg = dict(num_requests=R, num_layers=1, top_k=K, hot_slots=n, num_heads=H, ctx_len=[1],
+               kv_dtype="fp8", kv_scale=[kvs])
+    hs = HiSparse(cfg, "cuda:0")
+    dev = hs.device
+    hs.kv[0][:n] = torch.from_numpy(codes).to(dev)
+    out = torch.full((R, H, 512), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((R, H), float("nan"), dtype=torch.float32, device=dev)
+    log("decode formats: fp8 rows, query beyond fp16")
+    hs.decode(0, torch.from_numpy(q.view(np.int16)).to(dev), torch.from_numpy(sel).to(dev), scale, out, lse)
+    torch.cuda.synchronize()
+    assert hs.decode_fallback_count() >= 1
+    assert hs.decode_fallback_count() == 0
+    assert hs.check_errors() == 0
+    x = e4m3_to_f64(codes[sel[0]]) * kvs
+    o_ref, l_ref = attend_f64(bf16_bits_to_f64(q[0]), x, scale)
+    got_o, got_l = out.cpu().numpy()[0].astype(np.float64), lse.cpu().numpy()[0].astype(np.float64)
+    err = np.abs(got_o - o_ref).max() / np.abs(o_ref).max()
+    assert np.isfinite(err) and err <= O_TOL, f"O rel err {err:.3e}"
+    assert np.abs(got_l - l_ref).max() <= LSE_TOL
+    hs.close()
