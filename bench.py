@@ -151,7 +151,7 @@ def cpu_baseline(w, trace, budget_s=20.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    reqs = list(range(min(2, w.num_requests)))
+    reqs = list(range(min(6, w.num_requests)))  # about 10-20 s of oracle work on the machine's host
     dec = OracleDecoder(w, requests=reqs)
     t0 = time.time()
     steps = 0
