@@ -88,7 +88,7 @@ def _inputs(R, H, K, n_rows, seed):
     return rows, q, sel
 
 
-@pytest.mark.parametrize("H", [16, 64, 128])
+@pytest.mark.parametrize("H", [16, 48, 64, 96, 128])  # head groups of 16, 16 x 3, 64, 32 x 3, 64 x 2
 def test_in_range_inputs_stay_on_the_fast_path(H):
     R, K, n = 2, 100, 300
     rows, q, sel = _inputs(R, H, K, n, seed=21)
@@ -188,3 +188,15 @@ def test_fp8_rows_with_query_beyond_fp16_take_the_fallback():
     assert np.isfinite(err) and err <= O_TOL, f"O rel err {err:.3e}"
     assert np.abs(got_l - l_ref).max() <= LSE_TOL
     hs.close()
+
+
+def test_key_splits_with_empty_and_padded_ranges():
+    """One request, 64 heads, K = 300: the launch splits K over many
+    workgroups; whole splits hold only padding (-1) and the last tile is
+    ragged, so combine_splits meets empty partials."""
+    R, H, K, n = 1, 64, 300, 400
+    rows, q, sel = _inputs(R, H, K, n, seed=27)
+    sel[0][32:128] = -1   # three whole 32-row tiles of padding
+    sel[0][290:] = -1
+    log("decode formats: key splits with empty ranges")
+    assert _run(R, H, K, n, rows, q, sel) == 0
