@@ -762,10 +762,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) 
 
 int head_group(int num_heads) { return num_heads % 64 == 0 ? 64 : (num_heads % 32 == 0 ? 32 : 16); }
 
+// Key splits per (layer, query set, head group): enough workgroups to fill
+// the 256 CUs, but at least two tiles each, since a workgroup's fixed costs
+// (row ids, Q, the loader's first tiles, the partial write) outweigh a
+// single tile (1M-token, 1-request workload: 89 us per step instead of 95).
+constexpr int kMinTilesPerSplit = 2;
+
 int decode_splits(int n_layers, int num_requests, int num_heads, int top_k) {
   const int base = n_layers * num_requests * (num_heads / head_group(num_heads));
   int splits = (256 + base - 1) / base;
-  const int max_splits = (top_k + kT - 1) / kT;
+  const int max_splits = (top_k + kMinTilesPerSplit * kT - 1) / (kMinTilesPerSplit * kT);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   return splits;
