@@ -50,7 +50,8 @@ def log(msg: str) -> None:
 
 
 def host_link_probe(torch, H, dev, nbytes=256 << 20, reps=5):
-    """Measured host->device bandwidth: DMA copy and zero-copy kernel read."""
+    """Measured host->device bandwidth: DMA copy, zero-copy kernel read, and a
+    zero-copy gather of random whole rows (1152 and 576 bytes)."""
     stream = torch.cuda.current_stream(dev)
     host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     host.fill_(1)
@@ -75,6 +76,22 @@ def host_link_probe(torch, H, dev, nbytes=256 << 20, reps=5):
             e1.record(stream)
             torch.cuda.synchronize(dev)
             zc = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if not coherent:
+                # random whole rows, the miss fetch's access pattern (64 MiB per pass)
+                gen = torch.Generator(device=dev).manual_seed(12345)
+                for row_bytes in (1152, 576):
+                    n_rows = (64 << 20) // row_bytes
+                    rows = torch.randint(0, nbytes // row_bytes, (n_rows,), generator=gen, device=dev,
+                                         dtype=torch.int64)
+                    H.hisparse_row_gather(dst.data_ptr(), d, rows.data_ptr(), n_rows, row_bytes, stream.cuda_stream)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        H.hisparse_row_gather(dst.data_ptr(), d, rows.data_ptr(), n_rows, row_bytes,
+                                              stream.cuda_stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize(dev)
+                    out[f"random_{row_bytes}B_row_gather_GBs"] = round(
+                        n_rows * row_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
         finally:
             H.hisparse_host_free(h)
         out["zero_copy_read_GBs_" + ("coherent" if coherent else "noncoherent")] = round(zc, 2)

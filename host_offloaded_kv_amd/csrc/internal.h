@@ -218,6 +218,8 @@ hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);
 hipError_t launch_fetch(hisparse_pool* p, const FetchArgs& a, int grid, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_row_gather(void* dst, const void* src, const int64_t* rows, int64_t n_rows, int row_bytes,
+                             hipStream_t s);
 
 // residency.hip
 hipError_t launch_append(hisparse_pool* p, const AppendArgs& a, hipStream_t s);

@@ -957,4 +957,16 @@ hisparse_status hisparse_stream_copy(void* dst, const void* src, size_t bytes, v
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_stream_copy");
 }
 
+hisparse_status hisparse_row_gather(void* dst, const void* src, const int64_t* d_rows, int64_t n_rows,
+                                    int32_t row_bytes, void* stream) {
+  if (!dst || !src || (n_rows > 0 && !d_rows) || n_rows < 0 || row_bytes <= 0 || row_bytes % 16 ||
+      (uintptr_t)dst % 16 || (uintptr_t)src % 16 || (uintptr_t)d_rows % 8) {
+    set_error("hisparse_row_gather: bad argument (16-byte aligned pointers, row_bytes a positive multiple of 16)");
+    return HISPARSE_EINVAL;
+  }
+  if (n_rows == 0) return HISPARSE_OK;
+  hipError_t e = launch_row_gather(dst, src, d_rows, n_rows, row_bytes, (hipStream_t)stream);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "hisparse_row_gather");
+}
+
 }  // extern "C"

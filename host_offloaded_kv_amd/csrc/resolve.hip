@@ -585,6 +585,30 @@ __global__ __launch_bounds__(kCopyThreads) void copy16(u32x4* __restrict__ dst, 
   }
 }
 
+// Rows of `rc` 16-byte chunks gathered by a list of row indices: the miss
+// fetch's access pattern (one flat index over all chunks, nontemporal
+// 16-byte loads, several in flight per thread) without its metadata.
+__global__ __launch_bounds__(kCopyThreads) void gather16(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                        const int64_t* __restrict__ rows, int64_t n_chunks, int rc) {
+  const int64_t stride = (int64_t)gridDim.x * kCopyThreads * kFetchUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kCopyThreads * kFetchUnroll; base < n_chunks; base += stride) {
+    u32x4 v[kFetchUnroll];
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t q = base + (int64_t)u * kCopyThreads + threadIdx.x;
+      if (q < n_chunks) {
+        const int64_t i = q / rc;
+        v[u] = __builtin_nontemporal_load(src + rows[i] * rc + (q - i * rc));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t q = base + (int64_t)u * kCopyThreads + threadIdx.x;
+      if (q < n_chunks) dst[q] = v[u];
+    }
+  }
+}
+
 }  // namespace
 
 size_t resolve_lds_bytes(int top_k, int hot_slots) { return lds_map(top_k, hot_slots).total; }
@@ -638,6 +662,18 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(copy16, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, (u32x4*)dst, (const u32x4*)src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_gather(void* dst, const void* src, const int64_t* rows, int64_t n_rows, int row_bytes,
+                             hipStream_t s) {
+  const int rc = row_bytes / 16;
+  const int64_t n = n_rows * rc;
+  int64_t blocks = (n + kCopyThreads * kFetchUnroll - 1) / (kCopyThreads * kFetchUnroll);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(gather16, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, (u32x4*)dst, (const u32x4*)src,
+                     rows, n, rc);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ EXPORTED = (
     "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
     "hisparse_set_replacement",
     "hisparse_export_state", "hisparse_check_errors", "hisparse_decode_fallback_count",
-    "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy",
+    "hisparse_host_alloc", "hisparse_host_free", "hisparse_stream_copy", "hisparse_row_gather",
     "hisparse_profile_enable", "hisparse_profile_read",
 )
 
@@ -133,6 +133,7 @@ def load() -> ctypes.CDLL:
         "hisparse_host_alloc": (_I32, [ctypes.c_size_t, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP)]),
         "hisparse_host_free": (None, [_VP]),
         "hisparse_stream_copy": (_I32, [_VP, _VP, ctypes.c_size_t, _VP]),
+        "hisparse_row_gather": (_I32, [_VP, _VP, _VP, ctypes.c_int64, ctypes.c_int32, _VP]),
         "hisparse_profile_enable": (_I32, [_VP, _I32]),
         "hisparse_profile_read": (_I32, [_VP, ctypes.POINTER(hisparse_kernel_time), _I32, ctypes.POINTER(_I32)]),
     }
@@ -298,6 +299,10 @@ def hisparse_host_free(host: int) -> None:
 
 def hisparse_stream_copy(dst: int, src: int, nbytes: int, stream: int) -> None:
     _check(load().hisparse_stream_copy(dst, src, nbytes, stream))
+
+
+def hisparse_row_gather(dst: int, src: int, d_rows: int, n_rows: int, row_bytes: int, stream: int) -> None:
+    _check(load().hisparse_row_gather(dst, src, d_rows, n_rows, row_bytes, stream))
 
 
 def hisparse_profile_enable(pool: int, enable: bool) -> None:

@@ -368,6 +368,15 @@ void hisparse_host_free(void* host);
  * address (zero-copy read over the host link) or device memory. */
 hisparse_status hisparse_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Gather rows with the miss fetch's access pattern, for measuring the host
+ * link under it: row i of dst (row_bytes bytes, a positive multiple of 16)
+ * receives row d_rows[i] of src, for i < n_rows.  d_rows is a device array
+ * of n_rows int64 indices, which the caller keeps within src (they are not
+ * checked); src may be a device-mapped host address or device memory.
+ * Pointers 16-byte aligned (d_rows 8).  Errors: EINVAL, EHIP. */
+hisparse_status hisparse_row_gather(void* dst, const void* src, const int64_t* d_rows, int64_t n_rows,
+                                    int32_t row_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

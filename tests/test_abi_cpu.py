@@ -87,6 +87,7 @@ def test_null_arguments_rejected():
     assert lib.hisparse_step(None, None, None, None, 1.0, None, None, None, None, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_host_rows(None, 0, 0) is None
     assert lib.hisparse_stream_copy(None, None, 16, None) == H.HISPARSE_EINVAL
+    assert lib.hisparse_row_gather(None, None, None, 1, 1152, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_reset_state(None, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_set_replacement(None, 0, 0, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_sparse_mla_decode_layers(None, 0, 1, None, None, 1.0, None, None, None) == H.HISPARSE_EINVAL
