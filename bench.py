@@ -428,8 +428,10 @@ def main() -> int:
             alg = attn_bytes.sum() / n
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
         elif name == "resolve_meta":
+            # bound by latency (dependent LDS phases of one workgroup per
+            # (request, layer)); its HBM fraction is context only
             alg = meta_bytes.sum() / n
-            bound, peak, unit = "alu", None, "GB/s"
+            bound, peak, unit = "latency", HBM_PEAK_GBS, "GB/s"
         else:
             alg = None  # split merge: overhead only
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
