@@ -13,29 +13,30 @@
 // Work split: a workgroup handles (layer, request, group of up to 64 heads,
 // K split) with 12 wavefronts, three per SIMD, specialised by role:
 //  * score waves 0-3: wave w keeps the Q of heads 16w .. 16w+15 in
-//    registers and scores all 32 rows of each tile on 16x16x32 fp16 MFMA;
+//    registers and scores all 32 rows of each tile on 16x16x32 bf16 MFMA;
 //    it applies the softmax with a reference max per head and writes the
 //    probabilities P to LDS;
 //  * value waves 4-7: wave 4+c owns output columns 128c .. 128c+127 for
 //    every head of the group (fp32 accumulators in registers); it multiplies
 //    the transposed tile (read with ds_read_b64_tr_b16) by P;
 //  * loader waves 8-11: gather the row tiles through registers, three tiles
-//    ahead, convert them to fp16 and write them to LDS.
+//    ahead, and write them to LDS as bf16 (FP8 rows widened exactly).
 // The value waves run one tile behind the score waves and the loaders one
 // tile ahead, so each tile costs a single workgroup barrier, and no compute
 // wave waits on a global load or an LDS store.  Split partials are merged by
 // a second kernel.
 //
-// Precision.  Rows and Q are converted from bf16 to fp16, which is exact for
-// magnitudes in [2^-14, 2^16); smaller ones become fp16 subnormals (absolute
-// error below 2^-25).  The scores are therefore those of the bf16 inputs
-// with fp32 accumulation.  P is one fp16 plane: 11 significant bits, a
-// relative rounding error of at most 2^-11 per weight, while O and lse are
-// normalised by the sum of the unrounded fp32 weights.  (A single bf16
-// plane, 8 bits, gave O errors above 2e-3 of max|O| for near-uniform
-// weights.)  A value of magnitude 2^16 or more (or inf, NaN) becomes inf in
-// fp16 and makes every score of its row or head non-finite; the score waves
-// detect that, and the workgroup then computes its result again in plain
+// Precision.  The scores multiply the bf16 rows and queries as given (the
+// products are exact, accumulation fp32).  For PV the value waves convert
+// the row operands from bf16 to fp16, which is exact for magnitudes in
+// [2^-14, 2^16); smaller ones become fp16 subnormals (absolute error below
+// 2^-25).  P is one fp16 plane: 11 significant bits, a relative rounding
+// error of at most 2^-11 per weight, while O and lse are normalised by the
+// sum of the unrounded fp32 weights.  (A single bf16 plane, 8 bits, gave O
+// errors above 2e-3 of max|O| for near-uniform weights.)  A V value of
+// magnitude 2^16 or more becomes inf in fp16 and makes O inf or NaN (also
+// where its weight is zero), and an inf or NaN input makes a score
+// non-finite; either way the workgroup computes its result again in plain
 // fp32 arithmetic on the values as given (exact_fallback), a slow path for
 // inputs that KV caches do not hold.  FP8 rows always fit fp16.
 #include "internal.h"
@@ -78,6 +79,11 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two fp32 values that bf16 holds exactly -> their bf16 pair.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
 // A bf16 pair -> the fp16 pair of the same values.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t b) {
   return pack_f16(__uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
@@ -104,9 +110,9 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
 // row): eight threads cover contiguous bytes of a row per k, and every
 // address is one base plus an immediate.
 //
-// The LDS tile is fp16.  FP8 E4M3 rows are widened while staging: every
+// The LDS tile is bf16.  FP8 E4M3 rows are widened while staging: every
 // E4M3 value (at most 4 significant bits, magnitude at most 448, smallest
-// 2^-9) converts to fp32 and then to fp16 exactly; the layer's scale is
+// 2^-9) converts to fp32 and then to bf16 exactly; the layer's scale is
 // applied to the scores and to O instead.
 template <bool FP8>
 struct TileStage;
@@ -122,11 +128,7 @@ struct TileStage<false> {
   __device__ __forceinline__ void store(unsigned char* xs, int t) const {
     u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
 #pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-      const u32x4 w = {bf16x2_to_f16x2(v[k][0]), bf16x2_to_f16x2(v[k][1]), bf16x2_to_f16x2(v[k][2]),
-                       bf16x2_to_f16x2(v[k][3])};
-      dst[8 * k] = w;
-    }
+    for (int k = 0; k < kStage; ++k) dst[8 * k] = v[k];
   }
 };
 
@@ -146,8 +148,8 @@ struct TileStage<true> {
       const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][0], true);
       const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], false);
       const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[k][1], true);
-      const u32x4 w = {pack_f16(a0[0], a0[1]), pack_f16(a1[0], a1[1]), pack_f16(b0[0], b0[1]),
-                       pack_f16(b1[0], b1[1])};
+      const u32x4 w = {pack_bf16_exact(a0[0], a0[1]), pack_bf16_exact(a1[0], a1[1]), pack_bf16_exact(b0[0], b0[1]),
+                       pack_bf16_exact(b1[0], b1[1])};
       dst[8 * k] = w;
     }
   }
@@ -183,10 +185,10 @@ __device__ __forceinline__ void zero_acc(f32x4& d) {
 // Score MFMAs: A (tile rows) and B (Q) in VGPRs; the first k-step starts
 // from srcC = 0.
 __device__ __forceinline__ void mfma_score_first(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_score(f32x4& d, const u32x4& a, const f32x4& b) {
-  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 // The drains name the registers they protect as read-write operands of the
 // wait-state asm itself, so the MFMAs writing them stay above it and no
@@ -218,6 +220,7 @@ struct DecodeSmem {
   float lexact[HG], mfin[HG];           // weight sum and reference max per head
   int overflow[kMaxPasses];             // a tile exceeded the reference max
   int nonfinite;                        // a score was inf or NaN: exact_fallback takes over
+  int vbad;                             // an O accumulator is inf or NaN (read after the last barrier)
 };
 
 // Passes over the K range: the first uses the reference max of the first
@@ -295,7 +298,7 @@ __device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)
           mx = fmaxf(mx, sacc[rb][v]);
         }
       }
-      if (!finite) sm.nonfinite = 1;  // the fp16 result is discarded
+      if (!finite) sm.nonfinite = 1;  // the fast-path result is discarded
       m_seen = fmaxf(m_seen, mx);  // this lane's rows only; reduced when needed
       if (__builtin_amdgcn_readfirstlane(m_run == -INFINITY ? 1 : 0)) {
         // first tile with a valid row (the same tile for every head)
@@ -335,15 +338,13 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
                                            int n_tiles, int w, int g, int i16) {
   const bool active = 16 * w < HG;
   // Q as MFMA B operands: lane (g, i16) holds dims 32 s + 8 g .. +7 of
-  // head 16 w + i16, in fp16.
+  // head 16 w + i16, in bf16.
   f32x4 q[kLatent / 32];
   if (active) {
     gu32x4* qp = (gu32x4*)(a.q + (head0 + 16 * w + i16) * kLatent + 8 * g);
 #pragma unroll
     for (int s = 0; s < kLatent / 32; ++s) {
-      const u32x4 u = qp[4 * s];
-      const u32x4 h = {bf16x2_to_f16x2(u[0]), bf16x2_to_f16x2(u[1]), bf16x2_to_f16x2(u[2]), bf16x2_to_f16x2(u[3])};
-      q[s] = __builtin_bit_cast(f32x4, h);
+      q[s] = __builtin_bit_cast(f32x4, qp[4 * s]);
     }
 #pragma unroll
     for (int s = 0; s < kLatent / 32; s += 2) asm volatile("" : "+v"(q[s]), "+v"(q[s + 1]));
@@ -423,7 +424,7 @@ __device__ __forceinline__ void value_tiles(DecodeSmem<HG>& sm, f32x4 (&acc)[HG 
       // A operand (X^T, 16 cols x 32 rows) by two transposed reads: lane
       // (g, i16) addresses row 8 g + i16 / 4 (+4), columns 128 cw + 16 mb +
       // 4 (i16 % 4) .. +3, and receives column 128 cw + 16 mb + i16 of rows
-      // 8 g .. 8 g + 7.
+      // 8 g .. 8 g + 7 (bf16, converted to fp16 for the MFMA).
       uint32_t xoff = (8 * g + (i16 >> 2)) * kPitch + (128 * cw + 4 * (i16 & 3)) * 2;
       asm volatile("" : "+v"(xoff));
       const lds_u8* xl = (const lds_u8*)xb + xoff;
@@ -433,7 +434,9 @@ __device__ __forceinline__ void value_tiles(DecodeSmem<HG>& sm, f32x4 (&acc)[HG 
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(xl + 32 * mb));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(xl + 32 * mb + 4 * kPitch));
-        const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 raw = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 av = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
+                          bf16x2_to_f16x2(raw[3])};
         mfma_acc_after_valu(acc[mb * NBP], av, bp[0]);
 #pragma unroll
         for (int nb = 1; nb < NBP; ++nb) mfma_acc(acc[mb * NBP + nb], av, bp[nb]);
@@ -446,7 +449,7 @@ __device__ __forceinline__ void value_tiles(DecodeSmem<HG>& sm, f32x4 (&acc)[HG 
 
 // Value waves 4-7: wave 4+cw owns output columns 128cw .. 128cw+127 of every
 // head of the group, O^T[128 cols x HG heads] += X^T[cols x 32 rows] P^T.
-// Writes nothing when the fp16 result is discarded.
+// Writes nothing when the fast-path result is discarded.
 template <int HG, bool FP8>
 __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
                                            int pair, int split, int hg, int n_tiles, int cw, int g, int i16) {
@@ -463,10 +466,17 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
     if (!again(sm, p)) break;
     lds_barrier();
   }
-  __syncthreads();  // the score waves' normalisers are in LDS
-  if (sm.nonfinite) return;
-
   acc_drain(acc);
+  // A V value beyond fp16 became inf in the operand and shows up in O.
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 8 * NBP; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bad = bad || !(__builtin_fabsf(acc[i][v]) <= 3.0e38f);
+  if (bad) sm.vbad = 1;
+  __syncthreads();  // the score waves' normalisers are in LDS
+  if (sm.nonfinite || sm.vbad) return;
+
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
     const OutSlot o =
@@ -540,9 +550,10 @@ __device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned c
   __syncthreads();
 }
 
-// The result of a workgroup whose fp16 pass met a value beyond fp16, in
-// plain fp32 arithmetic on the values as given: a first sweep over the
-// rows finds each head's maximum score, a second forms the weights and O.
+// The result of a workgroup whose fast path met a value beyond fp16 or a
+// non-finite input, in plain fp32 arithmetic on the values as given: a
+// first sweep over the rows finds each head's maximum score, a second forms
+// the weights and O.
 // Rows are staged 16 at a time as fp32 in the tile buffers (with Q as
 // bf16); thread t < 8 HG owns O of head t / 8, columns 64 (t % 8) .. +63.
 constexpr int kFbRows = 16;
@@ -672,7 +683,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
 
   // Row ids of the whole K range, validated once.
   if (tid < kMaxPasses) sm.overflow[tid] = 0;
-  if (tid == 0) sm.nonfinite = 0;
+  if (tid == 0) {
+    sm.nonfinite = 0;
+    sm.vbad = 0;
+  }
   for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
   __syncthreads();
 
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   else
     loader_role<HG, FP8>(sm, kv, n_tiles, tid - 512);
   // nonfinite is final after every role's last barrier.
-  if (sm.nonfinite) {
+  if (sm.nonfinite || sm.vbad) {
     exact_fallback<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, k1 > k0 ? k1 - k0 : 0, tid);
     if (tid == 0) atomicAdd(a.fallback_count, 1u);
   }

@@ -330,11 +330,13 @@ hisparse_status hisparse_check_errors(hisparse_pool* pool, void* stream, uint32_
 
 /* Read and clear the number of decode workgroups (one per layer, query
  * set, head group and key split) that took the exact fp32 path since the
- * last call or pool creation.  The decode computes in fp16 (exact for bf16
- * values of magnitude below 2^16); a workgroup whose rows or queries hold a
- * value of magnitude 2^16 or more, an inf or a NaN (any staged row counts,
- * also the filler row of a -1 entry) computes its result again in fp32 on
- * the values as given, which is correct but far slower.  A nonzero count
+ * last call or pool creation.  The decode scores the bf16 values as given
+ * and multiplies P by the V part (the first 512 values) of each row in fp16
+ * (exact for bf16 values of magnitude below 2^16).  A workgroup whose rows
+ * hold a V value of magnitude 2^16 or more, or whose rows or queries hold
+ * an inf or a NaN (any staged row counts, also the filler row of a -1
+ * entry), computes its result again in fp32 on the values as given, which
+ * is correct but far slower.  A nonzero count
  * thus flags inputs outside the fast path; results do not depend on it
  * beyond rounding.  Synchronises the stream.  Errors: EINVAL, EHIP. */
 hisparse_status hisparse_decode_fallback_count(hisparse_pool* pool, void* stream, int64_t* count);
