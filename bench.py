@@ -168,7 +168,7 @@ def cpu_baseline(w, trace, budget_s=20.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    reqs = list(range(min(6, w.num_requests)))  # about 10-20 s of oracle work on the machine's host
+    reqs = list(range(min(6, w.num_requests)))  # about 10-20 s of oracle work on the host
     dec = OracleDecoder(w, requests=reqs)
     t0 = time.time()
     steps = 0
@@ -215,8 +215,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: every (request, layer) is independent and this build "
-              "measures one GPU's share; multi-GPU runs are not part of it.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: every (request, layer) is independent, and the benchmark "
+              "measures one GPU's share; runs on several GPUs are not supported.", file=sys.stderr)
         return 2
 
     import numpy as np
