@@ -141,8 +141,8 @@ struct Layout {
       err, fallback_count, partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
+  size_t partial_floats;   // floats of the split-partial region
   int32_t splits_max;      // largest split count any decode launch uses
-  int32_t layers_batched;  // layers decoded by one launch in hisparse_step
 };
 
 }  // namespace hs

@@ -121,16 +121,21 @@ Layout make_layout(const hisparse_config* c) {
   int64_t bt_entries = 0;
   for (size_t r = 0; r < R; ++r) bt_entries += (capacity_of(c, (int)r) + c->page_size - 1) / c->page_size;
   L.bt_entries = bt_entries;
-  L.layers_batched = c->index_share;
-  const int s1 = decode_splits(1, (int)(R * T), c->num_heads, c->top_k);
-  const int sg = decode_splits(c->index_share, (int)(R * T), c->num_heads, c->top_k);
-  L.splits_max = s1 > sg ? s1 : sg;
-  size_t part_1 = 0;  // one layer, any request count up to R (pipelined chunks)
-  for (size_t nreq = 1; nreq <= R; ++nreq) {
-    const int sn = decode_splits(1, (int)(nreq * T), c->num_heads, c->top_k);
-    if (sn > 1) part_1 = std::max(part_1, (size_t)sn * nreq * T * c->num_heads * kPartW);
-  }
-  size_t part_g = sg > 1 ? (size_t)sg * c->index_share * R * T * c->num_heads * kPartW : 0;
+  // Split partials, sized for every decode launch the pool can make: any
+  // number of layers of one index-share group over all R * T query sets
+  // (hisparse_sparse_mla_decode_layers, hisparse_step), and one layer over
+  // any request chunk (the chunked last layer of hisparse_step).
+  size_t part = 0;
+  int smax = 1;
+  auto need = [&](int n_layers, size_t nsets) {
+    const int sn = decode_splits(n_layers, (int)nsets, c->num_heads, c->top_k);
+    smax = std::max(smax, sn);
+    if (sn > 1) part = std::max(part, (size_t)sn * n_layers * nsets * c->num_heads * kPartW);
+  };
+  for (int n = 1; n <= c->index_share; ++n) need(n, R * T);
+  for (size_t nreq = 1; nreq <= R; ++nreq) need(1, nreq * T);
+  L.splits_max = smax;
+  L.partial_floats = part;
   size_t off = 0;
   L.owner = off; off = align256(off + NL * R * B * 4);
   L.stamp = off; off = align256(off + NL * R * B * 4);
@@ -148,7 +153,7 @@ Layout make_layout(const hisparse_config* c) {
   L.kv_scale = off; off = align256(off + NL * 4);
   L.err = off; off = align256(off + 4);
   L.fallback_count = off; off = align256(off + 4);
-  L.partial = off; off = align256(off + (part_1 > part_g ? part_1 : part_g) * 4);
+  L.partial = off; off = align256(off + part * 4);
   int64_t ctx_sum = 0;
   for (size_t r = 0; r < R; ++r) ctx_sum += capacity_of(c, (int)r);
   L.posmap_entries = (int64_t)NL * ctx_sum;
@@ -538,6 +543,13 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.num_heads = p->cfg.num_heads;
   a.top_k = p->cfg.top_k;
   a.splits = splits > 0 ? splits : decode_splits(n_layers, nreq, p->cfg.num_heads, p->cfg.top_k);
+  if (a.splits > 1 &&
+      (size_t)a.splits * n_layers * nreq * p->cfg.num_heads * kPartW > p->lay.partial_floats) {
+    // cannot happen for the launches the workspace is sized for; refuse
+    // rather than write past the partial region
+    set_error("decode launch needs more split partials than the workspace holds");
+    return HISPARSE_EINVAL;
+  }
   a.kv_rows = p->kv_rows;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = launch_decode(p, a, s);

@@ -141,7 +141,13 @@ hisparse_status hisparse_workspace_bytes(const hisparse_config* cfg, size_t* byt
 /* Rows each layer's KV tensor must have: resident_rows_per_layer + R * B. */
 hisparse_status hisparse_kv_rows_per_layer(const hisparse_config* cfg, int64_t* rows);
 
-/* Create a pool on the current device.
+/* Create a pool on the current device.  The pool is the two-level store
+ * of the HiSparse summary article, section 02: the authoritative full KV of
+ * every request and sparse layer in pinned host DRAM, and B device slots per
+ * (request, layer) with a page table and LRU metadata.  The vLLM Hybrid
+ * HiSparse blog ("与 vLLM 其余部分的组合", appendix "附录：复现我们的结果")
+ * allocates that pinned pool per data-parallel replica, sized in whole host
+ * blocks; here one pool serves one GPU's requests.
  *   d_workspace: device buffer of at least hisparse_workspace_bytes bytes,
  *                256-byte aligned; owned by the caller, must outlive the pool.
  *   d_kv:        host array of L device pointers; d_kv[l] is a tensor of
@@ -166,7 +172,10 @@ void hisparse_destroy_pool(hisparse_pool* pool);
  * argument. */
 void* hisparse_host_rows(hisparse_pool* pool, int32_t r, int32_t l);
 
-/* Set the block table of request r: host_bt[page] is the resident block id
+/* Set the block table of request r (mixed residency, vLLM Hybrid HiSparse
+ * blog, "工作原理": residency is tracked per page; resident pages are read in
+ * place, the others are placeholders whose rows live in the host pool):
+ * host_bt[page] is the resident block id
  * of that page, or -1 (host-only placeholder); n_pages must equal
  * ceil(capacity_r / page_size).  Block ids must satisfy
  * (id + 1) * page_size <= resident_rows_per_layer.  The library never edits
@@ -177,20 +186,30 @@ hisparse_status hisparse_set_block_table(hisparse_pool* pool, int32_t r, const i
                                          int32_t n_pages, void* stream);
 
 /* RESOLVE layers [layer_begin, layer_begin + n_layers), which share one
- * selection (they must lie in one index-share group).
+ * selection (they must lie in one index-share group).  RESOLVE is the fused
+ * per-layer step of the HiSparse summary article, section 02 (hit
+ * detection, LRU replacement, metadata update and host fetch; logical
+ * positions in, physical rows out), with the residency rule of the vLLM
+ * Hybrid HiSparse blog, "工作原理" (resident tokens read in place, hot
+ * tokens refresh their LRU entry, a miss copies one row into an LRU slot).
  *   d_step:   device int32 scalar, the step index t (>= 0, non-decreasing
  *             per (request, layer)); read on the device.
  *   d_topk:   device int32 [R][K] logical positions, -1 = padding, any order.
  *   d_rows:   device int32 [n_layers][R][K] out: row id per entry (-1 for padding).
  *   d_counts: device int32 [n_layers][R][3] out: (resident, hit, miss).
- * Enqueues the metadata kernel (one four-wavefront workgroup per (request,
+ * Enqueues the metadata kernel (one 16-wavefront workgroup per (request,
  * layer)) and one miss fetch over all n_layers (zero-copy 16-byte loads
  * from the host pool into hot rows), both on `stream`. */
 hisparse_status hisparse_resolve(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers,
                                  const int32_t* d_step, const int32_t* d_topk, int32_t* d_rows,
                                  int32_t* d_counts, void* stream);
 
-/* Sparse MLA decode attention of one layer over resolved rows.
+/* Sparse MLA decode attention of one layer over resolved rows.  The HiSparse
+ * summary article, section 02, fixes that only the placement of KV changes:
+ * selected positions, scores and outputs are those of attention over the
+ * full KV (exactness); the vLLM Hybrid HiSparse blog (Fig. 1 text, "一个块池")
+ * puts resident and hot rows in one KV tensor, so the kernel sees ordinary
+ * rows.
  *   d_q:    device bf16 [R][H][576]
  *   d_rows: device int32 [R][K] row ids of this layer (-1 = skip)
  *   scale:  softmax scale applied to q . x
@@ -318,13 +337,18 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,
                                       int32_t unit_fetch_workgroups, int32_t tail_chunks);
 
-/* Copy the LRU state of (request r, layer l) to host arrays of B int32:
+/* Copy the LRU state of (request r, layer l) -- the slot owners and LRU
+ * stamps that the HiSparse summary article, section 02, keeps per device
+ * slot -- to host arrays of B int32:
  * owner (logical position per slot, -1 empty) and stamp (step of last use,
  * -1 never).  Synchronises the stream.  Errors: EINVAL, EHIP. */
 hisparse_status hisparse_export_state(hisparse_pool* pool, int32_t r, int32_t l, int32_t* host_owner,
                                       int32_t* host_stamp, void* stream);
 
-/* Read and clear the device error flags (HISPARSE_ERR_* bits).
+/* Read and clear the device error flags (HISPARSE_ERR_* bits).  The pages
+ * do not describe error handling; an indexer emits K distinct positions
+ * (HiSparse summary article, section 01), so a repeat or an out-of-range
+ * position is the caller's error, flagged here and treated as padding.
  * Synchronises the stream. */
 hisparse_status hisparse_check_errors(hisparse_pool* pool, void* stream, uint32_t* flags);
 

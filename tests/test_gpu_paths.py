@@ -230,3 +230,51 @@ def test_decode_layers_matches_oracle():
         log(f"decode_layers step {t}: worst O rel err {worst:.3e}")
     assert hs.check_errors() == 0
     hs.close()
+
+
+def test_decode_layers_part_of_group_then_steps():
+    """decode_layers over 1, 2 and 3 layers of a 4-layer index-share group
+    (launch shapes whose key splits need more partial rows than a whole-group
+    or a one-layer launch), then further steps: attention matches the oracle
+    and the LRU state stays exact, so no partial write reached the
+    metadata that follows the partial region in the workspace."""
+    import torch
+
+    # 64 requests x 64 heads x K 512: a 3-layer launch takes 2 key splits
+    # (384 partial sets) where one layer at any request count needs at most 315
+    w = make_workload("part_group_r64_g4", 21, 64, 4, 4, [4096] * 64, 64, 512, 1024, 6, 0.7, 0.8, "tail")
+    tr = w.trace(w.steps)
+    hs = make_pool(w)
+    buf = _Buffers(w, hs.device)
+    dec = OracleDecoder(w)
+    pairs = [(l, r) for l in range(w.num_layers) for r in range(w.num_requests)]
+    some = [(l, r) for l in range(w.num_layers) for r in (0, 17, 63)]
+    out2 = torch.full_like(buf.out, float("nan"))
+    lse2 = torch.full_like(buf.lse, float("nan"))
+
+    class _View:
+        pass
+
+    for t in range(w.steps):
+        buf.load(w, t, tr[t])
+        hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+        res = dec.resolve_step(t, tr[t])
+        torch.cuda.synchronize(hs.device)
+        rows, counts = buf.rows.cpu().numpy(), buf.counts.cpu().numpy()
+        for (l, r) in pairs:
+            rr = res[(l, r)]
+            assert np.array_equal(rows[l, r], np.asarray(rr.rows, np.int32)), f"rows t={t} l={l} r={r}"
+            assert tuple(int(x) for x in counts[l, r]) == (rr.n_resident, rr.n_hit, rr.n_miss), \
+                f"counts t={t} l={l} r={r}"
+        check_state(hs, dec, pairs, t)
+        for (l0, n) in ((0, 3), (1, 3), (1, 2), (3, 1)):
+            hs.decode_layers(l0, n, buf.q[l0:l0 + n], buf.rows[l0:l0 + n], w.scale, out2[l0:l0 + n],
+                             lse2[l0:l0 + n])
+            torch.cuda.synchronize(hs.device)
+            v = _View()
+            v.w, v.out, v.lse = w, out2.cpu(), lse2.cpu()
+            lp = [(l, r) for (l, r) in some if l0 <= l < l0 + n]
+            worst = check_attention(v, dec, t, tr[t], lp)
+            log(f"step {t}: decode_layers({l0}, {n}) worst O rel err {worst:.3e}")
+    assert hs.check_errors() == 0
+    hs.close()
