@@ -158,30 +158,102 @@ def ctypes_fill(addr: int, nbytes: int) -> None:
     ctypes.memset(addr, 1, nbytes)
 
 
-def cpu_baseline(w, trace, budget_s=20.0):
-    """The CPU oracle, untuned, on a bounded sample of the same workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, trace, warmup, budget_s=12.0, one_thread_steps=2):
+    """The CPU oracle, untuned, on a bounded sample of the same workload.
+
+    Requests 0..5 (all, if fewer) of every layer; steps 0..warmup-1 are
+    resolved untimed (they only build the LRU state, as the GPU's warm-up
+    steps do), then steps from `warmup` on are timed until `budget_s` runs
+    out.  Per step the time is split into RESOLVE (the pure-Python step
+    LRU), row generation (the oracle regenerates from the counter-based
+    generator every row and query it reads instead of holding a filled
+    pool) and ATTEND (fp64 NumPy).  ATTEND is timed again on the first
+    timed steps with the BLAS library held to one thread."""
+    import numpy as np
+
+    from oracle.attention import attend
     from oracle.step import OracleDecoder
+    from tracegen import kv_rows, q_block
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    reqs = list(range(min(6, w.num_requests)))  # about 10-20 s of oracle work on the host
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: no thread control
+        threadpool_limits, blas = None, None
+    reqs = list(range(min(6, w.num_requests)))
     dec = OracleDecoder(w, requests=reqs)
-    t0 = time.time()
-    steps = 0
-    for t in range(trace.shape[0]):
-        dec.step(t, trace[t])
-        steps += 1
-        if time.time() - t0 > budget_s:
+    units = [(l, r, i) for l in range(w.num_layers) for r in reqs for i in range(w.num_verify)]
+    t0 = time.perf_counter()
+    for t in range(min(warmup, trace.shape[0])):
+        dec.resolve_step(t, trace[t])
+    warm_s = time.perf_counter() - t0
+
+    T = w.num_verify
+
+    def gen(t, l, r, i):
+        g = l // w.index_share
+        sel = trace[t][g][r][i] if T > 1 else trace[t][g][r]
+        pos = list(dict.fromkeys(int(p) for p in sel if p >= 0))
+        q = q_block(w.seed, w.query_step(t, i), l, r, w.num_heads, w.latent_dim)
+        return q, kv_rows(w.seed, r, l, pos, w.latent_dim)
+
+    t_res = t_gen = t_att = 0.0
+    steps = []
+    t0 = time.perf_counter()
+    for t in range(warmup, trace.shape[0]):
+        a = time.perf_counter()
+        dec.resolve_step(t, trace[t])
+        b = time.perf_counter()
+        t_res += b - a
+        for (l, r, i) in units:
+            c = time.perf_counter()
+            q, x = gen(t, l, r, i)
+            d = time.perf_counter()
+            attend(q, x, w.scale, w.v_dim)
+            e = time.perf_counter()
+            t_gen += d - c
+            t_att += e - d
+        steps.append(t)
+        if time.perf_counter() - t0 > budget_s:
             break
-    el = time.time() - t0
-    tokens = len(reqs) * steps * w.num_verify
-    return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"requests {reqs} x all {w.num_layers} layers x steps 0..{steps - 1} "
-                      f"(resolve + fp64 attention), {el:.1f} s"}
+    n = len(steps)
+    tokens = len(reqs) * n * w.num_verify
+    total = t_res + t_gen + t_att
+    one = None
+    if threadpool_limits is not None and n:
+        sub = steps[:one_thread_steps]
+        data = [gen(t, l, r, i) for t in sub for (l, r, i) in units]
+        with threadpool_limits(limits=1):
+            a = time.perf_counter()
+            for q, x in data:
+                attend(q, x, w.scale, w.v_dim)
+            att1 = (time.perf_counter() - a) / len(sub)
+        per_step = (t_res + t_gen) / n + att1
+        one = {"value": round(len(reqs) * w.num_verify / per_step, 3), "attend_s_per_step": round(att1, 4),
+               "steps": len(sub)}
+    return {"value": round(tokens / total, 3), "unit": "tokens/s",
+            "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"requests {reqs} x all {w.num_layers} layers x steps {steps[0]}..{steps[-1]} after "
+                      f"{warmup} untimed warm-up steps (resolve + row generation + fp64 attention), {total:.1f} s",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "blas_threads": blas,
+            "split_s_per_step": {"resolve": round(t_res / n, 4), "row_generation": round(t_gen / n, 4),
+                                 "attend": round(t_att / n, 4)},
+            "warmup_resolve_s": round(warm_s, 2),
+            "one_thread": one}
 
 
 def main() -> int:
@@ -212,6 +284,11 @@ def main() -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 3 device-to-device copies of this size with the library's copy kernel "
                          "(a known-size reference for hardware byte counters)")
+    ap.add_argument("--calib-host-mib", type=int, default=0,
+                    help="also run 3 zero-copy reads of this size from a pinned host buffer into device memory "
+                         "with the same copy kernel (the reference for counters of host-link reads)")
+    ap.add_argument("--unsorted", action="store_true",
+                    help="feed every selection in a shuffled (indexer) order instead of ascending")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -242,6 +319,12 @@ def main() -> int:
     log(f"workload {w.name}: R={R} L={L} g={w.index_share} ctx={w.ctx_len[0]} H={Hh} K={K} B={B}")
     t0 = time.time()
     trace = w.trace(n_steps)
+    if args.unsorted:
+        rng = np.random.default_rng(2024)
+        trace = trace.copy()
+        flat = trace.reshape(-1, trace.shape[-1])
+        for i in range(flat.shape[0]):
+            flat[i] = rng.permutation(flat[i])
     log(f"trace generated ({n_steps} steps) in {time.time() - t0:.1f}s")
     cfg = w.config_dict()
     cfg["host_coherent"] = args.host_coherent
@@ -251,7 +334,8 @@ def main() -> int:
     log(f"pool created ({sum(w.ctx_len) * L * row_bytes / 1e9:.2f} GB pinned) in {time.time() - t0:.1f}s")
     t0 = time.time()
     populate(hs, w)
-    log(f"host pool filled and residency uploaded in {time.time() - t0:.1f}s")
+    pool_fill_s = time.time() - t0
+    log(f"host pool filled and residency uploaded in {pool_fill_s:.1f}s")
 
     d_steps = torch.arange(n_steps, dtype=torch.int32, device=dev)
     d_topk = torch.from_numpy(trace).to(dev)  # [T][G][R][K]
@@ -487,13 +571,25 @@ def main() -> int:
             H.hisparse_stream_copy(dst.data_ptr(), src.data_ptr(), nb, stream.cuda_stream)
         torch.cuda.synchronize(dev)
         del src, dst
+    if args.calib_host_mib:
+        nb = args.calib_host_mib << 20
+        h, d = H.hisparse_host_alloc(nb, 0)
+        try:
+            ctypes_fill(h, nb)
+            dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                H.hisparse_stream_copy(dst.data_ptr(), d, nb, stream.cuda_stream)
+            torch.cuda.synchronize(dev)
+            del dst
+        finally:
+            H.hisparse_host_free(h)
 
     cpu = None
     hs.close()
     del hs
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        cpu = cpu_baseline(w, trace)
+        cpu = cpu_baseline(w, trace, args.warmup)
         log(f"cpu baseline: {cpu}")
 
     out = {
@@ -512,7 +608,8 @@ def main() -> int:
         "config": {"workload": w.name, "requests": R, "ctx": int(w.ctx_len[0]), "layers": L,
                    "index_share": w.index_share, "heads": Hh, "top_k": K, "hot_slots": B,
                    "seed": w.seed, "host_coherent": args.host_coherent, "policy": args.policy,
-                   "kv_dtype": w.kv_dtype, "num_verify": T},
+                   "kv_dtype": w.kv_dtype, "num_verify": T,
+                   "selection_order": "shuffled (indexer order)" if args.unsorted else "ascending"},
         "roofline": roofline,
         "kernels": kern,
         "step": {"us": round(ms_step * 1e3, 2),
@@ -537,6 +634,7 @@ def main() -> int:
                                                                   4)}} if dec_us else None,
         "residency": residency,
         "host_link": probe,
+        "gpu_host_pool_fill_s": round(pool_fill_s, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -253,6 +253,20 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     set_error("workspace too small: need " + std::to_string(lay.total) + " bytes");
     return HISPARSE_EINVAL;
   }
+  if (cfg->host_pool_limit < 0) {
+    set_error("host_pool_limit must be >= 0");
+    return HISPARSE_EINVAL;
+  }
+  if (cfg->host_pool_limit > 0) {
+    const int64_t rb = cfg->kv_dtype == HISPARSE_KV_FP8_E4M3 ? kRowBytesFp8 : kRowBytes;
+    int64_t need = 0;
+    for (int r = 0; r < cfg->num_requests; ++r) need += (int64_t)cfg->num_layers * capacity_of(cfg, r) * rb;
+    if (need > cfg->host_pool_limit) {
+      set_error("the pinned host pool needs " + std::to_string(need) + " bytes, above host_pool_limit " +
+                std::to_string(cfg->host_pool_limit));
+      return HISPARSE_ENOMEM;
+    }
+  }
   hipStream_t s = (hipStream_t)stream;
 
   hisparse_pool* p = new (std::nothrow) hisparse_pool();

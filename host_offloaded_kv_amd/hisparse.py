@@ -75,6 +75,7 @@ class hisparse_config(ctypes.Structure):
         ("ctx_capacity", ctypes.POINTER(ctypes.c_int64)),
         ("kv_dtype", ctypes.c_int32), ("num_verify", ctypes.c_int32),
         ("kv_scale", ctypes.POINTER(ctypes.c_float)),
+        ("host_pool_limit", ctypes.c_int64),
     ]
 
 
@@ -170,6 +171,7 @@ def make_config(cfg: dict) -> tuple[hisparse_config, object]:
         ctx_capacity=ctypes.cast(cap, ctypes.POINTER(ctypes.c_int64)) if cap is not None else None,
         kv_dtype=kv_dtype_code(cfg.get("kv_dtype", "bf16")), num_verify=cfg.get("num_verify", 1),
         kv_scale=ctypes.cast(scl, ctypes.POINTER(ctypes.c_float)) if scl is not None else None,
+        host_pool_limit=int(cfg.get("host_pool_limit", 0)),
     )
     return c, (ctx, cap, scl)
 

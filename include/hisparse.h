@@ -113,6 +113,11 @@ typedef struct {
                             0 is read as 1.  T > 1 is multi-token verification (see below) */
   const float* kv_scale; /* [L] host array or NULL (= 1.0): scale of each layer's FP8 rows
                             (finite, > 0); ignored for bf16 rows; copied */
+  int64_t host_pool_limit; /* bytes of pinned host memory the pool may take, 0 = no limit.  The
+                              vLLM Hybrid HiSparse blog sizes the pinned pool per replica
+                              (host_pool_gib, appendix "附录：复现我们的结果"); a pool needing
+                              more (sum over r of L * capacity_r * row bytes) is refused with
+                              HISPARSE_ENOMEM before anything is allocated */
 } hisparse_config;
 
 /* Multi-token verification (num_verify = T > 1).  The vLLM Hybrid HiSparse
@@ -158,7 +163,8 @@ hisparse_status hisparse_kv_rows_per_layer(const hisparse_config* cfg, int64_t* 
  * capacity_r rows (filled by the caller via hisparse_host_rows).
  * Every slot starts empty and every page host-only.
  * Errors: EINVAL (bad config, null or misaligned pointers, workspace too
- * small), ENOMEM (pinned allocation failed), EHIP, EDEVICE. */
+ * small), ENOMEM (the pool exceeds host_pool_limit, or the pinned
+ * allocation failed), EHIP, EDEVICE. */
 hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspace, size_t ws_bytes,
                                      void* const* d_kv, void* stream, hisparse_pool** out);
 

@@ -103,3 +103,47 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(H, "LIB_PATH", os.path.join(ROOT, "does_not_exist.so"))
     with pytest.raises(RuntimeError):
         H.load()
+
+
+def _create(c, ws, ws_bytes, kv):
+    lib = H.load()
+    arr = (ctypes.c_void_p * len(kv))(*kv)
+    out = ctypes.c_void_p()
+    st = lib.hisparse_create_pool(ctypes.byref(c), ws, ws_bytes, arr, None, ctypes.byref(out))
+    return st, out.value
+
+
+def test_misaligned_and_short_buffers_rejected_before_any_device_call():
+    """The pointer checks run before the library touches the device, so
+    made-up aligned addresses reach them; nothing is dereferenced."""
+    c, keep = _cfg()
+    ws_bytes = H.hisparse_workspace_bytes(c)
+    good_kv = [0x10000 + 0x1000 * l for l in range(4)]
+    st, p = _create(c, 0x20000 + 128, ws_bytes, good_kv)  # workspace must be 256-byte aligned
+    assert st == H.HISPARSE_EINVAL and p is None
+    assert "d_workspace" in H.hisparse_last_error() and "aligned" in H.hisparse_last_error()
+    bad_kv = list(good_kv)
+    bad_kv[2] += 8  # KV tensors must be 16-byte aligned
+    st, p = _create(c, 0x20000, ws_bytes, bad_kv)
+    assert st == H.HISPARSE_EINVAL and "d_kv" in H.hisparse_last_error()
+    st, p = _create(c, 0x20000, ws_bytes - 1, good_kv)  # one byte short
+    assert st == H.HISPARSE_EINVAL and "workspace too small" in H.hisparse_last_error()
+
+
+def test_host_pool_limit_gives_enomem_before_allocating():
+    """A pool above its pinned-memory budget (the blog's per-replica
+    host_pool_gib) is refused with ENOMEM before any allocation."""
+    c, keep = _cfg()
+    need = 4 * (131072 + 5000) * 1152
+    ws_bytes = H.hisparse_workspace_bytes(c)
+    kv = [0x10000 + 0x1000 * l for l in range(4)]
+    c.host_pool_limit = need - 1
+    st, p = _create(c, 0x20000, ws_bytes, kv)
+    assert st == H.HISPARSE_ENOMEM and p is None
+    assert str(need) in H.hisparse_last_error()
+    c8, keep8 = _cfg(kv_dtype="fp8", host_pool_limit=need // 2 - 1)  # 576-byte rows need half
+    st, p = _create(c8, 0x20000, H.hisparse_workspace_bytes(c8), kv)
+    assert st == H.HISPARSE_ENOMEM and str(need // 2) in H.hisparse_last_error()
+    c.host_pool_limit = -5
+    st, p = _create(c, 0x20000, ws_bytes, kv)
+    assert st == H.HISPARSE_EINVAL

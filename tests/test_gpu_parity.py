@@ -181,3 +181,18 @@ def test_r32_ctx128k_l4():
     hs, _, _ = run_and_compare(w, attend_every=5, attend_pairs=pairs, bytes_pairs=[(3, 17)],
                                label="r32_ctx128k_l4")
     hs.close()
+
+
+def test_r8_ctx32k_indexer_order():
+    """The r8_ctx32k workload with every selection in a shuffled (indexer)
+    order instead of ascending: the metadata kernel's unsorted path at full
+    width (K = 2048, one token), bit-exact against the oracle."""
+    w = named_workload("r8_ctx32k")
+    tr = w.trace(w.steps).copy()
+    rng = np.random.default_rng(4242)
+    for t in range(tr.shape[0]):
+        for g in range(tr.shape[1]):
+            for r in range(tr.shape[2]):
+                tr[t, g, r] = rng.permutation(tr[t, g, r])
+    hs, _, _ = run_and_compare(w, attend_every=4, bytes_pairs=[(0, 3)], label="r8_ctx32k indexer order", trace=tr)
+    hs.close()
