@@ -42,6 +42,7 @@
 #include "internal.h"
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 namespace hs {
@@ -773,6 +774,32 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) 
 }
 
 }  // namespace
+
+// Split partials of hisparse_sparse_mla_decode_layers_static, for callers
+// that cannot allocate: a fixed array that every GPU the library runs on
+// holds until the process ends.  Host code never passes `scratch` itself
+// (its name is a host-side stand-in, not a device address); it looks up the
+// device address once per device and passes that to the kernels.
+static __device__ __align__(256) float scratch[HISPARSE_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch_address(int device, float** out) {
+  if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[device] = static_cast<float*>(ptr);
+  }
+  *out = scratch_ptr[device];
+  return hipSuccess;
+}
 
 int head_group(int num_heads) { return num_heads % 64 == 0 ? 64 : (num_heads % 32 == 0 ? 32 : 16); }
 

@@ -192,6 +192,7 @@ struct hisparse_pool {
   float* kv_scale_d;
   uint32_t* err;
   float* partial;
+  float* static_scratch = nullptr;  // fixed split-partial array of this pool's device
   uint32_t* fallback_count;
   // Overlapped step: per-layer miss fetches run on fetch_stream (default
   // priority) while the caller's stream decodes earlier layers.
@@ -227,5 +228,8 @@ hipError_t launch_writeback(hisparse_pool* p, const WritebackArgs& a, hipStream_
 
 // decode.hip
 int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
+// Device address of the fixed split-partial array on `device` (which must
+// be current), looked up once per device and kept.
+hipError_t static_scratch_address(int device, float** out);
 hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s);
 }  // namespace hs

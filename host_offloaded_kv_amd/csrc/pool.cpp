@@ -298,6 +298,11 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     delete p;
     return hip_fail(e, "hipGetDevice");
   }
+  e = static_scratch_address(p->device, &p->static_scratch);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetSymbolAddress(static split scratch)");
+  }
   p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots);
   int max_lds = 0;
   e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
@@ -537,9 +542,11 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
 // nreq: query sets per layer covered by the pointers -- requests times
 // verify tokens, for all requests or a chunk of them when one layer is
 // decoded piecewise.
+// use_static: split partials in the fixed device array instead of the
+// workspace (hisparse_sparse_mla_decode_layers_static).
 hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, int32_t nreq,
                                const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out, float* d_lse,
-                               hipStream_t s, int splits = 0) {
+                               hipStream_t s, int splits = 0, bool use_static = false) {
   DecodeArgs a;
   a.q = d_q;
   a.rows = d_rows;
@@ -548,7 +555,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.kv_dtype = p->cfg.kv_dtype;
   a.out = d_out;
   a.lse = d_lse;
-  a.partial = p->partial;
+  a.partial = use_static ? p->static_scratch : p->partial;
   a.fallback_count = p->fallback_count;
   a.err = p->err;
   a.layer_begin = layer_begin;
@@ -557,8 +564,14 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.num_heads = p->cfg.num_heads;
   a.top_k = p->cfg.top_k;
   a.splits = splits > 0 ? splits : decode_splits(n_layers, nreq, p->cfg.num_heads, p->cfg.top_k);
-  if (a.splits > 1 &&
-      (size_t)a.splits * n_layers * nreq * p->cfg.num_heads * kPartW > p->lay.partial_floats) {
+  const size_t part_floats = a.splits > 1 ? (size_t)a.splits * n_layers * nreq * p->cfg.num_heads * kPartW : 0;
+  if (use_static && part_floats * sizeof(float) > HISPARSE_STATIC_SCRATCH_BYTES) {
+    set_error("decode launch needs " + std::to_string(part_floats * sizeof(float)) +
+              " bytes of split partials; the static scratch holds " +
+              std::to_string(HISPARSE_STATIC_SCRATCH_BYTES));
+    return HISPARSE_EINVAL;
+  }
+  if (!use_static && part_floats > p->lay.partial_floats) {
     // cannot happen for the launches the workspace is sized for; refuse
     // rather than write past the partial region
     set_error("decode launch needs more split partials than the workspace holds");
@@ -612,29 +625,46 @@ hisparse_status hisparse_sparse_mla_decode(hisparse_pool* p, int32_t layer, cons
                         (hipStream_t)stream);
 }
 
-hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
-                                                  const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out,
-                                                  float* d_lse, void* stream) {
+namespace {
+hisparse_status decode_layers_impl(const char* fn, hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
+                                   const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out,
+                                   float* d_lse, void* stream, bool use_static) {
+  const std::string f(fn);
   if (!p || !d_q || !d_rows || !d_out || !d_lse) {
-    set_error("hisparse_sparse_mla_decode_layers: NULL argument");
+    set_error(f + ": NULL argument");
     return HISPARSE_EINVAL;
   }
   const int g = p->cfg.index_share;
   if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > p->cfg.num_layers ||
       layer_begin / g != (layer_begin + n_layers - 1) / g) {
-    set_error("hisparse_sparse_mla_decode_layers: layers must lie inside one index-share group");
+    set_error(f + ": layers must lie inside one index-share group");
     return HISPARSE_EINVAL;
   }
   if ((uintptr_t)d_q % 16) {
-    set_error("hisparse_sparse_mla_decode_layers: d_q must be 16-byte aligned");
+    set_error(f + ": d_q must be 16-byte aligned");
     return HISPARSE_EINVAL;
   }
   if (!std::isfinite(scale)) {
-    set_error("hisparse_sparse_mla_decode_layers: scale must be finite");
+    set_error(f + ": scale must be finite");
     return HISPARSE_EINVAL;
   }
   return enqueue_decode(p, layer_begin, n_layers, p->cfg.num_requests * p->T, d_q, d_rows, scale, d_out, d_lse,
-                        (hipStream_t)stream);
+                        (hipStream_t)stream, 0, use_static);
+}
+}  // namespace
+
+hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
+                                                  const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out,
+                                                  float* d_lse, void* stream) {
+  return decode_layers_impl("hisparse_sparse_mla_decode_layers", p, layer_begin, n_layers, d_q, d_rows, scale, d_out,
+                            d_lse, stream, false);
+}
+
+hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* p, int32_t layer_begin, int32_t n_layers,
+                                                         const uint16_t* d_q, const int32_t* d_rows, float scale,
+                                                         float* d_out, float* d_lse, void* stream) {
+  return decode_layers_impl("hisparse_sparse_mla_decode_layers_static", p, layer_begin, n_layers, d_q, d_rows, scale,
+                            d_out, d_lse, stream, true);
 }
 
 hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,

@@ -39,6 +39,9 @@ HISPARSE_KV_FP8_E4M3 = 1
 KV_DTYPES = {"bf16": HISPARSE_KV_BF16, "fp8": HISPARSE_KV_FP8_E4M3}
 ROW_BYTES = {HISPARSE_KV_BF16: 1152, HISPARSE_KV_FP8_E4M3: 576}
 
+# size of the fixed split-partial array of hisparse_sparse_mla_decode_layers_static
+HISPARSE_STATIC_SCRATCH_BYTES = 64 << 20
+
 # replacement policies (hisparse_set_replacement)
 HISPARSE_POLICY_LRU = 0
 HISPARSE_POLICY_FIFO = 1
@@ -53,7 +56,7 @@ EXPORTED = (
     "hisparse_last_error", "hisparse_workspace_bytes", "hisparse_kv_rows_per_layer",
     "hisparse_create_pool", "hisparse_destroy_pool", "hisparse_host_rows",
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
-    "hisparse_sparse_mla_decode_layers",
+    "hisparse_sparse_mla_decode_layers", "hisparse_sparse_mla_decode_layers_static",
     "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
     "hisparse_set_replacement",
@@ -120,6 +123,8 @@ def load() -> ctypes.CDLL:
         "hisparse_resolve": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_sparse_mla_decode": (_I32, [_VP, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
         "hisparse_sparse_mla_decode_layers": (_I32, [_VP, _I32, _I32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
+        "hisparse_sparse_mla_decode_layers_static": (_I32, [_VP, _I32, _I32, _VP, _VP, ctypes.c_float, _VP, _VP,
+                                                            _VP]),
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
         "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
@@ -230,6 +235,12 @@ def hisparse_sparse_mla_decode(pool, layer, d_q, d_rows, scale, d_out, d_lse, st
 def hisparse_sparse_mla_decode_layers(pool, layer_begin, n_layers, d_q, d_rows, scale, d_out, d_lse, stream) -> None:
     _check(load().hisparse_sparse_mla_decode_layers(pool, layer_begin, n_layers, d_q, d_rows, float(scale), d_out,
                                                     d_lse, stream))
+
+
+def hisparse_sparse_mla_decode_layers_static(pool, layer_begin, n_layers, d_q, d_rows, scale, d_out, d_lse,
+                                             stream) -> None:
+    _check(load().hisparse_sparse_mla_decode_layers_static(pool, layer_begin, n_layers, d_q, d_rows, float(scale),
+                                                           d_out, d_lse, stream))
 
 
 def hisparse_step(pool, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse, stream) -> None:

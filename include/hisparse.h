@@ -239,6 +239,24 @@ hisparse_status hisparse_sparse_mla_decode_layers(hisparse_pool* pool, int32_t l
                                                   const uint16_t* d_q, const int32_t* d_rows, float scale,
                                                   float* d_out, float* d_lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * launch as hisparse_sparse_mla_decode_layers, with the key-split partials
+ * kept in a fixed device array of HISPARSE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, instead of
+ * in the pool's workspace.  Allocates nothing.  Results are bit-identical
+ * to hisparse_sparse_mla_decode_layers.  The array is shared by every pool
+ * on a GPU and keeps the last call's contents (each launch writes every
+ * partial it reads, so nothing needs clearing); calls that overlap on one
+ * GPU -- on different streams, or under different pools -- race on it and
+ * must be ordered by the caller.  Errors: EINVAL when the launch needs more
+ * partials than the array holds (the message gives both sizes), and the
+ * checks of hisparse_sparse_mla_decode_layers. */
+#define HISPARSE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers,
+                                                         const uint16_t* d_q, const int32_t* d_rows, float scale,
+                                                         float* d_out, float* d_lse, void* stream);
+
 /* One decode step over every layer: for each index-share group, RESOLVE all
  * of its layers with the group's selection, then decode each layer.
  *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],

@@ -147,3 +147,9 @@ def test_host_pool_limit_gives_enomem_before_allocating():
     c.host_pool_limit = -5
     st, p = _create(c, 0x20000, ws_bytes, kv)
     assert st == H.HISPARSE_EINVAL
+
+
+def test_static_scratch_size_matches_header():
+    with open(os.path.join(ROOT, "include", "hisparse.h")) as f:
+        m = re.search(r"#define HISPARSE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == H.HISPARSE_STATIC_SCRATCH_BYTES
