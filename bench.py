@@ -279,6 +279,9 @@ def main() -> int:
     ap.add_argument("--num-verify", type=int, default=1,
                     help="query tokens per request per step (multi-token verification); the value "
                          "then counts verified query tokens")
+    ap.add_argument("--hot-slots", type=int, default=0,
+                    help="hot slots per (request, layer); 0 = the workload's, or (T + 1) x top-K with "
+                         "T = --num-verify > 1 verify tokens")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="KV row format: bf16 (the named workloads) or FP8 E4M3 codes with a per-layer scale")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -312,6 +315,11 @@ def main() -> int:
     if args.kv_dtype == "fp8":
         w = with_fp8(w)
     w.num_verify = args.num_verify
+    if args.hot_slots:
+        w.hot_slots = args.hot_slots
+    elif w.num_verify > 1:
+        # the blog sizes the hot buffer (num_speculative_tokens + 2) x top-K
+        w.hot_slots = max(w.hot_slots, (w.num_verify + 1) * w.top_k)
     n_steps = args.warmup + args.steps
     L, R, K, Hh, B = w.num_layers, w.num_requests, w.top_k, w.num_heads, w.hot_slots
     T = w.num_verify

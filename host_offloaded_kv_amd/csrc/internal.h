@@ -17,8 +17,9 @@ constexpr int kRowBytes = kLatent * 2;      // bf16 row
 constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks per bf16 row (72)
 constexpr int kRowBytesFp8 = kLatent;       // FP8 E4M3 row (36 chunks)
 constexpr int kPartW = kVDim + 4;           // split partial: o[512], m, l (rounded weights), l (exact), pad
-constexpr int kMaxTopK = 4096;
-constexpr int kMaxHotSlots = 8192;
+constexpr int kMaxTopK = 4096;       // K: entries of one token's selection
+constexpr int kMaxSelection = 8192;  // T * K: entries one RESOLVE covers (verify tokens concatenated)
+constexpr int kMaxHotSlots = 16384;  // B (slot ids stay below 2^15: the position map is int16)
 constexpr int kMaxHeads = 256;
 // Workgroups of the miss fetch: a whole-group fetch (hisparse_resolve) owns
 // the GPU; a per-layer fetch of the overlapped step leaves most CUs to the
@@ -178,6 +179,7 @@ struct hisparse_pool {
   int64_t kv_rows = 0;
   int32_t row_bytes = hs::kRowBytes;    // bytes per KV row (1152 bf16, 576 FP8)
   size_t resolve_lds = 0;
+  int max_lds = 0;                      // LDS bytes per workgroup the device allows
   int32_t policy = HISPARSE_POLICY_LRU;
   uint64_t policy_seed = 0;
   int32_t T = 1;                        // verify tokens per request per step
@@ -213,7 +215,7 @@ void prof_begin(hisparse_pool* p, int kid, hipStream_t s);
 void prof_end(hisparse_pool* p, hipStream_t s);
 
 // resolve.hip
-size_t resolve_lds_bytes(int top_k, int hot_slots);
+size_t resolve_lds_bytes(int selection_width, int hot_slots, bool random_policy);
 hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s);
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);

@@ -19,7 +19,7 @@
 #include "internal.h"
 
 namespace hs {
-hipError_t set_resolve_lds_limit(size_t bytes);
+hipError_t set_resolve_lds_limit(int device, size_t bytes);
 
 namespace {
 thread_local std::string g_last_error;
@@ -55,8 +55,8 @@ hisparse_status check_config(const hisparse_config* c) {
     return HISPARSE_EINVAL;
   }
   const int T = c->num_verify < 1 ? 1 : c->num_verify;
-  if (c->num_verify < 0 || (int64_t)T * c->top_k > kMaxTopK) {
-    set_error("num_verify must be >= 0 and num_verify * top_k <= 4096");
+  if (c->num_verify < 0 || (int64_t)T * c->top_k > kMaxSelection) {
+    set_error("num_verify must be >= 0 and num_verify * top_k <= 8192");
     return HISPARSE_EINVAL;
   }
   if (c->kv_scale && c->kv_dtype == HISPARSE_KV_FP8_E4M3) {
@@ -71,7 +71,7 @@ hisparse_status check_config(const hisparse_config* c) {
     return HISPARSE_EINVAL;
   }
   if (c->hot_slots < c->top_k * (c->num_verify < 1 ? 1 : c->num_verify) || c->hot_slots > kMaxHotSlots) {
-    set_error("hot_slots must satisfy num_verify * top_k <= hot_slots <= 8192");
+    set_error("hot_slots must satisfy num_verify * top_k <= hot_slots <= 16384");
     return HISPARSE_EINVAL;
   }
   if (c->page_size < 1 || ilog2_exact(c->page_size) < 0 || c->page_size > (1 << 20)) {
@@ -303,22 +303,25 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     delete p;
     return hip_fail(e, "hipGetSymbolAddress(static split scratch)");
   }
-  p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots);
+  p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots, false);
   int max_lds = 0;
   e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
   if (e != hipSuccess) {
     delete p;
     return hip_fail(e, "hipDeviceGetAttribute");
   }
+  p->max_lds = max_lds;
   if ((size_t)max_lds < p->resolve_lds) {
     set_error("resolve needs " + std::to_string(p->resolve_lds) + " bytes of LDS, device allows " +
               std::to_string(max_lds));
     delete p;
     return HISPARSE_EDEVICE;
   }
-  if (p->resolve_lds > 65536) {
-    e = set_resolve_lds_limit(p->resolve_lds);
-    if (e != hipSuccess) {
+  {
+    // allow the largest metadata launch of any policy that fits the device
+    const size_t lds_random = resolve_lds_bytes(p->W, cfg->hot_slots, true);
+    const size_t lim = lds_random <= (size_t)max_lds ? lds_random : p->resolve_lds;
+    if (lim > 65536 && (e = set_resolve_lds_limit(p->device, lim)) != hipSuccess) {
       delete p;
       return hip_fail(e, "hipFuncSetAttribute(resolve LDS)");
     }
@@ -856,6 +859,16 @@ hisparse_status hisparse_set_replacement(hisparse_pool* p, int32_t policy, uint6
   if (!p || (policy != HISPARSE_POLICY_LRU && policy != HISPARSE_POLICY_FIFO && policy != HISPARSE_POLICY_RANDOM)) {
     set_error("hisparse_set_replacement: bad argument");
     return HISPARSE_EINVAL;
+  }
+  if (policy == HISPARSE_POLICY_RANDOM) {
+    // random replacement sorts the unpinned slots in LDS beside the miss list
+    const size_t need = resolve_lds_bytes(p->W, p->cfg.hot_slots, true);
+    if (need > (size_t)p->max_lds) {
+      set_error("hisparse_set_replacement: random replacement needs " + std::to_string(need) +
+                " bytes of LDS at this selection width and slot count, the device allows " +
+                std::to_string(p->max_lds));
+      return HISPARSE_EDEVICE;
+    }
   }
   p->policy = policy;
   p->policy_seed = seed;

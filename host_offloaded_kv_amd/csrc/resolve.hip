@@ -30,6 +30,7 @@
 #include "internal.h"
 
 #include <climits>
+#include <mutex>
 
 namespace hs {
 namespace {
@@ -61,11 +62,13 @@ int ceil_log2(int64_t v) {
 
 constexpr int kMetaThreads = 1024;  // 16 wavefronts per (request, layer)
 constexpr int kMetaWaves = kMetaThreads / 64;
-constexpr int kSelChunks = kMaxTopK / kMetaThreads;       // 64-entry chunks of the selection per wave (max)
-constexpr int kSlotChunks = kMaxHotSlots / kMetaThreads;  // 64-entry chunks of the order array per wave (max)
 
+// LDS of one metadata workgroup: the selection (W int32), the sort and
+// miss-list region (W 64-bit keys, a power of two), the victims (W int32),
+// one pin byte per slot, and for random replacement a second key region of
+// B entries (the misses stay in the first while the victims are sorted).
 struct LdsMap {
-  size_t sel, mpos, mj, vic, rows, tflag, region, total;
+  size_t sel, key, vic, tflag, rkey, total;
 };
 
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -76,18 +79,14 @@ __host__ __device__ inline int next_pow2(int v) {
   return p;
 }
 
-__host__ __device__ inline LdsMap lds_map(int K, int B) {
+__host__ __device__ inline LdsMap lds_map(int W, int B, bool random) {
   LdsMap m;
   m.sel = 0;
-  m.mpos = m.sel + 4 * (size_t)K;
-  m.mj = m.mpos + 4 * (size_t)K;
-  m.vic = m.mj + 4 * (size_t)K;
-  m.rows = m.vic + 4 * (size_t)K;
-  m.tflag = m.rows + 4 * (size_t)K;
-  m.region = m.tflag + round16((size_t)B);
-  // sort keys: (position, index) on the unsorted-input path, (priority,
-  // slot) of the random replacement policy
-  m.total = m.region + 8 * (size_t)next_pow2(K > B ? K : B);
+  m.key = round16(m.sel + 4 * (size_t)W);
+  m.vic = m.key + 8 * (size_t)next_pow2(W);
+  m.tflag = round16(m.vic + 4 * (size_t)W);
+  m.rkey = round16(m.tflag + (size_t)B);
+  m.total = m.rkey + (random ? 8 * (size_t)next_pow2(B) : 0);
   return m;
 }
 
@@ -158,19 +157,22 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 //    keep its ballots in registers, exchange the sixteen counts through LDS
 //    and write at base + ballot prefix.  The order array is read once into
 //    registers and rewritten at the end.
+//  * The misses are kept as 64-bit keys (position << 32 | entry index), so
+//    the unsorted path sorts them in place.
+// SC / BC: 64-entry chunks of the selection / of the order array per wave
+// (the selection width W is at most 1024 SC, the slot count B at most 1024 BC).
+template <int SC, int BC>
 __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int cnt_s[2][kMetaWaves];
   __shared__ int red_s[2][kMetaWaves];
   const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
-  const LdsMap M = lds_map(K, B);
+  const LdsMap M = lds_map(K, B, a.policy == HISPARSE_POLICY_RANDOM);
   int32_t* sel_s = (int32_t*)(smem + M.sel);
-  int32_t* mpos_s = (int32_t*)(smem + M.mpos);
-  int32_t* mj_s = (int32_t*)(smem + M.mj);
+  unsigned long long* key_s = (unsigned long long*)(smem + M.key);  // sort region, then the miss list
   int32_t* vic_s = (int32_t*)(smem + M.vic);
-  int32_t* row_s = (int32_t*)(smem + M.rows);  // row of every resolved entry (copies read it)
   unsigned char* tflag_s = smem + M.tflag;
-  unsigned long long* key_s = (unsigned long long*)(smem + M.region);
+  unsigned long long* rkey_s = (unsigned long long*)(smem + M.rkey);
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -217,9 +219,9 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   const int nsc = Bq / 64;
 
   g2l_block(sel_s, topk, K, wid, lane);
-  int lv[kSlotChunks];  // order-array entries of this wave
+  int lv[BC];  // order-array entries of this wave
 #pragma unroll
-  for (int c = 0; c < kSlotChunks; ++c) {
+  for (int c = 0; c < BC; ++c) {
     const int i = ib + 64 * c + lane;
     lv[c] = (c < nsc && i < ie) ? lru_g[i] : 0;
   }
@@ -277,14 +279,14 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
         sel_s[j] = -2 - (int)(uint32_t)key_s[f];
       }
     }
-    __syncthreads();
+    __syncthreads();  // the key region is free again
   }
 
   // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
   const int32_t* bt = a.bt + a.bt_off[r];
-  int pv[kSelChunks], bv[kSelChunks], sv[kSelChunks];
+  int pv[SC], bv[SC], sv[SC];
 #pragma unroll
-  for (int c = 0; c < kSelChunks; ++c) {
+  for (int c = 0; c < SC; ++c) {
     const int j = jb + 64 * c + lane;
     const int p = (c < njc && j < je) ? sel_s[j] : -1;
     pv[c] = p;
@@ -292,9 +294,9 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     sv[c] = p >= 0 ? (int)map[p] : -1;
   }
   int n_res = 0, n_hit = 0, mloc = 0;
-  uint64_t mb[kSelChunks];
+  uint64_t mb[SC];
 #pragma unroll
-  for (int c = 0; c < kSelChunks; ++c) {
+  for (int c = 0; c < SC; ++c) {
     const int j = jb + 64 * c + lane;
     const int p = pv[c];
     bool miss = false;
@@ -318,10 +320,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
           miss = true;
         }
       }
-      if (!miss) {
-        rows_out[j] = row;
-        row_s[j] = row;
-      }
+      if (!miss) rows_out[j] = row;
     }
     mb[c] = __ballot(miss);
     mloc += __popcll(mb[c]);
@@ -332,11 +331,10 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   {
     int run = wave_base(cnt_s[0], wid, &m);
 #pragma unroll
-    for (int c = 0; c < kSelChunks; ++c) {
+    for (int c = 0; c < SC; ++c) {
       if ((mb[c] >> lane) & 1) {
         const int idx = run + __popcll(mb[c] & lt);
-        mpos_s[idx] = pv[c];
-        mj_s[idx] = jb + 64 * c + lane;
+        key_s[idx] = ((unsigned long long)(uint32_t)pv[c] << 32) | (uint32_t)(jb + 64 * c + lane);
       }
       run += __popcll(mb[c]);
     }
@@ -346,15 +344,9 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   if (!fast && m > 1) {
     // Ascending position order of the misses.
     const int mp = next_pow2(m);
-    for (int i = tid; i < mp; i += kMetaThreads)
-      key_s[i] = i < m ? (((unsigned long long)(uint32_t)mpos_s[i] << 32) | (uint32_t)mj_s[i]) : ~0ull;
+    for (int i = m + tid; i < mp; i += kMetaThreads) key_s[i] = ~0ull;
     __syncthreads();
     bitonic_sort(key_s, mp, tid);
-    for (int i = tid; i < m; i += kMetaThreads) {
-      mpos_s[i] = (int)(key_s[i] >> 32);
-      mj_s[i] = (int)(uint32_t)key_s[i];
-    }
-    __syncthreads();
   }
 
   if (a.policy == HISPARSE_POLICY_RANDOM) {
@@ -370,18 +362,17 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
         key = owner_g[i] < 0 ? (unsigned long long)i
                              : ((1ull << 63) | ((splitmix64(k ^ (uint64_t)i) >> 33) << 32) | (uint32_t)i);
       }
-      key_s[i] = key;
+      rkey_s[i] = key;
     }
     __syncthreads();
-    bitonic_sort(key_s, BP, tid);
-    for (int i = tid; i < m; i += kMetaThreads) vic_s[i] = (int)(uint32_t)key_s[i];
+    bitonic_sort(rkey_s, BP, tid);
+    for (int i = tid; i < m; i += kMetaThreads) vic_s[i] = (int)(uint32_t)rkey_s[i];
   } else {
-  // Victims: the first m unpinned slots of the (stamp, slot) order array.
-  {
-    uint64_t vb[kSlotChunks];
+    // Victims: the first m unpinned slots of the (stamp, slot) order array.
+    uint64_t vb[BC];
     int uloc = 0;
 #pragma unroll
-    for (int c = 0; c < kSlotChunks; ++c) {
+    for (int c = 0; c < BC; ++c) {
       const int i = ib + 64 * c + lane;
       const bool cand = c < nsc && i < ie && (tflag_s[lv[c]] & 1) == 0;
       vb[c] = __ballot(cand);
@@ -392,14 +383,13 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     int unpinned;
     int run = wave_base(cnt_s[1], wid, &unpinned);
 #pragma unroll
-    for (int c = 0; c < kSlotChunks; ++c) {
+    for (int c = 0; c < BC; ++c) {
       if ((vb[c] >> lane) & 1) {
         const int rank = run + __popcll(vb[c] & lt);
         if (rank < m) vic_s[rank] = lv[c];
       }
       run += __popcll(vb[c]);
     }
-  }
   }
   __syncthreads();
 
@@ -408,7 +398,8 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   // map entries cleared and set here are all distinct.
   int2* fetch = a.fetch + cpair * K;
   for (int i = tid; i < m; i += kMetaThreads) {
-    const int v = vic_s[i], p = mpos_s[i], j = mj_s[i];
+    const unsigned long long x = key_s[i];
+    const int v = vic_s[i], p = (int)(x >> 32), j = (int)(uint32_t)x;
     const int old = owner_g[v];
     if (old >= 0) map[old] = -1;
     map[p] = (int16_t)v;
@@ -416,25 +407,24 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     stamp_g[v] = t;
     tflag_s[v] |= 5;
     rows_out[j] = (int)(hot_base + v);
-    row_s[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
-  __syncthreads();
+  __syncthreads();  // also makes every row id written above visible to the workgroup
   if (!fast) {
     // Entries that repeat a position of an earlier verify token take its row.
     for (int j = tid; j < K; j += kMetaThreads) {
       const int p = sel_s[j];
-      if (p <= -2) rows_out[j] = row_s[-2 - p];
+      if (p <= -2) rows_out[j] = rows_out[-2 - p];
     }
   }
 
   // New order: slots with stamp < t (untouched; old order), then every slot
   // stamped t, by slot index.
   {
-    uint64_t ka[kSlotChunks], kb[kSlotChunks];
+    uint64_t ka[BC], kb[BC];
     int ca = 0, cb = 0;
 #pragma unroll
-    for (int c = 0; c < kSlotChunks; ++c) {
+    for (int c = 0; c < BC; ++c) {
       const int i = ib + 64 * c + lane;
       const bool in = c < nsc && i < ie;
       // stamp < t: neither stamped by this call nor earlier in this step
@@ -452,7 +442,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     int ra = wave_base(cnt_s[0], wid, &nA);
     int rb = nA + wave_base(cnt_s[1], wid, &nB);
 #pragma unroll
-    for (int c = 0; c < kSlotChunks; ++c) {
+    for (int c = 0; c < BC; ++c) {
       const int i = ib + 64 * c + lane;
       if ((ka[c] >> lane) & 1) lru_g[ra + __popcll(ka[c] & lt)] = lv[c];
       if ((kb[c] >> lane) & 1) lru_g[rb + __popcll(kb[c] & lt)] = i;
@@ -611,7 +601,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather16(u32x4* __restrict__ dst
 
 }  // namespace
 
-size_t resolve_lds_bytes(int top_k, int hot_slots) { return lds_map(top_k, hot_slots).total; }
+size_t resolve_lds_bytes(int top_k, int hot_slots, bool random) { return lds_map(top_k, hot_slots, random).total; }
 
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   const auto& c = p->cfg;
@@ -638,10 +628,25 @@ hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s) {
   return launch_state_reset(p, s);
 }
 
+// Chunk counts of the metadata kernel: the common sizes (W <= 4096, B <=
+// 8192) keep the per-wave register arrays of the first instance; larger
+// selections (multi-token verification) and buffers take the second.
+constexpr int kSelChunksSmall = 4, kSlotChunksSmall = 8;
+constexpr int kSelChunksLarge = kMaxSelection / kMetaThreads;
+constexpr int kSlotChunksLarge = kMaxHotSlots / kMetaThreads;
+static_assert(kSelChunksLarge * kMetaThreads == kMaxSelection && kSlotChunksLarge * kMetaThreads == kMaxHotSlots,
+              "whole chunks per wave");
+
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
-  const size_t lds = lds_map(a.top_k, a.hot_slots).total;
+  const size_t lds = lds_map(a.top_k, a.hot_slots, a.policy == HISPARSE_POLICY_RANDOM).total;
+  const dim3 grid(a.n_layers * a.num_requests), block(kMetaThreads);
+  const bool small_sel = a.top_k <= kSelChunksSmall * kMetaThreads;
+  const bool small_slots = a.hot_slots <= kSlotChunksSmall * kMetaThreads;
   prof_begin(p, kKMeta, s);
-  hipLaunchKernelGGL(resolve_meta, dim3(a.n_layers * a.num_requests), dim3(kMetaThreads), lds, s, a);
+  if (small_sel && small_slots)
+    hipLaunchKernelGGL((resolve_meta<kSelChunksSmall, kSlotChunksSmall>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((resolve_meta<kSelChunksLarge, kSlotChunksLarge>), grid, block, lds, s, a);
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   return e;
@@ -677,8 +682,22 @@ hipError_t launch_row_gather(void* dst, const void* src, const int64_t* rows, in
   return hipGetLastError();
 }
 
-hipError_t set_resolve_lds_limit(size_t bytes) {
-  return hipFuncSetAttribute((const void*)resolve_meta, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+// The dynamic-LDS limit is an attribute of the kernel, shared by every pool
+// of the process, so it only ever grows (per device): a pool with a smaller
+// selection must not lower the limit another pool's launches rely on.
+hipError_t set_resolve_lds_limit(int device, size_t bytes) {
+  static std::mutex mu;
+  static size_t cur[64] = {};
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (bytes <= cur[device]) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)resolve_meta<kSelChunksSmall, kSlotChunksSmall>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)resolve_meta<kSelChunksLarge, kSlotChunksLarge>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) cur[device] = bytes;
+  return e;
 }
 
 }  // namespace hs

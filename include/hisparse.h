@@ -98,7 +98,7 @@ typedef struct {
   int32_t latent_dim;    /* must be 576 */
   int32_t v_dim;         /* must be 512 */
   int32_t top_k;         /* K: positions per selection, 1..4096 */
-  int32_t hot_slots;     /* B: hot rows per (request, layer), K <= B <= 8192 */
+  int32_t hot_slots;     /* B: hot rows per (request, layer), num_verify * K <= B <= 16384 */
   int32_t page_size;     /* tokens per page, a power of two (64) */
   int32_t num_heads;     /* H: query heads, a multiple of 16, <= 256 */
   int32_t host_coherent; /* 0: coarse-grained (non-coherent) pinned pool, 1: coherent */
@@ -130,7 +130,8 @@ typedef struct {
  * selected by several tokens is resolved once, at its earliest entry, and
  * every copy gets that row; a repeat inside one token's list is an error
  * (HISPARSE_ERR_DUP, padding).  Counts are over the distinct positions.
- * Requires T*K <= 4096 and B >= T*K (the blog sizes B = (T + 1) * K).
+ * Requires T*K <= 8192 and B >= T*K (the blog sizes B = (T + 1) * K, so
+ * MTP3 at K = 2048 is T = 4, B = 10240).
  * Selections, row ids, queries and outputs then carry a token axis after
  * the request axis: d_topk [..][R][T][K], d_rows [..][R][T][K],
  * d_q [..][R][T][H][576], d_out [..][R][T][H][512], d_lse [..][R][T][H];

@@ -90,7 +90,7 @@ def check_hot_bytes(hs, w, dec, pairs, t):
 
 
 # Worst secondary error metrics seen by check_attention (reported, see below).
-ATTN_STATS = {"per_head": 0.0, "elementwise_floor": 0.0}
+ATTN_STATS = {"block": 0.0, "per_head": 0.0, "elementwise_floor": 0.0}
 
 
 def attention_errors(o, o_ref):
@@ -125,6 +125,7 @@ def check_attention(run, dec, t, sel_t, pairs):
             continue
         err, per_head, floor = attention_errors(o, o_ref)
         worst = max(worst, err)
+        ATTN_STATS["block"] = max(ATTN_STATS["block"], err)
         ATTN_STATS["per_head"] = max(ATTN_STATS["per_head"], per_head)
         ATTN_STATS["elementwise_floor"] = max(ATTN_STATS["elementwise_floor"], floor)
         assert err <= O_TOL, f"O rel err {err:.3e} t={t} l={l} r={r}"

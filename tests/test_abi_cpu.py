@@ -47,7 +47,7 @@ def test_sizes():
     dict(hot_slots=1000),            # B < K
     dict(top_k=0),
     dict(top_k=5000, hot_slots=8000),
-    dict(hot_slots=9000),
+    dict(hot_slots=17000),           # above 16384
     dict(index_share=3),             # L % g != 0
     dict(num_heads=24),              # not a multiple of 16
     dict(page_size=48),              # not a power of two
@@ -56,7 +56,8 @@ def test_sizes():
     dict(latent_dim=512),
     dict(kv_dtype=2),                        # unknown row format
     dict(num_verify=-1),
-    dict(num_verify=3),                      # T * K = 6144 > 4096
+    dict(num_verify=3),                      # B = 4096 < T * K = 6144
+    dict(num_verify=5, hot_slots=16384),     # T * K = 10240 > 8192
     dict(num_verify=2, hot_slots=4095),      # B < T * K
     dict(kv_dtype="fp8", kv_scale=[1.0, 0.0, 1.0, 1.0]),
     dict(kv_dtype="fp8", kv_scale=[1.0, float("nan"), 1.0, 1.0]),
@@ -153,3 +154,10 @@ def test_static_scratch_size_matches_header():
     with open(os.path.join(ROOT, "include", "hisparse.h")) as f:
         m = re.search(r"#define HISPARSE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
     assert m and int(m.group(1)) << int(m.group(2)) == H.HISPARSE_STATIC_SCRATCH_BYTES
+
+
+def test_mtp3_at_top_k_2048_is_accepted():
+    """The blog's MTP3 setting at K = 2048: T = 4, B = (T + 1) K = 10240."""
+    c, keep = _cfg(num_verify=4, hot_slots=10240)
+    assert H.hisparse_workspace_bytes(c) > 0
+    assert H.hisparse_kv_rows_per_layer(c) == 128 + 2 * 10240

@@ -104,3 +104,30 @@ def test_verify_mtp1_r8_ctx32k():
     w.num_verify = 2
     w.name = "r8_ctx32k_mtp1"
     assert _run(w, 8, attend_every=3, attend_pairs=[(0, 0), (0, 5)]) == 0
+
+
+def test_verify_mtp3_r8_ctx32k():
+    """Three speculative tokens (MTP3, the blog's benchmark setting) on the
+    8 x 32K workload at its top-K of 2048: one RESOLVE over T*K = 8192
+    entries per (request, layer) into a buffer of (T + 1) * K = 10240 slots,
+    the blog's (num_speculative_tokens + 2) x top-K sizing."""
+    w = named_workload("r8_ctx32k")
+    w.num_verify = 4
+    w.hot_slots = (w.num_verify + 1) * w.top_k
+    w.name = "r8_ctx32k_mtp3"
+    assert _run(w, 6, attend_every=2, attend_pairs=[(0, 0), (0, 6)]) == 0
+
+
+def test_random_policy_refused_where_its_sort_does_not_fit():
+    """Random replacement sorts B keys in LDS beside the miss list; at T*K =
+    8192 and B = 10240 that does not fit, and the pool says so."""
+    from host_offloaded_kv_amd import hisparse as H
+
+    w = make_workload("mtp3_small", 5, 1, 1, 1, [16384], 16, 2048, 10240, 2, 0.7, 0.8, "none")
+    w.num_verify = 4
+    hs = make_pool(w)
+    with pytest.raises(H.HiSparseError) as ei:
+        hs.set_replacement("random", 1)
+    assert ei.value.status == H.HISPARSE_EDEVICE and "LDS" in H.hisparse_last_error()
+    hs.set_replacement("fifo", 0)  # the order-array policies fit
+    hs.close()
