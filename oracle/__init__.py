@@ -27,4 +27,5 @@ Modules:
   attention   dense fp64 softmax attention over the selected rows
   step        one decode step over a workload (resolve every layer of a
               group, then attend every layer)
+  prefetch    cross-step prefetch of a predicted selection into the buffer
 """

@@ -58,3 +58,43 @@ def replay(owner, stamp, sel, t, ctx, block_table, page_size, hot_base):
         used[best] = True
         rows[j] = hot_base + best
     return rows, (n_res, n_hit, len(pending)), owner, stamp
+
+
+def replay_prefetch(owner, stamp, sel, t, block_table, page_size):
+    """Brute-force prefetch (same reading as ``oracle.prefetch``): slots
+    stamped t and slots holding a selected position are off limits; each
+    missing position, smallest first, takes the slot of smallest (stamp,
+    slot) among the rest, found by a full scan, until none is left.
+    Returns (filled [(position, slot)], new_owner, new_stamp).  Assumes a
+    valid call (distinct in-range positions, t not decreasing)."""
+    owner = list(owner)
+    stamp = list(stamp)
+    B = len(owner)
+    off = [stamp[s] == t for s in range(B)]
+    missing = []
+    for p in sel:
+        p = int(p)
+        if p < 0 or block_table[p // page_size] >= 0:
+            continue
+        hit = False
+        for s in range(B):
+            if owner[s] == p:
+                off[s] = True
+                hit = True
+        if not hit:
+            missing.append(p)
+    filled = []
+    for p in sorted(missing):
+        best = -1
+        for s in range(B):
+            if off[s]:
+                continue
+            if best < 0 or stamp[s] < stamp[best] or (stamp[s] == stamp[best] and s < best):
+                best = s
+        if best < 0:
+            break
+        owner[best] = p
+        stamp[best] = t
+        off[best] = True
+        filled.append((p, best))
+    return filled, owner, stamp
