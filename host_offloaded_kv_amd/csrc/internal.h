@@ -110,6 +110,10 @@ struct ResolveArgs {
   int64_t resident_rows;
   int32_t policy;           // HISPARSE_POLICY_*
   uint64_t policy_seed;     // random replacement: SplitMix64 seed
+  int32_t prefetch;         // 1: prefetch of a predicted selection (no row ids; slots stamped t are
+                            // pinned; hits pinned without a stamp; misses beyond the free slots
+                            // dropped); counts then holds [n_layers][R][4] (resident, hit, filled,
+                            // dropped) or is NULL
   int16_t* posmap;          // [L][sum ctx] position -> slot (-1: not in the hot buffer)
   const int64_t* map_off;   // [R] offset of request r within a layer's map
   int64_t map_layer_stride; // sum of ctx_r
@@ -138,8 +142,8 @@ struct DecodeArgs {
 
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
-  size_t owner, stamp, lru, last_t, miss_count, fetch, bt, bt_off, ctx, cap, hv, host_rows, kv_ptrs, kv_scale,
-      err, fallback_count, partial, posmap, map_off, total;
+  size_t owner, stamp, lru, last_t, miss_count, fetch, pf_miss_count, pf_fetch, bt, bt_off, ctx, cap, hv, host_rows,
+      kv_ptrs, kv_scale, err, fallback_count, partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
   size_t partial_floats;   // floats of the split-partial region
@@ -189,6 +193,8 @@ struct hisparse_pool {
   int16_t* posmap;
   int64_t* map_off;
   int2* fetch;
+  int32_t* pf_miss_count;               // prefetch miss lists, apart from the step's own (a prefetch
+  int2* pf_fetch;                       // runs while the step's fetch may still read those)
   uint64_t* host_rows_d;
   unsigned char** kv_d;
   float* kv_scale_d;
@@ -200,6 +206,7 @@ struct hisparse_pool {
   // priority) while the caller's stream decodes earlier layers.
   hipStream_t fetch_stream = nullptr;
   hipEvent_t ev_meta = nullptr;
+  hipEvent_t ev_prefetch = nullptr;     // end of the in-step prefetch on the side stream
   std::vector<hipEvent_t> ev_fetch;  // one per pipelined unit of an index-share group
   int fetch_wg_all = hs::kDefaultGroupFetchWorkgroups;   // workgroups of a whole-group fetch
   int fetch_wg_unit = hs::kDefaultUnitFetchWorkgroups;   // workgroups of a pipelined fetch

@@ -143,6 +143,8 @@ Layout make_layout(const hisparse_config* c) {
   L.last_t = off; off = align256(off + NL * R * 4);
   L.miss_count = off; off = align256(off + NL * R * 4);
   L.fetch = off; off = align256(off + NL * R * W * 8);
+  L.pf_miss_count = off; off = align256(off + NL * R * 4);
+  L.pf_fetch = off; off = align256(off + NL * R * W * 8);
   L.bt = off; off = align256(off + (size_t)bt_entries * 4);
   L.bt_off = off; off = align256(off + R * 4);
   L.ctx = off; off = align256(off + R * 4);
@@ -365,6 +367,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->last_t = (int32_t*)(w + lay.last_t);
   p->miss_count = (int32_t*)(w + lay.miss_count);
   p->fetch = (int2*)(w + lay.fetch);
+  p->pf_miss_count = (int32_t*)(w + lay.pf_miss_count);
+  p->pf_fetch = (int2*)(w + lay.pf_fetch);
   p->bt = (int32_t*)(w + lay.bt);
   p->bt_off = (int32_t*)(w + lay.bt_off);
   p->ctx_d = (int32_t*)(w + lay.ctx);
@@ -416,7 +420,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   // Side stream and events of the overlapped step (default priority).
   p->ev_fetch.assign(cfg->index_share - 1 + kMaxTailChunks, nullptr);
   if ((e = hipStreamCreateWithFlags(&p->fetch_stream, hipStreamNonBlocking)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&p->ev_meta, hipEventDisableTiming)) != hipSuccess) {
+      (e = hipEventCreateWithFlags(&p->ev_meta, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&p->ev_prefetch, hipEventDisableTiming)) != hipSuccess) {
     hisparse_destroy_pool(p);
     return hip_fail(e, "stream/event creation");
   }
@@ -437,6 +442,7 @@ void hisparse_destroy_pool(hisparse_pool* p) {
   for (hipEvent_t e : p->ev_fetch)
     if (e) (void)hipEventDestroy(e);
   if (p->ev_meta) (void)hipEventDestroy(p->ev_meta);
+  if (p->ev_prefetch) (void)hipEventDestroy(p->ev_prefetch);
   if (p->fetch_stream) (void)hipStreamDestroy(p->fetch_stream);
   for (void* h : p->host_alloc)
     if (h) (void)hipHostFree(h);
@@ -478,9 +484,13 @@ hisparse_status hisparse_set_block_table(hisparse_pool* p, int32_t r, const int3
 }
 
 namespace {
+// prefetch: the metadata pass of a prefetch (d_rows unused, d_counts
+// [n_layers][R][4] or NULL, miss lists in the prefetch arrays).
 hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const int32_t* d_step,
-                                const int32_t* d_topk, int32_t* d_rows, int32_t* d_counts, hipStream_t s) {
+                                const int32_t* d_topk, int32_t* d_rows, int32_t* d_counts, hipStream_t s,
+                                bool prefetch = false) {
   ResolveArgs a;
+  a.prefetch = prefetch ? 1 : 0;
   a.step = d_step;
   a.topk = d_topk;
   a.rows = d_rows;
@@ -489,8 +499,8 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.stamp = p->stamp;
   a.lru = p->lru;
   a.last_t = p->last_t;
-  a.miss_count = p->miss_count + (size_t)layer_begin * p->cfg.num_requests;
-  a.fetch = p->fetch + (size_t)layer_begin * p->cfg.num_requests * p->W;
+  a.miss_count = (prefetch ? p->pf_miss_count : p->miss_count) + (size_t)layer_begin * p->cfg.num_requests;
+  a.fetch = (prefetch ? p->pf_fetch : p->fetch) + (size_t)layer_begin * p->cfg.num_requests * p->W;
   a.bt = p->bt;
   a.bt_off = p->bt_off;
   a.ctx = p->ctx_d;
@@ -518,11 +528,11 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
 // n_layers) (nreq < R only with one layer): their miss lists, stored per
 // (layer, request) by the metadata kernel, are copied from the host pool.
 hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers, int32_t r0, int32_t nreq, int grid,
-                              hipStream_t s) {
+                              hipStream_t s, bool prefetch = false) {
   const int R = p->cfg.num_requests;
   FetchArgs f;
-  f.miss_count = p->miss_count + (size_t)layer * R + r0;
-  f.fetch = p->fetch + ((size_t)layer * R + r0) * p->W;
+  f.miss_count = (prefetch ? p->pf_miss_count : p->miss_count) + (size_t)layer * R + r0;
+  f.fetch = (prefetch ? p->pf_fetch : p->fetch) + ((size_t)layer * R + r0) * p->W;
   f.host_rows = p->host_rows_d;
   f.kv = p->kv_d;
   f.layer_begin = layer;
@@ -670,15 +680,20 @@ hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* p, int32
                             d_out, d_lse, stream, true);
 }
 
-hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,
-                              float scale, int32_t* d_rows, int32_t* d_counts, float* d_out, float* d_lse,
-                              void* stream) {
+namespace {
+// One decode step (hisparse_step); with d_next, also the prefetch of the
+// predicted next selections on the side stream, behind the step's own
+// fetches and beside its decodes (hisparse_step_prefetch).
+hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk,
+                          const int32_t* d_next, const uint16_t* d_q, float scale, int32_t* d_rows,
+                          int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts, void* stream) {
+  const std::string f(fn);
   if (!p || !d_step || !d_topk || !d_q || !d_rows || !d_counts || !d_out || !d_lse) {
-    set_error("hisparse_step: NULL argument");
+    set_error(f + ": NULL argument");
     return HISPARSE_EINVAL;
   }
   if ((uintptr_t)d_q % 16 || !std::isfinite(scale)) {
-    set_error("hisparse_step: d_q must be 16-byte aligned and scale finite");
+    set_error(f + ": d_q must be 16-byte aligned and scale finite");
     return HISPARSE_EINVAL;
   }
   const auto& c = p->cfg;
@@ -688,6 +703,7 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
   hipStream_t s = (hipStream_t)stream;
   hipStream_t fs = p->fetch_stream;
   const int C = std::min<int>(p->tail_chunks, (int)R);
+  const bool pf = d_next != nullptr;
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
@@ -703,17 +719,22 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
                                          d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
     if (G == 1 && C == 1) {
-      // One layer, one unit: nothing to overlap, so no fork; the fetch takes
-      // the whole-group launch shape.
+      // One layer, one unit: its fetch and decode have nothing to overlap,
+      // so they run on `stream` with the whole-group fetch shape; a
+      // prefetch forks off after the fetch.
       const size_t pr = (size_t)l0 * R * T;  // first query set of the layer
       if ((st = enqueue_fetch(p, l0, 1, 0, (int)R, p->fetch_wg_all, s))) return st;
+      if (pf && g + 1 == c.num_layers / G) {
+        if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
+          return hip_fail(e, (f + ": fork").c_str());
+      }
       st = enqueue_decode(p, l0, 1, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
                           d_out + pr * H * kVDim, d_lse + pr * H, s);
       if (st) return st;
       continue;
     }
     if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
-      return hip_fail(e, "hisparse_step: fork");
+      return hip_fail(e, (f + ": fork").c_str());
     struct Unit {
       int layer, r0, nreq, splits;
     };
@@ -726,18 +747,72 @@ hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int
     }
     for (int u = 0; u < nu; ++u) {
       if ((st = enqueue_fetch(p, units[u].layer, 1, units[u].r0, units[u].nreq, p->fetch_wg_unit, fs))) return st;
-      if ((e = hipEventRecord(p->ev_fetch[u], fs)) != hipSuccess) return hip_fail(e, "hisparse_step: fetch event");
+      if ((e = hipEventRecord(p->ev_fetch[u], fs)) != hipSuccess) return hip_fail(e, (f + ": fetch event").c_str());
     }
     for (int u = 0; u < nu; ++u) {
       const Unit& un = units[u];
       const size_t pr = ((size_t)un.layer * R + un.r0) * T;  // first query set of the unit
-      if ((e = hipStreamWaitEvent(s, p->ev_fetch[u], 0)) != hipSuccess) return hip_fail(e, "hisparse_step: join");
+      if ((e = hipStreamWaitEvent(s, p->ev_fetch[u], 0)) != hipSuccess) return hip_fail(e, (f + ": join").c_str());
       st = enqueue_decode(p, un.layer, 1, (int)(un.nreq * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
                           d_out + pr * H * kVDim, d_lse + pr * H, s, un.splits);
       if (st) return st;
     }
   }
+  if (!pf) return HISPARSE_OK;
+  // Prefetch of the predicted next selections: on the side stream, after
+  // every fetch of this step (the host link stays busy), beside the
+  // decodes still running on `stream`.  It writes only the hot rows of
+  // slots this step did not touch and its own miss lists, so it races with
+  // nothing the step reads.  `stream` waits for it at the end, which also
+  // joins the fork for graph capture.
+  for (int g = 0; g < c.num_layers / G; ++g) {
+    const int l0 = g * G;
+    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_next + (size_t)g * R * W, nullptr,
+                                         d_pf_counts ? d_pf_counts + (size_t)l0 * R * 4 : nullptr, fs, true);
+    if (st) return st;
+    if ((st = enqueue_fetch(p, l0, G, 0, (int)R, p->fetch_wg_unit, fs, true))) return st;
+  }
+  if ((e = hipEventRecord(p->ev_prefetch, fs)) != hipSuccess || (e = hipStreamWaitEvent(s, p->ev_prefetch, 0)) != hipSuccess)
+    return hip_fail(e, (f + ": prefetch join").c_str());
   return HISPARSE_OK;
+}
+}  // namespace
+
+hisparse_status hisparse_step(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk, const uint16_t* d_q,
+                              float scale, int32_t* d_rows, int32_t* d_counts, float* d_out, float* d_lse,
+                              void* stream) {
+  return step_impl("hisparse_step", p, d_step, d_topk, nullptr, d_q, scale, d_rows, d_counts, d_out, d_lse, nullptr,
+                   stream);
+}
+
+hisparse_status hisparse_step_prefetch(hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk,
+                                       const int32_t* d_topk_next, const uint16_t* d_q, float scale, int32_t* d_rows,
+                                       int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts,
+                                       void* stream) {
+  if (!d_topk_next) {
+    set_error("hisparse_step_prefetch: d_topk_next is NULL");
+    return HISPARSE_EINVAL;
+  }
+  return step_impl("hisparse_step_prefetch", p, d_step, d_topk, d_topk_next, d_q, scale, d_rows, d_counts, d_out,
+                   d_lse, d_pf_counts, stream);
+}
+
+hisparse_status hisparse_prefetch(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, const int32_t* d_step,
+                                  const int32_t* d_topk, int32_t* d_counts, void* stream) {
+  if (!p || !d_step || !d_topk) {
+    set_error("hisparse_prefetch: NULL argument");
+    return HISPARSE_EINVAL;
+  }
+  const int g = p->cfg.index_share;
+  if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > p->cfg.num_layers ||
+      layer_begin / g != (layer_begin + n_layers - 1) / g) {
+    set_error("hisparse_prefetch: layers must lie inside one index-share group");
+    return HISPARSE_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hisparse_status st = enqueue_resolve(p, layer_begin, n_layers, d_step, d_topk, nullptr, d_counts, s, true);
+  if (st) return st;
+  return enqueue_fetch(p, layer_begin, n_layers, 0, p->cfg.num_requests, p->fetch_wg_all, s, true);
 }
 
 hisparse_status hisparse_reset_state(hisparse_pool* p, void* stream) {

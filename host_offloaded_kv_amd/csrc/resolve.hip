@@ -193,17 +193,27 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   const int page_mask = (1 << page_shift) - 1;
 
   if (t < 0 || t < last) {
-    for (int j = tid; j < K; j += kMetaThreads) rows_out[j] = -1;
+    if (!a.prefetch)
+      for (int j = tid; j < K; j += kMetaThreads) rows_out[j] = -1;
     if (tid == 0) {
-      a.counts[cpair * 3 + 0] = 0;
-      a.counts[cpair * 3 + 1] = 0;
-      a.counts[cpair * 3 + 2] = 0;
+      if (a.prefetch) {
+        if (a.counts)
+          for (int i = 0; i < 4; ++i) a.counts[cpair * 4 + i] = 0;
+      } else {
+        a.counts[cpair * 3 + 0] = 0;
+        a.counts[cpair * 3 + 1] = 0;
+        a.counts[cpair * 3 + 2] = 0;
+      }
       a.miss_count[cpair] = 0;
       atomicOr(a.err, HISPARSE_ERR_STEP);
     }
     return;
   }
   const bool same_step = t == last;
+  // A prefetch leaves every slot stamped t alone (the running step's
+  // selection, and earlier fills of this step), as well as its own hits.
+  const bool pf = a.prefetch != 0;
+  const int pin_mask = pf ? 3 : 1;
 
   int32_t* owner_g = a.owner + pair * B;
   int32_t* stamp_g = a.stamp + pair * B;
@@ -308,8 +318,8 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
           ++n_res;
         } else if (sv[c] >= 0) {
           const int s = sv[c];
-          if (a.policy == HISPARSE_POLICY_FIFO) {
-            tflag_s[s] |= 1;  // pinned; the fill stamp stays
+          if (pf || a.policy == HISPARSE_POLICY_FIFO) {
+            tflag_s[s] |= 1;  // pinned; the stamp stays (FIFO: fill step; prefetch: a guess refreshes nothing)
           } else {
             tflag_s[s] |= 5;
             stamp_g[s] = t;
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
           miss = true;
         }
       }
-      if (!miss) rows_out[j] = row;
+      if (!miss && !pf) rows_out[j] = row;
     }
     mb[c] = __ballot(miss);
     mloc += __popcll(mb[c]);
@@ -349,6 +359,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     bitonic_sort(key_s, mp, tid);
   }
 
+  int unpinned = 0;  // slots a fill may take
   if (a.policy == HISPARSE_POLICY_RANDOM) {
     // Victims: empty slots by index, then ascending (priority, slot); the
     // priority of slot s is the top 31 bits of SplitMix64(k ^ s) with k
@@ -356,17 +367,22 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     const uint64_t k = splitmix64(splitmix64(splitmix64(a.policy_seed) ^ (uint64_t)(uint32_t)t) ^
                                   (((uint64_t)(uint32_t)l << 32) | (uint32_t)r));
     const int BP = next_pow2(B);
+    int uloc = 0;
     for (int i = tid; i < BP; i += kMetaThreads) {
       unsigned long long key = ~0ull;
-      if (i < B && !(tflag_s[i] & 1)) {
+      if (i < B && !(tflag_s[i] & pin_mask)) {
+        ++uloc;
         key = owner_g[i] < 0 ? (unsigned long long)i
                              : ((1ull << 63) | ((splitmix64(k ^ (uint64_t)i) >> 33) << 32) | (uint32_t)i);
       }
       rkey_s[i] = key;
     }
+    uloc = wave_sum(uloc);
+    if (lane == 0) cnt_s[1][wid] = uloc;
     __syncthreads();
+    wave_base(cnt_s[1], wid, &unpinned);
     bitonic_sort(rkey_s, BP, tid);
-    for (int i = tid; i < m; i += kMetaThreads) vic_s[i] = (int)(uint32_t)rkey_s[i];
+    for (int i = tid; i < m && i < unpinned; i += kMetaThreads) vic_s[i] = (int)(uint32_t)rkey_s[i];
   } else {
     // Victims: the first m unpinned slots of the (stamp, slot) order array.
     uint64_t vb[BC];
@@ -374,13 +390,12 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
 #pragma unroll
     for (int c = 0; c < BC; ++c) {
       const int i = ib + 64 * c + lane;
-      const bool cand = c < nsc && i < ie && (tflag_s[lv[c]] & 1) == 0;
+      const bool cand = c < nsc && i < ie && (tflag_s[lv[c]] & pin_mask) == 0;
       vb[c] = __ballot(cand);
       uloc += __popcll(vb[c]);
     }
     if (lane == 0) cnt_s[1][wid] = uloc;
     __syncthreads();
-    int unpinned;
     int run = wave_base(cnt_s[1], wid, &unpinned);
 #pragma unroll
     for (int c = 0; c < BC; ++c) {
@@ -392,6 +407,10 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     }
   }
   __syncthreads();
+  // A RESOLVE always has a victim per miss (B >= the selection width); a
+  // prefetch fills what the free slots hold and drops the largest positions.
+  const int m_all = m;
+  m = min(m, unpinned);
 
   // Fill: i-th smallest missing position -> i-th victim.  The evicted
   // position cannot be in this selection (its slot would be pinned), so the
@@ -406,11 +425,11 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     owner_g[v] = p;
     stamp_g[v] = t;
     tflag_s[v] |= 5;
-    rows_out[j] = (int)(hot_base + v);
+    if (!pf) rows_out[j] = (int)(hot_base + v);
     fetch[i] = make_int2(p, v);
   }
   __syncthreads();  // also makes every row id written above visible to the workgroup
-  if (!fast) {
+  if (!fast && !pf) {
     // Entries that repeat a position of an earlier verify token take its row.
     for (int j = tid; j < K; j += kMetaThreads) {
       const int p = sel_s[j];
@@ -466,9 +485,18 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
       tr += red_s[0][w2];
       th += red_s[1][w2];
     }
-    a.counts[cpair * 3 + 0] = tr;
-    a.counts[cpair * 3 + 1] = th;
-    a.counts[cpair * 3 + 2] = m;
+    if (pf) {
+      if (a.counts) {
+        a.counts[cpair * 4 + 0] = tr;
+        a.counts[cpair * 4 + 1] = th;
+        a.counts[cpair * 4 + 2] = m;
+        a.counts[cpair * 4 + 3] = m_all - m;
+      }
+    } else {
+      a.counts[cpair * 3 + 0] = tr;
+      a.counts[cpair * 3 + 1] = th;
+      a.counts[cpair * 3 + 2] = m;
+    }
     a.miss_count[cpair] = m;
     a.last_t[pair] = t;
   }

@@ -57,7 +57,7 @@ EXPORTED = (
     "hisparse_create_pool", "hisparse_destroy_pool", "hisparse_host_rows",
     "hisparse_set_block_table", "hisparse_resolve", "hisparse_sparse_mla_decode",
     "hisparse_sparse_mla_decode_layers", "hisparse_sparse_mla_decode_layers_static",
-    "hisparse_step", "hisparse_reset_state", "hisparse_set_pipeline",
+    "hisparse_step", "hisparse_step_prefetch", "hisparse_prefetch", "hisparse_reset_state", "hisparse_set_pipeline",
     "hisparse_append", "hisparse_writeback", "hisparse_set_pages", "hisparse_get_lengths",
     "hisparse_set_replacement",
     "hisparse_export_state", "hisparse_check_errors", "hisparse_decode_fallback_count",
@@ -126,6 +126,8 @@ def load() -> ctypes.CDLL:
         "hisparse_sparse_mla_decode_layers_static": (_I32, [_VP, _I32, _I32, _VP, _VP, ctypes.c_float, _VP, _VP,
                                                             _VP]),
         "hisparse_step": (_I32, [_VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP]),
+        "hisparse_step_prefetch": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "hisparse_prefetch": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
         "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32]),
         "hisparse_append": (_I32, [_VP, _VP, _VP]),
@@ -245,6 +247,16 @@ def hisparse_sparse_mla_decode_layers_static(pool, layer_begin, n_layers, d_q, d
 
 def hisparse_step(pool, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse, stream) -> None:
     _check(load().hisparse_step(pool, d_step, d_topk, d_q, float(scale), d_rows, d_counts, d_out, d_lse, stream))
+
+
+def hisparse_step_prefetch(pool, d_step, d_topk, d_topk_next, d_q, scale, d_rows, d_counts, d_out, d_lse,
+                           d_pf_counts, stream) -> None:
+    _check(load().hisparse_step_prefetch(pool, d_step, d_topk, d_topk_next, d_q, float(scale), d_rows, d_counts,
+                                         d_out, d_lse, d_pf_counts, stream))
+
+
+def hisparse_prefetch(pool, layer_begin, n_layers, d_step, d_topk, d_counts, stream) -> None:
+    _check(load().hisparse_prefetch(pool, layer_begin, n_layers, d_step, d_topk, d_counts, stream))
 
 
 def hisparse_reset_state(pool: int, stream: int) -> None:
@@ -396,6 +408,16 @@ class HiSparse:
     def step(self, d_step, d_topk, d_q, scale, d_rows, d_counts, d_out, d_lse) -> None:
         hisparse_step(self.pool, d_step.data_ptr(), d_topk.data_ptr(), d_q.data_ptr(), scale,
                       d_rows.data_ptr(), d_counts.data_ptr(), d_out.data_ptr(), d_lse.data_ptr(), self.stream)
+
+    def step_prefetch(self, d_step, d_topk, d_topk_next, d_q, scale, d_rows, d_counts, d_out, d_lse,
+                      d_pf_counts=None) -> None:
+        hisparse_step_prefetch(self.pool, d_step.data_ptr(), d_topk.data_ptr(), d_topk_next.data_ptr(), d_q.data_ptr(),
+                               scale, d_rows.data_ptr(), d_counts.data_ptr(), d_out.data_ptr(), d_lse.data_ptr(),
+                               d_pf_counts.data_ptr() if d_pf_counts is not None else None, self.stream)
+
+    def prefetch(self, layer_begin, n_layers, d_step, d_topk, d_counts=None) -> None:
+        hisparse_prefetch(self.pool, layer_begin, n_layers, d_step.data_ptr(), d_topk.data_ptr(),
+                          d_counts.data_ptr() if d_counts is not None else None, self.stream)
 
     def reset_state(self) -> None:
         hisparse_reset_state(self.pool, self.stream)

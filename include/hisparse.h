@@ -283,6 +283,48 @@ hisparse_status hisparse_step(hisparse_pool* pool, const int32_t* d_step, const 
                               const uint16_t* d_q, float scale, int32_t* d_rows, int32_t* d_counts,
                               float* d_out, float* d_lse, void* stream);
 
+/* ---- cross-step prefetch (HiSparse summary article, sections 03-04:
+ * fetching the rows a coming step will select before it asks for them
+ * hides host I/O; a selection the model provides beats speculation) ----
+ * The pages give the effect, not the mechanism.  Reading: a prefetch issued
+ * during step t with a predicted selection S' (same layout as d_topk)
+ * leaves every slot stamped t alone (the running step's selection, which
+ * its attention may still read, and earlier fills of this step) and every
+ * slot holding a position of S' (pinned, stamp unchanged); the positions of
+ * S' neither resident nor in the buffer are filled, smallest first, into
+ * the remaining slots in the policy's victim order, with stamp t, and
+ * fetched from the host pool; misses beyond the free slots are dropped
+ * (largest positions first).  No row ids are produced: the coming step's
+ * RESOLVE finds the filled rows as hits.  With the exact next selection and
+ * room for its misses, the next step has no miss and the same rows and
+ * state as without prefetch.  Range and repeat errors set the same flags as
+ * RESOLVE; a step index below the last one seen sets HISPARSE_ERR_STEP and
+ * prefetches nothing. */
+
+/* Prefetch S' into layers [layer_begin, layer_begin + n_layers) (one
+ * index-share group) during the step whose index d_step holds.
+ *   d_topk:   device int32 [R][T*K] predicted selection.
+ *   d_counts: device int32 [n_layers][R][4] out, or NULL: (resident, hit,
+ *             filled, dropped) per (layer, request).
+ * Enqueues the metadata kernel and the fetch of the filled rows on
+ * `stream`; the prefetch keeps its own miss lists, so it may overlap a
+ * fetch of the running step.  Errors: EINVAL. */
+hisparse_status hisparse_prefetch(hisparse_pool* pool, int32_t layer_begin, int32_t n_layers, const int32_t* d_step,
+                                  const int32_t* d_topk, int32_t* d_counts, void* stream);
+
+/* hisparse_step, followed by the prefetch of d_topk_next ([L/g][R][T*K],
+ * the predicted selections of the next step) into every layer: the prefetch
+ * runs on the pool's side stream after all of this step's miss fetches and
+ * beside its decodes, and `stream` waits for it before the call's work
+ * ends (graph-capturable like hisparse_step).  d_pf_counts: device int32
+ * [L][R][4] out, or NULL (as hisparse_prefetch's d_counts).  Row ids,
+ * counts, O and lse of this step are those of hisparse_step.
+ * Errors: EINVAL. */
+hisparse_status hisparse_step_prefetch(hisparse_pool* pool, const int32_t* d_step, const int32_t* d_topk,
+                                       const int32_t* d_topk_next, const uint16_t* d_q, float scale, int32_t* d_rows,
+                                       int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts,
+                                       void* stream);
+
 /* Return every (request, layer) to the empty state (owner -1, stamp -1,
  * no step seen) and every context to its length at creation (host pool
  * held up to that length); block tables and host rows are kept.  Waits for
