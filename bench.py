@@ -274,6 +274,7 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph replay of the same steps")
     ap.add_argument("--no-decode-only", action="store_true", help="skip the decode-only timing")
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
+    ap.add_argument("--no-prefetch", action="store_true", help="skip the cross-step prefetch runs")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
     ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
     ap.add_argument("--num-verify", type=int, default=1,
@@ -326,7 +327,7 @@ def main() -> int:
 
     log(f"workload {w.name}: R={R} L={L} g={w.index_share} ctx={w.ctx_len[0]} H={Hh} K={K} B={B}")
     t0 = time.time()
-    trace = w.trace(n_steps)
+    trace = w.trace(n_steps + 1)  # one step past the timed ones: the prediction of the last step
     if args.unsorted:
         rng = np.random.default_rng(2024)
         trace = trace.copy()
@@ -454,6 +455,59 @@ def main() -> int:
         log("synchronous path (resolve, then per-layer decode, one stream)")
         sync_ms = time_steps(sync_step)
         log(f"synchronous path: {sync_ms / args.steps * 1e3:.1f} us/step")
+
+    # 2b) cross-step prefetch (graph replays of hisparse_step_prefetch): the
+    #     true next selection (the model-provided signal of the HiSparse
+    #     summary article, section 04) and the current one reused (speculation
+    #     that the selection does not move)
+    prefetch = None
+    if not args.no_prefetch:
+        prefetch = {}
+        pf_counts = torch.zeros((n_steps, L, R, 4), dtype=torch.int32, device=dev)
+        for kind in ("exact_next", "reuse_current"):
+            log(f"prefetch run ({kind})")
+            side = torch.cuda.Stream(device=dev)
+            hs.reset_state()
+            side.wait_stream(stream)
+            graphs = []
+            for t in range(n_steps):
+                nxt = d_topk[t + 1] if kind == "exact_next" else d_topk[t]
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    H.hisparse_step_prefetch(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(),
+                                             nxt.data_ptr(), d_q[t].data_ptr(), w.scale, d_rows[t].data_ptr(),
+                                             d_counts[t].data_ptr(), d_out.data_ptr(), d_lse.data_ptr(),
+                                             pf_counts[t].data_ptr(), side.cuda_stream)
+                graphs.append(g)
+            torch.cuda.synchronize(dev)
+            graph_pf_ms = time_steps(lambda t: graphs[t].replay())
+            del graphs
+
+            def eager_pf(t):
+                nxt = d_topk[t + 1] if kind == "exact_next" else d_topk[t]
+                H.hisparse_step_prefetch(hs.pool, d_steps[t:t + 1].data_ptr(), d_topk[t].data_ptr(), nxt.data_ptr(),
+                                         d_q[t].data_ptr(), w.scale, d_rows[t].data_ptr(), d_counts[t].data_ptr(),
+                                         d_out.data_ptr(), d_lse.data_ptr(), pf_counts[t].data_ptr(),
+                                         stream.cuda_stream)
+
+            eager_pf_ms = time_steps(eager_pf)
+            pf_ms = min(graph_pf_ms, eager_pf_ms)
+            own = d_counts[args.warmup:].cpu().numpy().astype(np.int64)[..., 2]  # [steps][L][R]
+            pfc = pf_counts[args.warmup:].cpu().numpy().astype(np.int64)
+            host_rows = own.sum() + pfc[..., 2].sum()
+            us = pf_ms / args.steps * 1e3
+            prefetch[kind] = {
+                "us_per_step": round(us, 2), "tokens_per_s": round(R * T * args.steps / (pf_ms * 1e-3), 2),
+                "graph_replay_us_per_step": round(graph_pf_ms / args.steps * 1e3, 2),
+                "eager_us_per_step": round(eager_pf_ms / args.steps * 1e3, 2),
+                "own_misses_per_step": round(float(own.sum()) / args.steps, 1),
+                "prefetched_rows_per_step": round(float(pfc[..., 2].sum()) / args.steps, 1),
+                "dropped_per_step": round(float(pfc[..., 3].sum()) / args.steps, 1),
+                "host_GBs_over_step": round(float(host_rows) * row_bytes / args.steps / (us * 1e-6) / 1e9, 2)}
+            log(f"prefetch {kind}: {prefetch[kind]}")
+        if hs.check_errors():
+            log("device error flags after the prefetch runs")
+            return 1
 
     # 3) decode alone: every layer of the last step, one launch per layer
     #    (default key splits), over rows that are already resident
@@ -597,7 +651,7 @@ def main() -> int:
     del hs
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        cpu = cpu_baseline(w, trace, args.warmup)
+        cpu = cpu_baseline(w, trace[:n_steps], args.warmup)
         log(f"cpu baseline: {cpu}")
 
     out = {
@@ -632,6 +686,7 @@ def main() -> int:
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
                         "sync_path_tokens_per_s": round(R * T * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
+        "prefetch": dict(prefetch, no_prefetch_us_per_step=round(ms_step * 1e3, 2)) if prefetch else None,
         "decode_only": {"alg_bytes": int(dec_bytes),
                         "per_group_launch": {"us_per_step": round(dec_us, 2), "launches": w.groups,
                                              "achieved_GBs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 2),

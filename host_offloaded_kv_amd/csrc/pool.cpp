@@ -681,9 +681,37 @@ hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* p, int32
 }
 
 namespace {
+// The prefetch part of hisparse_step_prefetch: for every index-share group,
+// the metadata pass over the predicted selection and the fetch of the filled
+// rows, on the side stream fs, then an event the caller's stream joins.
+hisparse_status enqueue_step_prefetch(hisparse_pool* p, const int32_t* d_step, const int32_t* d_next,
+                                      int32_t* d_pf_counts, hipStream_t fs) {
+  const auto& c = p->cfg;
+  const size_t R = c.num_requests, W = p->W;
+  const int G = c.index_share;
+  for (int g = 0; g < c.num_layers / G; ++g) {
+    const int l0 = g * G;
+    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_next + (size_t)g * R * W, nullptr,
+                                         d_pf_counts ? d_pf_counts + (size_t)l0 * R * 4 : nullptr, fs, true);
+    if (st) return st;
+    if ((st = enqueue_fetch(p, l0, G, 0, (int)R, p->fetch_wg_unit, fs, true))) return st;
+  }
+  hipError_t e = hipEventRecord(p->ev_prefetch, fs);
+  return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "prefetch event");
+}
+
 // One decode step (hisparse_step); with d_next, also the prefetch of the
 // predicted next selections on the side stream, behind the step's own
 // fetches and beside its decodes (hisparse_step_prefetch).
+//
+// The prefetch is enqueued on the side stream right after the last group's
+// own fetches and before that group's decodes.  It writes only the hot rows
+// of slots this step did not touch and its own miss lists, so it races with
+// nothing the step reads.  Enqueued in that order, a captured graph keeps
+// the prefetch on the fetches' chain (one queue) and the decodes on their
+// own: enqueued after the decodes, the prefetch became a third chain that a
+// graph launch queued ahead of the decodes, serialising them behind its
+// fetch.
 hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk,
                           const int32_t* d_next, const uint16_t* d_q, float scale, int32_t* d_rows,
                           int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts, void* stream) {
@@ -727,6 +755,7 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       if (pf && g + 1 == c.num_layers / G) {
         if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
           return hip_fail(e, (f + ": fork").c_str());
+        if ((st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, fs))) return st;
       }
       st = enqueue_decode(p, l0, 1, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
                           d_out + pr * H * kVDim, d_lse + pr * H, s);
@@ -749,6 +778,7 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       if ((st = enqueue_fetch(p, units[u].layer, 1, units[u].r0, units[u].nreq, p->fetch_wg_unit, fs))) return st;
       if ((e = hipEventRecord(p->ev_fetch[u], fs)) != hipSuccess) return hip_fail(e, (f + ": fetch event").c_str());
     }
+    if (pf && g + 1 == c.num_layers / G && (st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, fs))) return st;
     for (int u = 0; u < nu; ++u) {
       const Unit& un = units[u];
       const size_t pr = ((size_t)un.layer * R + un.r0) * T;  // first query set of the unit
@@ -758,21 +788,8 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       if (st) return st;
     }
   }
-  if (!pf) return HISPARSE_OK;
-  // Prefetch of the predicted next selections: on the side stream, after
-  // every fetch of this step (the host link stays busy), beside the
-  // decodes still running on `stream`.  It writes only the hot rows of
-  // slots this step did not touch and its own miss lists, so it races with
-  // nothing the step reads.  `stream` waits for it at the end, which also
-  // joins the fork for graph capture.
-  for (int g = 0; g < c.num_layers / G; ++g) {
-    const int l0 = g * G;
-    hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_next + (size_t)g * R * W, nullptr,
-                                         d_pf_counts ? d_pf_counts + (size_t)l0 * R * 4 : nullptr, fs, true);
-    if (st) return st;
-    if ((st = enqueue_fetch(p, l0, G, 0, (int)R, p->fetch_wg_unit, fs, true))) return st;
-  }
-  if ((e = hipEventRecord(p->ev_prefetch, fs)) != hipSuccess || (e = hipStreamWaitEvent(s, p->ev_prefetch, 0)) != hipSuccess)
+  // `stream` waits for the prefetch, which also joins the fork for capture.
+  if (pf && (e = hipStreamWaitEvent(s, p->ev_prefetch, 0)) != hipSuccess)
     return hip_fail(e, (f + ": prefetch join").c_str());
   return HISPARSE_OK;
 }
