@@ -27,22 +27,34 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, published
 
 
-def pmc_bytes(workload: str, kernel: str):
-    """Per-launch bytes of `kernel` from the committed PMC summary of this
-    workload, or None when there is none or the kernel's source changed."""
+def pmc_ratio(workload: str, kernel: str, host_link: bool):
+    """Counted bytes per algorithmic byte of `kernel` from the committed PMC
+    summary of this workload (reads only for the host-link-bound fetch, reads
+    plus writes otherwise), with the counted bytes per launch; None when there
+    is no summary or the kernel's source file changed since it was taken.
+    The counters come from other steps of the same trace than the timed
+    ones, so they are carried over as a ratio to the algorithmic bytes."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"pmc_bytes_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        e = json.load(f).get("kernels", {}).get(kernel)
-    if not e:
+        ks = json.load(f).get("kernels", {})
+    names = {"sparse_mla_decode": ["decode_ws_unsplit", "decode_ws_split"]}.get(kernel, [kernel])
+    es = [ks[n] for n in names if n in ks and "alg_bytes_per_launch" in ks[n]]
+    if not es:
         return None
-    with open(os.path.join(ROOT, e["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != e["source_sha256_16"]:
-            return None
-    return e
+    for e in es:
+        with open(os.path.join(ROOT, e["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != e["source_sha256_16"]:
+                return None
+    key = "read_per_alg_byte" if host_link else "traffic_per_alg_byte"
+    n = sum(e["launches"] for e in es)
+    ratio = sum(e[key] * e["launches"] for e in es) / n
+    rd = sum(e["read_bytes_per_launch"] * e["launches"] for e in es) / n
+    wr = sum(e["write_bytes_per_launch"] * e["launches"] for e in es) / n
+    return ratio, rd, wr
 
 
 def log(msg: str) -> None:
@@ -600,15 +612,18 @@ def main() -> int:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_full / HBM_PEAK_GBS, 4)}
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kern[dom]
-    pmc = pmc_bytes(w.name, dom)
+    pmc = pmc_ratio(w.name, dom, d["bound"] == "host_link") if T == 1 and args.kv_dtype == "bf16" else None
     traffic = None
-    if pmc is not None:
-        # the host-link side of the fetch is what it reads; other kernels: reads + writes
-        traffic = pmc["read_bytes_per_launch"] if d["bound"] == "host_link" else pmc["traffic_bytes_per_launch"]
+    if pmc is not None and d["alg_bytes_per_launch"]:
+        # counted bytes of the timed launches: the counters' ratio to the
+        # algorithmic bytes (host-link side: reads) times the timed launches'
+        # algorithmic bytes
+        traffic = int(pmc[0] * d["alg_bytes_per_launch"])
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
                 "frac": d["frac"], "traffic": traffic, "kernel": dom, "avg_us": d["avg_us"],
                 "alg_bytes_per_launch": d["alg_bytes_per_launch"],
-                "traffic_read_write": [pmc["read_bytes_per_launch"], pmc["write_bytes_per_launch"]] if pmc else None}
+                "traffic_per_alg_byte": round(pmc[0], 4) if pmc else None,
+                "counted_read_write_per_launch_pmc_steps": [int(pmc[1]), int(pmc[2])] if pmc else None}
 
     residency = None
     if not args.no_residency:
