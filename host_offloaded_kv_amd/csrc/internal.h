@@ -222,7 +222,7 @@ void prof_begin(hisparse_pool* p, int kid, hipStream_t s);
 void prof_end(hisparse_pool* p, hipStream_t s);
 
 // resolve.hip
-size_t resolve_lds_bytes(int selection_width, int hot_slots, bool random_policy);
+size_t resolve_lds_bytes(int selection_width, int hot_slots, bool random_policy, bool one_token);
 hipError_t launch_workspace_init(hisparse_pool* p, hipStream_t s);
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s);
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s);

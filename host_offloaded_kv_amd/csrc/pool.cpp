@@ -305,7 +305,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     delete p;
     return hip_fail(e, "hipGetSymbolAddress(static split scratch)");
   }
-  p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots, false);
+  p->resolve_lds = resolve_lds_bytes(p->W, cfg->hot_slots, false, p->T == 1);
   int max_lds = 0;
   e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
   if (e != hipSuccess) {
@@ -321,7 +321,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   }
   {
     // allow the largest metadata launch of any policy that fits the device
-    const size_t lds_random = resolve_lds_bytes(p->W, cfg->hot_slots, true);
+    const size_t lds_random = resolve_lds_bytes(p->W, cfg->hot_slots, true, p->T == 1);
     const size_t lim = lds_random <= (size_t)max_lds ? lds_random : p->resolve_lds;
     if (lim > 65536 && (e = set_resolve_lds_limit(p->device, lim)) != hipSuccess) {
       delete p;
@@ -954,7 +954,7 @@ hisparse_status hisparse_set_replacement(hisparse_pool* p, int32_t policy, uint6
   }
   if (policy == HISPARSE_POLICY_RANDOM) {
     // random replacement sorts the unpinned slots in LDS beside the miss list
-    const size_t need = resolve_lds_bytes(p->W, p->cfg.hot_slots, true);
+    const size_t need = resolve_lds_bytes(p->W, p->cfg.hot_slots, true, p->T == 1);
     if (need > (size_t)p->max_lds) {
       set_error("hisparse_set_replacement: random replacement needs " + std::to_string(need) +
                 " bytes of LDS at this selection width and slot count, the device allows " +

@@ -62,13 +62,18 @@ int ceil_log2(int64_t v) {
 
 constexpr int kMetaThreads = 1024;  // 16 wavefronts per (request, layer)
 constexpr int kMetaWaves = kMetaThreads / 64;
+constexpr int kSelChunksMax = kMaxTopK / kMetaThreads;  // entries per thread of a one-token selection
 
 // LDS of one metadata workgroup: the selection (W int32), the sort and
 // miss-list region (W 64-bit keys, a power of two), the victims (W int32),
-// one pin byte per slot, and for random replacement a second key region of
-// B entries (the misses stay in the first while the victims are sorted).
+// one pin byte per slot, and an auxiliary region used at two different
+// times: the hash table that finds repeated positions of a one-token
+// selection in input order (2 W' int32 positions and 2 W' int32 earliest
+// entries, W' = W rounded up to a power of two), and, for random
+// replacement, B 64-bit keys (the misses stay in the key region while the
+// victims are sorted).
 struct LdsMap {
-  size_t sel, key, vic, tflag, rkey, total;
+  size_t sel, key, vic, tflag, aux, total;
 };
 
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -79,14 +84,18 @@ __host__ __device__ inline int next_pow2(int v) {
   return p;
 }
 
-__host__ __device__ inline LdsMap lds_map(int W, int B, bool random) {
+__host__ __device__ inline size_t hash_entries(int W) { return 2 * (size_t)next_pow2(W); }
+
+__host__ __device__ inline LdsMap lds_map(int W, int B, bool random, bool one_token) {
   LdsMap m;
   m.sel = 0;
   m.key = round16(m.sel + 4 * (size_t)W);
   m.vic = m.key + 8 * (size_t)next_pow2(W);
   m.tflag = round16(m.vic + 4 * (size_t)W);
-  m.rkey = round16(m.tflag + (size_t)B);
-  m.total = m.rkey + (random ? 8 * (size_t)next_pow2(B) : 0);
+  m.aux = round16(m.tflag + (size_t)B);
+  const size_t hash = one_token ? 8 * hash_entries(W) : 0;
+  const size_t rkey = random ? 8 * (size_t)next_pow2(B) : 0;
+  m.total = m.aux + (hash > rkey ? hash : rkey);
   return m;
 }
 
@@ -167,12 +176,13 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   __shared__ int cnt_s[2][kMetaWaves];
   __shared__ int red_s[2][kMetaWaves];
   const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
-  const LdsMap M = lds_map(K, B, a.policy == HISPARSE_POLICY_RANDOM);
+  const bool one_token = a.tok_k == K;
+  const LdsMap M = lds_map(K, B, a.policy == HISPARSE_POLICY_RANDOM, one_token);
   int32_t* sel_s = (int32_t*)(smem + M.sel);
   unsigned long long* key_s = (unsigned long long*)(smem + M.key);  // sort region, then the miss list
   int32_t* vic_s = (int32_t*)(smem + M.vic);
   unsigned char* tflag_s = smem + M.tflag;
-  unsigned long long* rkey_s = (unsigned long long*)(smem + M.rkey);
+  unsigned long long* rkey_s = (unsigned long long*)(smem + M.aux);
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,7 +274,47 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   const bool fast = __syncthreads_or(bad) == 0;
   const int KP = next_pow2(K);
 
-  if (!fast) {
+  if (!fast && one_token) {
+    // Repeated positions of a one-token selection: an LDS hash table keyed
+    // by position (open addressing over twice the width, so every position
+    // finds a slot) keeps the earliest entry of each position; every later
+    // entry is an error and becomes padding.
+    const int HN = (int)hash_entries(K);
+    int* hpos = (int*)(smem + M.aux);
+    int* hidx = hpos + HN;
+    for (int i = tid; i < HN; i += kMetaThreads) {
+      hpos[i] = -1;
+      hidx[i] = INT_MAX;
+    }
+    __syncthreads();
+    int hs[kSelChunksMax];
+#pragma unroll
+    for (int c = 0; c < kSelChunksMax; ++c) {
+      const int j = tid + c * kMetaThreads;
+      hs[c] = -1;
+      const int p = j < K ? sel_s[j] : -1;
+      if (p >= 0) {
+        int h = (int)(((uint32_t)p * 0x9E3779B1u) & (uint32_t)(HN - 1));
+        for (int probe = 0; probe < HN; ++probe) {
+          const int old = atomicCAS(&hpos[h], -1, p);
+          if (old == -1 || old == p) break;
+          h = (h + 1) & (HN - 1);
+        }
+        atomicMin(&hidx[h], j);
+        hs[c] = h;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kSelChunksMax; ++c) {
+      const int j = tid + c * kMetaThreads;
+      if (hs[c] >= 0 && hidx[hs[c]] != j) {
+        sel_s[j] = -1;
+        errbits |= HISPARSE_ERR_DUP;
+      }
+    }
+    __syncthreads();
+  } else if (!fast) {
     // Repeated positions: sort (position, index); the earliest index of
     // each position is the one resolved.  A later entry in the same
     // verify token's list as the entry before it is an error (padding); an
@@ -351,8 +401,19 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   }
   __syncthreads();
 
-  if (!fast && m > 1) {
-    // Ascending position order of the misses.
+  if (!fast && m > 1 && m <= kMetaThreads) {
+    // Ascending position order of the misses: thread i counts the keys
+    // below miss i (the keys are distinct; every thread reads the same key
+    // at a time, an LDS broadcast), then writes it at that rank.
+    const unsigned long long x = tid < m ? key_s[tid] : 0ull;
+    int rank = 0;
+    if (tid < m)
+      for (int i = 0; i < m; ++i) rank += key_s[i] < x ? 1 : 0;
+    __syncthreads();
+    if (tid < m) key_s[rank] = x;
+    __syncthreads();
+  } else if (!fast && m > 1) {
+    // more misses than threads: bitonic sort
     const int mp = next_pow2(m);
     for (int i = m + tid; i < mp; i += kMetaThreads) key_s[i] = ~0ull;
     __syncthreads();
@@ -629,7 +690,9 @@ __global__ __launch_bounds__(kCopyThreads) void gather16(u32x4* __restrict__ dst
 
 }  // namespace
 
-size_t resolve_lds_bytes(int top_k, int hot_slots, bool random) { return lds_map(top_k, hot_slots, random).total; }
+size_t resolve_lds_bytes(int width, int hot_slots, bool random, bool one_token) {
+  return lds_map(width, hot_slots, random, one_token).total;
+}
 
 hipError_t launch_state_reset(hisparse_pool* p, hipStream_t s) {
   const auto& c = p->cfg;
@@ -666,7 +729,7 @@ static_assert(kSelChunksLarge * kMetaThreads == kMaxSelection && kSlotChunksLarg
               "whole chunks per wave");
 
 hipError_t launch_meta(hisparse_pool* p, const ResolveArgs& a, hipStream_t s) {
-  const size_t lds = lds_map(a.top_k, a.hot_slots, a.policy == HISPARSE_POLICY_RANDOM).total;
+  const size_t lds = lds_map(a.top_k, a.hot_slots, a.policy == HISPARSE_POLICY_RANDOM, a.tok_k == a.top_k).total;
   const dim3 grid(a.n_layers * a.num_requests), block(kMetaThreads);
   const bool small_sel = a.top_k <= kSelChunksSmall * kMetaThreads;
   const bool small_slots = a.hot_slots <= kSlotChunksSmall * kMetaThreads;
