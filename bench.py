@@ -287,6 +287,8 @@ def main() -> int:
     ap.add_argument("--no-decode-only", action="store_true", help="skip the decode-only timing")
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the cross-step prefetch runs")
+    ap.add_argument("--no-resident-first", action="store_true",
+                    help="decode each group's last layer in one launch after its fetch")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
     ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
     ap.add_argument("--num-verify", type=int, default=1,
@@ -370,7 +372,7 @@ def main() -> int:
     log("inputs staged in HBM")
 
     stream = torch.cuda.current_stream(dev)
-    hs.set_pipeline(0, args.fetch_wg, args.tail_chunks)
+    hs.set_pipeline(0, args.fetch_wg, args.tail_chunks, -1 if args.no_resident_first else 0)
     if args.policy != "lru":
         hs.set_replacement(args.policy, args.policy_seed)
 
@@ -699,6 +701,7 @@ def main() -> int:
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 2),
                    "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
+                        "resident_first": not args.no_resident_first,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
                         "sync_path_tokens_per_s": round(R * T * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
         "prefetch": dict(prefetch, no_prefetch_us_per_step=round(ms_step * 1e3, 2)) if prefetch else None,

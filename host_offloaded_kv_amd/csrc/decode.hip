@@ -41,6 +41,7 @@
 // inputs that KV caches do not hold.  FP8 rows always fit fp16.
 #include "internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
@@ -222,6 +223,9 @@ struct DecodeSmem {
   int overflow[kMaxPasses];             // a tile exceeded the reference max
   int nonfinite;                        // a score was inf or NaN: exact_fallback takes over
   int vbad;                             // an O accumulator is inf or NaN (read after the last barrier)
+  int cnt[kThreads / 64];               // per-wave counts of the row-id compaction
+  // merging an earlier launch's partials: factors per head (see merge_prepare)
+  float mown[HG], minv[HG], mlse[HG], mf[HG][kMaxMergeSlots];
 };
 
 // Passes over the K range: the first uses the reference max of the first
@@ -336,7 +340,7 @@ __device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)
 // the exact softmax.
 template <int HG, bool FP8>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
-                                           int n_tiles, int w, int g, int i16) {
+                                           int pair, int hg, int n_tiles, int w, int g, int i16) {
   const bool active = 16 * w < HG;
   // Q as MFMA B operands: lane (g, i16) holds dims 32 s + 8 g .. +7 of
   // head 16 w + i16, in bf16.
@@ -375,6 +379,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& 
     if (g == 0) {
       sm.lexact[16 * w + i16] = le;
       sm.mfin[16 * w + i16] = m_run;
+      if (a.merge_from > 0) merge_prepare<HG>(a, sm, kvs, pair, hg, 16 * w + i16, m_run, le);
     }
   }
   __syncthreads();
@@ -393,18 +398,69 @@ __device__ __forceinline__ OutSlot out_slot(const DecodeArgs& a, const DecodeSme
   // O and lse are normalised by the sum of the unrounded weights.
   const float lsum = sm.lexact[h];
   const float m = sm.mfin[h];
-  if (a.splits == 1) {
+  if (!a.out_partial) {
     if (writer)
       a.lse[head0 + h] = lsum > 0.f ? (m + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
     return {lsum > 0.f ? kvs / lsum : 0.f, a.out + (head0 + h) * kVDim + c0};
   }
-  float* part = a.partial + (((size_t)pair * a.splits + split) * a.num_heads + hg * HG + h) * kPartW;
+  float* part =
+      a.partial + (((size_t)pair * a.split_total + a.split_base + split) * a.num_heads + hg * HG + h) * kPartW;
   if (writer) {
     part[kVDim] = m;
     part[kVDim + 1] = lsum;
     part[kVDim + 2] = lsum;
   }
   return {kvs, part + c0};
+}
+
+// The output of head h of the group when the launch merges the partials of
+// an earlier launch over the other entries of the same query sets (slots
+// 0 .. merge_from-1): O = (sum_s f_s O_s + f O_own) / L and lse = m +
+// log2(L) (in log2 units, then ln), where m is the largest reference max
+// among the parts with weight and each part's sums are rescaled to it.
+// Called by one thread per head with this workgroup's reference max and
+// weight sum of the head; the factors go to LDS.
+template <int HG>
+__device__ __forceinline__ void merge_prepare(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, int pair, int hg,
+                                              int h, float mo, float lo) {
+  const size_t stride = (size_t)a.num_heads * kPartW;
+  const float* part = a.partial + ((size_t)pair * a.merge_from * a.num_heads + hg * HG + h) * kPartW;
+  float m = lo > 0.f ? mo : -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kMaxMergeSlots; ++q)
+    if (q < a.merge_from && part[q * stride + kVDim + 1] > 0.f) m = fmaxf(m, part[q * stride + kVDim]);
+  float own = 0.f, inv = 0.f, lse = -INFINITY, L = 0.f, LE = 0.f;
+  if (m != -INFINITY) {
+    const float fo = lo > 0.f ? exp2f(mo - m) : 0.f;
+    L = lo * fo;
+    LE = lo * fo;
+    own = kvs * fo;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxMergeSlots; ++q) {
+    float f = 0.f;
+    if (q < a.merge_from && m != -INFINITY) {
+      const float ls = part[q * stride + kVDim + 1];
+      if (ls > 0.f) {
+        f = exp2f(part[q * stride + kVDim] - m);
+        L += ls * f;
+        LE += part[q * stride + kVDim + 2] * f;
+      }
+    }
+    sm.mf[h][q] = f;
+  }
+  if (m != -INFINITY) {
+    inv = 1.f / L;
+    lse = (m + log2f(LE)) * 0.69314718055994531f;
+  }
+  sm.mown[h] = own;
+  sm.minv[h] = inv;
+  sm.mlse[h] = lse;
+}
+
+// Partial row of slot q of head h for the merge.
+__device__ __forceinline__ const float* merge_part(const DecodeArgs& a, int pair, int head_in_layer, int q) {
+  return a.partial + (((size_t)pair * a.merge_from + q) * a.num_heads + head_in_layer) * kPartW;
 }
 
 // One pass of a value wave over the tiles (see value_role).  The P
@@ -477,6 +533,39 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
   if (bad) sm.vbad = 1;
   __syncthreads();  // the score waves' normalisers are in LDS
   if (sm.nonfinite || sm.vbad) return;
+
+  if (a.merge_from > 0) {
+    // per head block: this workgroup's sums rescaled in place, then each
+    // earlier slot's 8 column groups loaded four at a time and added
+#pragma unroll
+    for (int nb = 0; nb < NBP; ++nb) {
+      const int h = nb * 16 + i16;
+      if (cw == 0 && g == 0) a.lse[head0 + h] = sm.mlse[h];
+      const float own = sm.mown[h], inv = sm.minv[h];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb * NBP + nb] *= own;
+#pragma unroll
+      for (int q = 0; q < kMaxMergeSlots; ++q) {
+        if (q >= a.merge_from) break;
+        const float* src = merge_part(a, pair, hg * HG + h, q) + 128 * cw + 4 * g;
+        const float f = sm.mf[h][q];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x4 pa[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pa[i] = *reinterpret_cast<const f32x4*>(src + 16 * (4 * half + i));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[(4 * half + i) * NBP + nb] += pa[i] * f;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float* dst = a.out + (head0 + h) * kVDim + 128 * cw + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(dst + 16 * mb) = acc[mb * NBP + nb] * inv;
+      __builtin_amdgcn_sched_barrier(0);  // one head block's loads in flight at a time
+    }
+    return;
+  }
 
 #pragma unroll
   for (int nb = 0; nb < NBP; ++nb) {
@@ -644,9 +733,28 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
   if (tid < HG) {
     sm.lexact[tid] = l;
     sm.mfin[tid] = m;
+    if (a.merge_from > 0) merge_prepare<HG>(a, sm, kvs, pair, hg, tid, m, l);
   }
   __syncthreads();
   if (!owner) return;
+  if (a.merge_from > 0) {
+    if ((tid & 7) == 0) a.lse[head0 + oh] = sm.mlse[oh];
+    const float own = sm.mown[oh], inv = sm.minv[oh];
+    float* dst = a.out + (head0 + oh) * kVDim + oc;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) acc[c] *= own;
+#pragma unroll
+    for (int q = 0; q < kMaxMergeSlots; ++q) {
+      if (q >= a.merge_from) break;
+      const float* pq = merge_part(a, pair, hg * HG + oh, q) + oc;
+      const float fq = sm.mf[oh][q];
+#pragma unroll
+      for (int c = 0; c < 64; ++c) acc[c] += pq[c] * fq;
+    }
+#pragma unroll
+    for (int c = 0; c < 64; ++c) dst[c] = acc[c] * inv;
+    return;
+  }
   const OutSlot o = out_slot(a, sm, kvs, head0, pair, split, hg, oh, oc, (tid & 7) == 0);
 #pragma unroll
   for (int c = 0; c < 64; ++c) o.dst[c] = acc[c] * o.scale;
@@ -680,27 +788,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   per = (per + kT - 1) / kT * kT;
   const int k0 = split * per;
   const int k1 = min(K, k0 + per);
-  const int n_tiles = k1 > k0 ? (k1 - k0 + kT - 1) / kT : 0;
 
-  // Row ids of the whole K range, validated once.
+  // Row ids of the K range, validated once.  A part launch keeps only the
+  // entries of its part, in order (ballot compaction over the range).
   if (tid < kMaxPasses) sm.overflow[tid] = 0;
   if (tid == 0) {
     sm.nonfinite = 0;
     sm.vbad = 0;
   }
-  for (int k = tid; k < n_tiles * kT; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
+  int n_rows = k1 > k0 ? k1 - k0 : 0;
+  if (a.part == 0) {
+    const int n_pad = (n_rows + kT - 1) / kT * kT;
+    for (int k = tid; k < n_pad; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
+  } else {
+    const uint64_t* mask = a.fill_mask + (size_t)pair * a.mask_words;
+    const bool want_filled = a.part == 2;
+    int base = 0;
+    for (int c0 = k0; c0 < k1; c0 += kThreads) {
+      const int k = c0 + tid;
+      const bool in = k < k1 && (((mask[k >> 6] >> (k & 63)) & 1ull) != 0) == want_filled;
+      const uint64_t b = __ballot(in);
+      if (lane == 0) sm.cnt[w] = __popcll(b);
+      __syncthreads();
+      int off = base, tot = 0;
+#pragma unroll
+      for (int i = 0; i < kThreads / 64; ++i) {
+        const int n = sm.cnt[i];
+        off += i < w ? n : 0;
+        tot += n;
+      }
+      if (in) sm.rowid[off + __popcll(b & ((1ull << lane) - 1))] = load_row_id(a, rows, k, k1);
+      base += tot;
+      __syncthreads();  // cnt is rewritten by the next chunk
+    }
+    n_rows = base;
+    for (int k = n_rows + tid; k < (n_rows + kT - 1) / kT * kT; k += kThreads) sm.rowid[k] = -1;
+  }
+  const int n_tiles = (n_rows + kT - 1) / kT;
   __syncthreads();
 
   const size_t head0 = (size_t)pair * H + hg * HG;
   if (w < 4)
-    score_role<HG, FP8>(a, sm, kvs, head0, n_tiles, w, g, i16);
+    score_role<HG, FP8>(a, sm, kvs, head0, pair, hg, n_tiles, w, g, i16);
   else if (w < 8)
     value_role<HG, FP8>(a, sm, kvs, head0, pair, split, hg, n_tiles, w - 4, g, i16);
   else
     loader_role<HG, FP8>(sm, kv, n_tiles, tid - 512);
   // nonfinite is final after every role's last barrier.
   if (sm.nonfinite || sm.vbad) {
-    exact_fallback<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, k1 > k0 ? k1 - k0 : 0, tid);
+    exact_fallback<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, n_rows, tid);
     if (tid == 0) atomicAdd(a.fallback_count, 1u);
   }
 }
@@ -715,7 +851,7 @@ constexpr int kMaxSplits = kMaxTopK / kT;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_splits(DecodeArgs a) {
   __shared__ float f_s[kCombineThreads / 64][kMaxSplits];
-  const int H = a.num_heads, S = a.splits;
+  const int H = a.num_heads, S = a.split_total;
   const int wv = threadIdx.x >> 6;
   const size_t ph = (size_t)blockIdx.x * (kCombineThreads / 64) + wv;  // pair * H + head
   const int lane = threadIdx.x & 63;
@@ -818,8 +954,36 @@ int decode_splits(int n_layers, int num_requests, int num_heads, int top_k) {
   return splits;
 }
 
-hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s) {
-  const int hgs = head_group(a.num_heads);
+// With at least 32 (request, head group) workgroups, the part beside the
+// fetches runs without key splits (a whole fetch to hide under) and the
+// part after the fetch is one launch without key splits that merges it, on
+// workgroups of 16 heads: that part holds only the misses, so a workgroup
+// has few tiles, and 16-head workgroups spread them over more CUs (the rows
+// re-read by a request's head groups come from its XCD's L2) and merge
+// fewer heads each.
+// With fewer, the first part takes about 128 workgroups (at most
+// kMaxMergeSlots key splits), leaving the other CUs to the fetch, and the
+// second is split to fill the GPU and merged by combine_splits.
+constexpr int kMergeMinWorkgroups = 32;
+
+bool resident_first_pays(int num_requests, int num_heads) {
+  return num_requests * (num_heads / head_group(num_heads)) >= kMergeMinWorkgroups;
+}
+
+void resident_first_splits(int num_requests, int num_heads, int top_k, int* before, int* after) {
+  const int base = num_requests * (num_heads / head_group(num_heads));
+  const int max_splits = (top_k + kMinTilesPerSplit * kT - 1) / (kMinTilesPerSplit * kT);
+  if (base >= kMergeMinWorkgroups) {
+    *before = 1;
+    *after = 0;
+  } else {
+    *before = std::max(1, std::min({max_splits, kMaxMergeSlots, 128 / base}));
+    *after = decode_splits(1, num_requests, num_heads, top_k);
+  }
+}
+
+hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s, bool combine) {
+  const int hgs = a.head_group > 0 ? a.head_group : head_group(a.num_heads);
   const int nhg = a.num_heads / hgs;
   const int grid = a.n_layers * a.num_requests * nhg * a.splits;
   prof_begin(p, kKDecode, s);
@@ -837,7 +1001,7 @@ hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   prof_end(p, s);
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess || a.split_total == 1 || !combine) return e;
   prof_begin(p, kKCombine, s);
   // num_heads is a multiple of 16, so the (pair, head) count divides by 4
   hipLaunchKernelGGL(combine_splits, dim3(a.n_layers * a.num_requests * a.num_heads / (kCombineThreads / 64)),

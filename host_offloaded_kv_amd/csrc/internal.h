@@ -114,6 +114,8 @@ struct ResolveArgs {
                             // pinned; hits pinned without a stamp; misses beyond the free slots
                             // dropped); counts then holds [n_layers][R][4] (resident, hit, filled,
                             // dropped) or is NULL
+  uint64_t* fill_mask;      // [n_layers][R][ceil(top_k / 64)]: bit j set when entry j's row is filled by
+                            // this call (a miss); NULL: not written
   int16_t* posmap;          // [L][sum ctx] position -> slot (-1: not in the hot buffer)
   const int64_t* map_off;   // [R] offset of request r within a layer's map
   int64_t map_layer_stride; // sum of ctx_r
@@ -126,7 +128,7 @@ struct DecodeArgs {
   const float* kv_scale;   // [L] FP8 row scales (device)
   float* out;              // [n_layers][R][H][512]
   float* lse;              // [n_layers][R][H]
-  float* partial;          // [n_layers][R][splits][H][kPartW] when splits > 1
+  float* partial;          // [n_layers][R][split_total][H][kPartW] when split_total > 1
   uint32_t* fallback_count;  // workgroups that took the exact fp32 path (read and cleared by the host)
   uint32_t* err;
   int32_t layer_begin;
@@ -134,7 +136,18 @@ struct DecodeArgs {
   int32_t num_requests;
   int32_t num_heads;
   int32_t top_k;
-  int32_t splits;
+  int32_t splits;          // key-range splits of this launch
+  int32_t split_base;      // partial slot of the launch's split 0
+  int32_t split_total;     // partial slots per (query set, head)
+  int32_t out_partial;     // 1: the launch writes partial slots (merged later); 0: O and lse
+  int32_t part;            // entries attended: 0 all; 1 those whose row was in place before this step's
+                           // fetch (fill_mask bit clear); 2 those filled by it (bit set)
+  const uint64_t* fill_mask;  // [n_layers][R][mask_words] (part != 0)
+  int32_t mask_words;
+  int32_t head_group;      // heads per workgroup (16, 32 or 64); 0: the default for num_heads
+  int32_t merge_from;      // > 0: partial slots [0, merge_from) of every (query set, head), written by an
+                           // earlier launch over other entries, are merged into this launch's O and lse
+                           // (which then has one split and split_total 1)
   int64_t kv_rows;         // rows per KV tensor
   float scale_log2;        // scale * log2(e)
   int32_t kv_dtype;        // HISPARSE_KV_BF16 or HISPARSE_KV_FP8_E4M3
@@ -142,8 +155,8 @@ struct DecodeArgs {
 
 // Workspace carving, computed identically for sizing and for creation.
 struct Layout {
-  size_t owner, stamp, lru, last_t, miss_count, fetch, pf_miss_count, pf_fetch, bt, bt_off, ctx, cap, hv, host_rows,
-      kv_ptrs, kv_scale, err, fallback_count, partial, posmap, map_off, total;
+  size_t owner, stamp, lru, last_t, miss_count, fetch, pf_miss_count, pf_fetch, fill_mask, bt, bt_off, ctx, cap, hv,
+      host_rows, kv_ptrs, kv_scale, err, fallback_count, partial, posmap, map_off, total;
   int64_t bt_entries;
   int64_t posmap_entries;   // L * sum ctx_r
   size_t partial_floats;   // floats of the split-partial region
@@ -195,6 +208,8 @@ struct hisparse_pool {
   int2* fetch;
   int32_t* pf_miss_count;               // prefetch miss lists, apart from the step's own (a prefetch
   int2* pf_fetch;                       // runs while the step's fetch may still read those)
+  uint64_t* fill_mask;                  // [L][R][mask_words] entries filled by the last RESOLVE
+  int32_t mask_words = 0;               // ceil(K / 64)
   uint64_t* host_rows_d;
   unsigned char** kv_d;
   float* kv_scale_d;
@@ -211,6 +226,10 @@ struct hisparse_pool {
   int fetch_wg_all = hs::kDefaultGroupFetchWorkgroups;   // workgroups of a whole-group fetch
   int fetch_wg_unit = hs::kDefaultUnitFetchWorkgroups;   // workgroups of a pipelined fetch
   int tail_chunks = hs::kDefaultTailChunks;              // request chunks of a group's last layer
+  // A group's last layer decoded in two parts: rows in place before its
+  // fetch (beside the fetches), then the fetched rows.  -1 never, 0 where
+  // the part after the fetch fills enough workgroups, 1 always.
+  int resident_first = 0;
 };
 
 namespace hs {
@@ -237,8 +256,17 @@ hipError_t launch_writeback(hisparse_pool* p, const WritebackArgs& a, hipStream_
 
 // decode.hip
 int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
+// A layer decoded resident rows first: `before` key splits for the part
+// beside the fetches; after the fetch either one launch without key splits
+// that also merges the first part's partials (*after = 0), or `after` key
+// splits and combine_splits.  resident_first_pays: whether the merging
+// launch has enough workgroups (the default of hisparse_set_pipeline).
+constexpr int kMaxMergeSlots = 4;
+void resident_first_splits(int num_requests, int num_heads, int top_k, int* before, int* after);
+bool resident_first_pays(int num_requests, int num_heads);
 // Device address of the fixed split-partial array on `device` (which must
 // be current), looked up once per device and kept.
 hipError_t static_scratch_address(int device, float** out);
-hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s);
+// combine: merge the split partials after the launch (when split_total > 1).
+hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s, bool combine = true);
 }  // namespace hs

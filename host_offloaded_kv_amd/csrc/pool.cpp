@@ -134,6 +134,13 @@ Layout make_layout(const hisparse_config* c) {
   };
   for (int n = 1; n <= c->index_share; ++n) need(n, R * T);
   for (size_t nreq = 1; nreq <= R; ++nreq) need(1, nreq * T);
+  if (T == 1) {
+    // a group's last layer decoded in two parts (resident rows first)
+    int before = 1, after = 0;
+    resident_first_splits((int)R, c->num_heads, c->top_k, &before, &after);
+    smax = std::max(smax, before + after);
+    part = std::max(part, (size_t)(before + after) * R * c->num_heads * kPartW);
+  }
   L.splits_max = smax;
   L.partial_floats = part;
   size_t off = 0;
@@ -145,6 +152,7 @@ Layout make_layout(const hisparse_config* c) {
   L.fetch = off; off = align256(off + NL * R * W * 8);
   L.pf_miss_count = off; off = align256(off + NL * R * 4);
   L.pf_fetch = off; off = align256(off + NL * R * W * 8);
+  L.fill_mask = off; off = align256(off + NL * R * ((c->top_k + 63) / 64) * 8);
   L.bt = off; off = align256(off + (size_t)bt_entries * 4);
   L.bt_off = off; off = align256(off + R * 4);
   L.ctx = off; off = align256(off + R * 4);
@@ -369,6 +377,8 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->fetch = (int2*)(w + lay.fetch);
   p->pf_miss_count = (int32_t*)(w + lay.pf_miss_count);
   p->pf_fetch = (int2*)(w + lay.pf_fetch);
+  p->fill_mask = (uint64_t*)(w + lay.fill_mask);
+  p->mask_words = (cfg->top_k + 63) / 64;
   p->bt = (int32_t*)(w + lay.bt);
   p->bt_off = (int32_t*)(w + lay.bt_off);
   p->ctx_d = (int32_t*)(w + lay.ctx);
@@ -517,6 +527,9 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.resident_rows = p->cfg.resident_rows_per_layer;
   a.policy = p->policy;
   a.policy_seed = p->policy_seed;
+  // The fill mask serves the two-part decode of a one-token selection.
+  a.fill_mask = (!prefetch && p->T == 1) ? p->fill_mask + (size_t)layer_begin * p->cfg.num_requests * p->mask_words
+                                         : nullptr;
   a.posmap = p->posmap;
   a.map_off = p->map_off;
   a.map_layer_stride = p->lay.posmap_entries / p->cfg.num_layers;
@@ -557,9 +570,19 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
 // decoded piecewise.
 // use_static: split partials in the fixed device array instead of the
 // workspace (hisparse_sparse_mla_decode_layers_static).
+// part: one part of a layer decoded resident rows first -- part 1 (rows in
+// place before the step's fetch) or 2 (rows it fills) -- writing partial
+// slots [split_base, split_base + splits) of split_total, merged by
+// combine_splits after the launch of part 2; or, with merge_from > 0, part
+// 2 in one launch that merges part 1's slots [0, merge_from) itself.
+struct PartSpec {
+  int part = 0, split_base = 0, split_total = 0, merge_from = 0, head_group = 0;
+  bool combine = true;
+};
+
 hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, int32_t nreq,
                                const uint16_t* d_q, const int32_t* d_rows, float scale, float* d_out, float* d_lse,
-                               hipStream_t s, int splits = 0, bool use_static = false) {
+                               hipStream_t s, int splits = 0, bool use_static = false, PartSpec ps = PartSpec()) {
   DecodeArgs a;
   a.q = d_q;
   a.rows = d_rows;
@@ -577,7 +600,21 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.num_heads = p->cfg.num_heads;
   a.top_k = p->cfg.top_k;
   a.splits = splits > 0 ? splits : decode_splits(n_layers, nreq, p->cfg.num_heads, p->cfg.top_k);
-  const size_t part_floats = a.splits > 1 ? (size_t)a.splits * n_layers * nreq * p->cfg.num_heads * kPartW : 0;
+  a.split_base = ps.split_base;
+  a.split_total = ps.split_total > 0 ? ps.split_total : a.splits;
+  a.out_partial = a.split_total > 1 || ps.part == 1 ? 1 : 0;
+  a.part = ps.part;
+  a.merge_from = ps.merge_from;
+  a.head_group = ps.head_group;
+  a.mask_words = p->mask_words;
+  a.fill_mask = p->fill_mask + ((size_t)layer_begin * p->cfg.num_requests) * p->mask_words;
+  if ((ps.part != 0 && (n_layers != 1 || nreq != p->cfg.num_requests || p->T != 1)) ||
+      (ps.merge_from > 0 && (a.splits != 1 || a.split_total != 1 || ps.merge_from > kMaxMergeSlots))) {
+    set_error("bad two-part decode launch");
+    return HISPARSE_EINVAL;
+  }
+  const size_t part_floats =
+      a.out_partial ? (size_t)a.split_total * n_layers * nreq * p->cfg.num_heads * kPartW : 0;
   if (use_static && part_floats * sizeof(float) > HISPARSE_STATIC_SCRATCH_BYTES) {
     set_error("decode launch needs " + std::to_string(part_floats * sizeof(float)) +
               " bytes of split partials; the static scratch holds " +
@@ -592,7 +629,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   }
   a.kv_rows = p->kv_rows;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = launch_decode(p, a, s);
+  hipError_t e = launch_decode(p, a, s, ps.combine);
   return e == hipSuccess ? HISPARSE_OK : hip_fail(e, "decode launch");
 }
 }  // namespace
@@ -732,6 +769,12 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
   hipStream_t fs = p->fetch_stream;
   const int C = std::min<int>(p->tail_chunks, (int)R);
   const bool pf = d_next != nullptr;
+  // The group's last layer in two parts: the rows in place before its fetch
+  // are decoded beside the fetch, the fetched rows after it.
+  const bool rf = T == 1 && C == 1 &&
+                  (p->resident_first > 0 || (p->resident_first == 0 && resident_first_pays((int)R, (int)H)));
+  int rf_before = 1, rf_after = 0;
+  if (rf) resident_first_splits((int)R, (int)H, (int)K, &rf_before, &rf_after);
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
@@ -746,10 +789,10 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
     hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
                                          d_counts + (size_t)l0 * R * 3, s);
     if (st) return st;
-    if (G == 1 && C == 1) {
-      // One layer, one unit: its fetch and decode have nothing to overlap,
-      // so they run on `stream` with the whole-group fetch shape; a
-      // prefetch forks off after the fetch.
+    if (G == 1 && C == 1 && !rf) {
+      // One layer, one unit, decoded whole: its fetch and decode have
+      // nothing to overlap, so they run on `stream` with the whole-group
+      // fetch shape; a prefetch forks off after the fetch.
       const size_t pr = (size_t)l0 * R * T;  // first query set of the layer
       if ((st = enqueue_fetch(p, l0, 1, 0, (int)R, p->fetch_wg_all, s))) return st;
       if (pf && g + 1 == c.num_layers / G) {
@@ -774,18 +817,44 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       const int r0 = (int)(R * ch / C), r1 = (int)(R * (ch + 1) / C);
       units[nu++] = {l0 + G - 1, r0, r1 - r0, 0};
     }
+    auto decode = [&](const Unit& un, int splits, PartSpec ps) {
+      const size_t pr = ((size_t)un.layer * R + un.r0) * T;  // first query set of the unit
+      return enqueue_decode(p, un.layer, 1, (int)(un.nreq * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                            d_out + pr * H * kVDim, d_lse + pr * H, s, splits, false, ps);
+    };
+    if (rf) {
+      // Part 1 of the last layer: its entries whose rows are in place
+      // before this step's fetches (which never write them), decoded
+      // beside the group's first fetch.
+      PartSpec ps;
+      ps.part = 1;
+      ps.split_total = rf_before + rf_after;
+      ps.combine = false;
+      if ((st = decode(units[nu - 1], rf_before, ps))) return st;
+    }
     for (int u = 0; u < nu; ++u) {
       if ((st = enqueue_fetch(p, units[u].layer, 1, units[u].r0, units[u].nreq, p->fetch_wg_unit, fs))) return st;
       if ((e = hipEventRecord(p->ev_fetch[u], fs)) != hipSuccess) return hip_fail(e, (f + ": fetch event").c_str());
     }
     if (pf && g + 1 == c.num_layers / G && (st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, fs))) return st;
     for (int u = 0; u < nu; ++u) {
-      const Unit& un = units[u];
-      const size_t pr = ((size_t)un.layer * R + un.r0) * T;  // first query set of the unit
       if ((e = hipStreamWaitEvent(s, p->ev_fetch[u], 0)) != hipSuccess) return hip_fail(e, (f + ": join").c_str());
-      st = enqueue_decode(p, un.layer, 1, (int)(un.nreq * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
-                          d_out + pr * H * kVDim, d_lse + pr * H, s, un.splits);
-      if (st) return st;
+      if (rf && u + 1 == nu) {
+        // Part 2: the entries the fetch filled, merged with part 1.
+        PartSpec ps;
+        ps.part = 2;
+        if (rf_after == 0) {
+          ps.merge_from = rf_before;
+          ps.head_group = 16;
+          if ((st = decode(units[u], 1, ps))) return st;
+        } else {
+          ps.split_base = rf_before;
+          ps.split_total = rf_before + rf_after;
+          if ((st = decode(units[u], rf_after, ps))) return st;
+        }
+        continue;
+      }
+      if ((st = decode(units[u], units[u].splits, PartSpec()))) return st;
     }
   }
   // `stream` waits for the prefetch, which also joins the fork for capture.
@@ -968,15 +1037,17 @@ hisparse_status hisparse_set_replacement(hisparse_pool* p, int32_t policy, uint6
 }
 
 hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_workgroups,
-                                      int32_t unit_fetch_workgroups, int32_t tail_chunks) {
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first) {
   if (!p || group_fetch_workgroups < 0 || group_fetch_workgroups > 65536 || unit_fetch_workgroups < 0 ||
-      unit_fetch_workgroups > 65536 || tail_chunks < 0 || tail_chunks > kMaxTailChunks) {
+      unit_fetch_workgroups > 65536 || tail_chunks < 0 || tail_chunks > kMaxTailChunks || resident_first < -1 ||
+      resident_first > 1) {
     set_error("hisparse_set_pipeline: bad argument");
     return HISPARSE_EINVAL;
   }
   p->fetch_wg_all = group_fetch_workgroups > 0 ? group_fetch_workgroups : kDefaultGroupFetchWorkgroups;
   p->fetch_wg_unit = unit_fetch_workgroups > 0 ? unit_fetch_workgroups : kDefaultUnitFetchWorkgroups;
   p->tail_chunks = tail_chunks > 0 ? tail_chunks : kDefaultTailChunks;
+  p->resident_first = resident_first;
   return HISPARSE_OK;
 }
 

@@ -205,6 +205,8 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   if (t < 0 || t < last) {
     if (!a.prefetch)
       for (int j = tid; j < K; j += kMetaThreads) rows_out[j] = -1;
+    if (a.fill_mask && !a.prefetch)
+      for (int i = tid; i < (K + 63) / 64; i += kMetaThreads) a.fill_mask[cpair * ((K + 63) / 64) + i] = 0ull;
     if (tid == 0) {
       if (a.prefetch) {
         if (a.counts)
@@ -384,6 +386,13 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     }
     mb[c] = __ballot(miss);
     mloc += __popcll(mb[c]);
+  }
+  // The entries this call fills, one bit each (wave ranges start on 64).
+  if (a.fill_mask && !pf && lane == 0) {
+    uint64_t* fm = a.fill_mask + cpair * ((K + 63) / 64);
+#pragma unroll
+    for (int c = 0; c < SC; ++c)
+      if (c < njc && jb + 64 * c < je) fm[(jb >> 6) + c] = mb[c];
   }
   if (lane == 0) cnt_s[0][wid] = mloc;
   __syncthreads();

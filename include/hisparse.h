@@ -270,7 +270,15 @@ hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* pool, in
  * and the decode of a unit waits (by event) only for that unit's fetch, so
  * it overlaps the fetches of the units after it (a whole layer is decoded
  * without key splits, on few CUs; chunks of the last layer are split to
- * fill the GPU).  A group of one layer fetched in one piece has nothing
+ * fill the GPU).  With one verify token and the last layer in one piece,
+ * that layer can be decoded in two parts (resident_first of
+ * hisparse_set_pipeline): its entries whose rows were already in place
+ * (resident pages and hits, which no fetch of the step writes) right after
+ * the metadata kernel, beside the group's fetches, then the entries its
+ * fetch fills, and the two parts' sums are merged -- attention over a set
+ * of keys splits into any partition (the summary article, section 02: the
+ * outputs are those of attention over the selected keys, wherever they
+ * live).  Otherwise a group of one layer fetched in one piece has nothing
  * to overlap and runs resolve, fetch and decode on `stream` alone.
  * `stream` waits for every fetch
  * before the call's last decode, so work enqueued on `stream` afterwards
@@ -398,11 +406,21 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *     hisparse_step (default 32), which leave the other CUs to the decode
  *     running beside them;
  *   tail_chunks: request chunks the last layer of an index-share group is
- *     fetched and decoded in (default 1, at most 16, capped at R).
+ *     fetched and decoded in (default 1, at most 16, capped at R);
+ *   resident_first: with one verify token and one tail chunk, the last
+ *     layer of an index-share group can be decoded in two parts -- the
+ *     entries whose rows were in place before this step's fetches
+ *     (resident pages and hits) beside the fetches, the entries its fetch
+ *     fills after it -- with the parts' softmax sums merged.  With at least
+ *     32 (request, head group) workgroups the second part is one launch
+ *     without key splits that merges the first; with fewer, both parts are
+ *     split and combine_splits merges them.  1: always; -1: never (one
+ *     launch after the fetch); 0 (default): where the merging launch
+ *     applies, i.e. with at least 32 such workgroups.
  * Results do not depend on these settings, except the rounding of O and
- * lse of the chunked layer.  Errors: EINVAL. */
+ * lse of the chunked or two-part layer.  Errors: EINVAL. */
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,
-                                      int32_t unit_fetch_workgroups, int32_t tail_chunks);
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first);
 
 /* Copy the LRU state of (request r, layer l) -- the slot owners and LRU
  * stamps that the HiSparse summary article, section 02, keeps per device

@@ -138,12 +138,15 @@ def check_attention(run, dec, t, sel_t, pairs):
 
 
 def run_and_compare(w, steps=None, attend_every=1, attend_pairs=None, state_pairs=None,
-                    bytes_pairs=None, requests_for_oracle=None, label="", trace=None):
+                    bytes_pairs=None, requests_for_oracle=None, label="", trace=None, setup=None):
     """Run ``steps`` decode steps on the GPU and check each one (``trace``:
-    the selections to use instead of the workload's own sorted trace)."""
+    the selections to use instead of the workload's own sorted trace;
+    ``setup``: called with the pool before the first step)."""
     steps = w.steps if steps is None else steps
     tr = w.trace(steps) if trace is None else trace
     hs = make_pool(w)
+    if setup is not None:
+        setup(hs)
     run = GpuRun(w, hs)
     dec = OracleDecoder(w, requests=requests_for_oracle)
     all_pairs = [(l, r) for l in range(w.num_layers) for r in dec.requests]
