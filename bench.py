@@ -41,7 +41,8 @@ def pmc_ratio(workload: str, kernel: str, host_link: bool):
         return None
     with open(path) as f:
         ks = json.load(f).get("kernels", {})
-    names = {"sparse_mla_decode": ["decode_ws_unsplit", "decode_ws_split"]}.get(kernel, [kernel])
+    names = {"sparse_mla_decode": ["decode_ws_unsplit", "decode_ws_split", "decode_ws_part1",
+                                   "decode_ws_part2"]}.get(kernel, [kernel])
     es = [ks[n] for n in names if n in ks and "alg_bytes_per_launch" in ks[n]]
     if not es:
         return None
