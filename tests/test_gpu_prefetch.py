@@ -143,20 +143,29 @@ def _grouped():
                          "tail")
 
 
-@pytest.mark.parametrize("shape", ["grouped", "single_layer"])
-def test_step_prefetch_matches_oracle(shape):
+@pytest.mark.parametrize("shape,two_part", [("grouped", 0), ("grouped", 1), ("single_layer", 0), ("single_layer", 1),
+                                            ("full_size", 1)])
+def test_step_prefetch_matches_oracle(shape, two_part):
     """hisparse_step_prefetch with the exact next selection: the step's own
     outputs as in the oracle, the in-step prefetch as oracle.prefetch, and
-    (room permitting) no miss in the next step."""
+    (room permitting) no miss in the next step.  two_part = 1 decodes each
+    group's last layer in two parts (resident_first) where the default would
+    not (small shapes: both parts split, merged by combine_splits); the full
+    size r32_ctx128k_l4 case (requests 0 and 17 checked) merges in the
+    second part."""
     import torch
 
-    w = _grouped() if shape == "grouped" else named_workload("r8_ctx32k")
-    steps = 6
+    w = {"grouped": _grouped, "single_layer": lambda: named_workload("r8_ctx32k"),
+         "full_size": lambda: named_workload("r32_ctx128k_l4")}[shape]()
+    steps = 6 if shape != "full_size" else 3
     tr = w.trace(steps + 1)
     hs = make_pool(w)
+    if two_part:
+        hs.set_pipeline(resident_first=1)
     buf = _Buffers(w, hs.device)
-    dec = OracleDecoder(w)
-    pairs = [(l, r) for l in range(w.num_layers) for r in range(w.num_requests)]
+    reqs = list(range(w.num_requests)) if shape != "full_size" else [0, 17]
+    dec = OracleDecoder(w, requests=reqs)
+    pairs = [(l, r) for l in range(w.num_layers) for r in reqs]
     pfc = torch.full((w.num_layers, w.num_requests, 4), -7, dtype=torch.int32, device=hs.device)
     d_next = torch.empty_like(buf.topk)
     for t in range(steps):
@@ -168,7 +177,8 @@ def test_step_prefetch_matches_oracle(shape):
         _check_rows(buf, res, pairs, t, "step_prefetch")
         if t > 0:
             assert all(res[p].n_miss == 0 for p in pairs), "an exact prediction with room leaves no miss"
-        check_attention(buf_view(w, buf), dec, t, tr[t], pairs if shape == "grouped" else [(0, 0), (0, 5)])
+        att = {"grouped": pairs, "single_layer": [(0, 0), (0, 5)], "full_size": [(3, 0), (3, 17)]}[shape]
+        check_attention(buf_view(w, buf), dec, t, tr[t], att)
         pres = _oracle_prefetch(dec, w, t, tr[t + 1])
         _check_pf_counts(pfc.cpu().numpy(), pres, pairs, t)
         assert all(pres[p].n_dropped == 0 for p in pairs)
