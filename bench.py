@@ -289,7 +289,10 @@ def main() -> int:
     ap.add_argument("--no-residency", action="store_true", help="skip the append / write-back timing")
     ap.add_argument("--no-prefetch", action="store_true", help="skip the cross-step prefetch runs")
     ap.add_argument("--no-resident-first", action="store_true",
-                    help="decode each group's last layer in one launch after its fetch")
+                    help="with separate fetches, decode each group's last layer in one launch after its fetch")
+    ap.add_argument("--no-fetch-in-decode", action="store_true",
+                    help="separate miss fetches (the layer pipeline) instead of the decode reading the filled rows "
+                         "from the host pool")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random"], help="replacement policy")
     ap.add_argument("--policy-seed", type=int, default=1, help="seed of the random replacement policy")
     ap.add_argument("--num-verify", type=int, default=1,
@@ -373,7 +376,8 @@ def main() -> int:
     log("inputs staged in HBM")
 
     stream = torch.cuda.current_stream(dev)
-    hs.set_pipeline(0, args.fetch_wg, args.tail_chunks, -1 if args.no_resident_first else 0)
+    hs.set_pipeline(0, args.fetch_wg, args.tail_chunks, -1 if args.no_resident_first else 0,
+                    -1 if args.no_fetch_in_decode else 0)
     if args.policy != "lru":
         hs.set_replacement(args.policy, args.policy_seed)
 
@@ -582,7 +586,9 @@ def main() -> int:
     for name, (n, tot_ms) in prof.items():
         # algorithmic bytes of the timed steps, spread evenly over the launches
         avg_ms = tot_ms / n
-        if name == "fetch_rows":
+        if name in ("fetch_rows", "sparse_mla_decode_fetch"):
+            # host-link bytes: the missed rows (the decode that fetches moves
+            # every filled row of its index-share group)
             alg = host_bytes.sum() / n
             bound, peak, unit = "host_link", PCIE_PEAK_GBS, "GB/s"
         elif name == "sparse_mla_decode":
@@ -602,17 +608,26 @@ def main() -> int:
                       "achieved": round(ach, 2) if ach is not None else None, "bound": bound, "peak": peak,
                       "unit": unit, "frac": round(ach / peak, 4) if (peak and ach is not None) else None,
                       "busy_share_of_step": round(tot_ms / ms_total, 4)}
+    if "sparse_mla_decode_fetch" in kern:
+        kf = kern["sparse_mla_decode_fetch"]
+        kf["decode_alg_bytes_per_launch"] = int(attn_bytes.sum() / kf["launches"])
+        kf["fp32_fallback_workgroups"] = int(fallbacks)
+        kf["note"] = ("the step's only launch besides the metadata kernel: the decode of every layer of an index-share "
+                      "group, reading the rows the step fills straight from the pinned host pool (and writing them to "
+                      "their hot rows); bound by the host link")
     if "sparse_mla_decode" in kern:
         kern["sparse_mla_decode"]["fp32_fallback_workgroups"] = int(fallbacks)
         kern["sparse_mla_decode"]["in_step_note"] = (
-            "in-step launches: every layer of an index-share group but the last is decoded without key splits "
-            "on few CUs while the next layer's miss fetch streams; the group's last layer is split over the "
-            "whole GPU; full_gpu_launch: one launch over all layers of a group on all CUs")
-        if dec_us:
-            ach_full = dec_bytes / (dec_us * 1e-6) / 1e9
-            kern["sparse_mla_decode"]["full_gpu_launch"] = {
-                "us": round(dec_us, 2), "alg_bytes": int(dec_bytes), "achieved": round(ach_full, 2),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_full / HBM_PEAK_GBS, 4)}
+            "in-step launches with separate fetches: the layers of an index-share group but the last decoded "
+            "without key splits while the next layer's miss fetch streams, the last layer in two parts (resident "
+            "rows beside the fetches, fetched rows after) or split over the whole GPU")
+    dk = kern.get("sparse_mla_decode") or kern.get("sparse_mla_decode_fetch")
+    if dk is not None and dec_us:
+        # the decode alone (rows already resident): one launch over all layers of a group on all CUs
+        ach_full = dec_bytes / (dec_us * 1e-6) / 1e9
+        dk["full_gpu_launch"] = {
+            "us": round(dec_us, 2), "alg_bytes": int(dec_bytes), "achieved": round(ach_full, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_full / HBM_PEAK_GBS, 4)}
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kern[dom]
     pmc = pmc_ratio(w.name, dom, d["bound"] == "host_link") if T == 1 and args.kv_dtype == "bf16" else None
@@ -640,8 +655,9 @@ def main() -> int:
         probe = host_link_probe(torch, H, dev)
         log(f"host-link probe: {probe}")
     measured_link = max(v for k, v in probe.items() if k != "d2d_copy_GBs") if probe else None
-    if "fetch_rows" in kern and measured_link:
-        kern["fetch_rows"]["frac_of_measured_link"] = round(kern["fetch_rows"]["achieved"] / measured_link, 4)
+    for kn in ("fetch_rows", "sparse_mla_decode_fetch"):
+        if kn in kern and measured_link:
+            kern[kn]["frac_of_measured_link"] = round(kern[kn]["achieved"] / measured_link, 4)
 
     if args.calib_copy_mib:
         nb = args.calib_copy_mib << 20
@@ -703,6 +719,7 @@ def main() -> int:
                    "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "resident_first": not args.no_resident_first,
+                        "fetch_in_decode": not args.no_fetch_in_decode,
                         "sync_path_us_per_step": round(sync_ms / args.steps * 1e3, 2) if sync_ms else None,
                         "sync_path_tokens_per_s": round(R * T * args.steps / (sync_ms * 1e-3), 2) if sync_ms else None},
         "prefetch": dict(prefetch, no_prefetch_us_per_step=round(ms_step * 1e3, 2)) if prefetch else None,

@@ -73,6 +73,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef const __attribute__((address_space(1))) u32x4 gu32x4;
 typedef const __attribute__((address_space(1))) u32x2 gu32x2;
+typedef const __attribute__((address_space(1))) uint32_t gu32;
+typedef const __attribute__((address_space(1))) uint16_t gu16;
 
 // Two fp32 values -> their fp16 pair, rounded to nearest even (overflow
 // gives +-inf).
@@ -119,13 +121,25 @@ __device__ __forceinline__ int load_row_id(const DecodeArgs& a, const int32_t* r
 template <bool FP8>
 struct TileStage;
 
+// A hot-row write of a fetched row goes through a buffer resource over
+// the request's hot rows; threads with nothing to write pass an offset
+// beyond its end, which the hardware drops.  The store is issued on every
+// path, so the loads in flight stay the same on all of them.
+constexpr int kNoHotWrite = 0x7FFF0000;
+
 template <>
 struct TileStage<false> {
   u32x4 v[kStage];
-  __device__ __forceinline__ void load_row(const unsigned char* kv, int rid, int t) {
-    gu32x4* src = (gu32x4*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytes + (t & 7) * 16);
+  // row: first byte of the row (a KV tensor row or a host pool row)
+  __device__ __forceinline__ void load_row(const unsigned char* row, int t) {
+    gu32x4* src = (gu32x4*)(row + (t & 7) * 16);
 #pragma unroll
     for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
+  }
+  __device__ __forceinline__ void store_hot(__amdgpu_buffer_rsrc_t hot, int off, int t) const {
+#pragma unroll
+    for (int k = 0; k < kStage; ++k)
+      __builtin_amdgcn_raw_buffer_store_b128(v[k], hot, off + ((t & 7) + 8 * k) * 16, 0, 0);
   }
   __device__ __forceinline__ void store(unsigned char* xs, int t) const {
     u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
@@ -137,10 +151,15 @@ struct TileStage<false> {
 template <>
 struct TileStage<true> {
   u32x2 v[kStage];
-  __device__ __forceinline__ void load_row(const unsigned char* kv, int rid, int t) {
-    gu32x2* src = (gu32x2*)(kv + (size_t)(rid < 0 ? 0 : rid) * kRowBytesFp8 + (t & 7) * 8);
+  __device__ __forceinline__ void load_row(const unsigned char* row, int t) {
+    gu32x2* src = (gu32x2*)(row + (t & 7) * 8);
 #pragma unroll
     for (int k = 0; k < kStage; ++k) v[k] = src[8 * k];
+  }
+  __device__ __forceinline__ void store_hot(__amdgpu_buffer_rsrc_t hot, int off, int t) const {
+#pragma unroll
+    for (int k = 0; k < kStage; ++k)
+      __builtin_amdgcn_raw_buffer_store_b64(v[k], hot, off + ((t & 7) + 8 * k) * 8, 0, 0);
   }
   __device__ __forceinline__ void store(unsigned char* xs, int t) const {
     u32x4* dst = reinterpret_cast<u32x4*>(xs + (t >> 3) * kPitch + (t & 7) * 16);
@@ -219,6 +238,7 @@ struct DecodeSmem {
   unsigned char xs[kNBuf][kTileBytes];  // row tiles: scored, multiplied, being stored
   uint16_t ps[2][HG][kPPitch];          // P by tile parity: [head][row], fp16
   int rowid[kMaxTopK];                  // row ids of the workgroup's K range
+  int rowpos[kMaxTopK];                 // fetch in the decode: host pool position of row k (-1: the KV tensor)
   float lexact[HG], mfin[HG];           // weight sum and reference max per head
   int overflow[kMaxPasses];             // a tile exceeded the reference max
   int nonfinite;                        // a score was inf or NaN: exact_fallback takes over
@@ -591,39 +611,78 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, DecodeSmem<HG>& 
 // loop runs three iterations per trip, and tiles past the range load row 0.
 constexpr int kLoadSets = 3;
 
-template <int HG, bool FP8>
-__device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned char* kv, int n_tiles, int lt) {
+// Where the loader reads the rows of a workgroup's tiles: the layer's KV
+// tensor, or, for rows this step fills when the decode fetches them, the
+// request's host pool rows; the workgroups of head group 0 then also write
+// those rows to their hot rows.
+struct RowSource {
+  const unsigned char* kv;
+  const unsigned char* host;       // the request's host pool rows (fetch in the decode)
+  __amdgpu_buffer_rsrc_t hot;      // the request's hot rows
+  int64_t hot_base;                // row id of the request's first hot row
+  bool writer;
+};
+
+template <int HG, bool FP8, bool FETCH>
+__device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const RowSource& rs, int n_tiles, int lt) {
   static_assert(kLoadSets == 3, "the loop below is unrolled for three register sets");
+  constexpr int RB = FP8 ? kRowBytesFp8 : kRowBytes;
   TileStage<FP8> st[kLoadSets];
+  int hoff[kLoadSets];  // hot-row write offset of each set's row (kNoHotWrite: none)
   const int row = lt >> 3;
   const int n_ids = n_tiles * kT;
-  // Row id of tile n for this thread; tiles past the range stage row 0
+  // Source of this thread's row of tile n; tiles past the range stage row 0
   // (their loads are issued anyway, so that every path has the same loads
   // in flight and the wait before a store names exactly its set's loads).
-  auto rid_of = [&](int n) {
-    const int i = n * kT + row;
-    const int r = sm.rowid[i < n_ids ? i : 0];
-    return i < n_ids ? r : -1;
+  struct Ref {
+    const unsigned char* src;
+    int hoff;
   };
-  int it = 0, rid = -1;
+  auto ref_of = [&](int n) {
+    const int i = n * kT + row;
+    const bool in = i < n_ids;
+    const int r = sm.rowid[in ? i : 0];
+    const int rid = in ? r : -1;
+    Ref x;
+    x.src = rs.kv + (size_t)(rid < 0 ? 0 : rid) * RB;
+    x.hoff = kNoHotWrite;
+    if constexpr (FETCH) {
+      const int pr = sm.rowpos[in ? i : 0];
+      const int pos = in ? pr : -1;
+      x.src = pos >= 0 ? rs.host + (size_t)pos * RB : x.src;
+      x.hoff = pos >= 0 && rs.writer ? (int)((rid - rs.hot_base) * RB) : kNoHotWrite;
+    }
+    return x;
+  };
+  int it = 0;
+  Ref nxt;
   // Iteration it stores tile it + 1 (from set (it + 1) % 3) and loads tile
   // it + 4 into the same set; stores past the range land in a buffer
   // nobody reads.
   auto step = [&](auto u) {
     constexpr int U = decltype(u)::value;
+    constexpr int S = (U + 1) % kLoadSets;
     const int nx = it + U + 1;
-    st[(U + 1) % kLoadSets].store(sm.xs[nx % kNBuf], lt);
-    st[(U + 1) % kLoadSets].load_row(kv, rid, lt);
-    rid = rid_of(nx + kLoadSets + 1);
+    st[S].store(sm.xs[nx % kNBuf], lt);
+    if constexpr (FETCH) st[S].store_hot(rs.hot, hoff[S], lt);
+    st[S].load_row(nxt.src, lt);
+    hoff[S] = nxt.hoff;
+    nxt = ref_of(nx + kLoadSets + 1);
     lds_barrier();
   };
   for (int p = 0; p < kMaxPasses; ++p) {
 #pragma unroll
-    for (int j = 0; j < kLoadSets; ++j) st[j].load_row(kv, rid_of(j), lt);
-    rid = rid_of(kLoadSets);
+    for (int j = 0; j < kLoadSets; ++j) {
+      const Ref x = ref_of(j);
+      st[j].load_row(x.src, lt);
+      hoff[j] = x.hoff;
+    }
+    nxt = ref_of(kLoadSets);
     st[0].store(sm.xs[0], lt);
-    st[0].load_row(kv, rid, lt);
-    rid = rid_of(kLoadSets + 1);
+    if constexpr (FETCH) st[0].store_hot(rs.hot, hoff[0], lt);
+    st[0].load_row(nxt.src, lt);
+    hoff[0] = nxt.hoff;
+    nxt = ref_of(kLoadSets + 1);
     lds_barrier();
     // iterations 0 .. n_tiles, three per trip so that each step's register
     // set is a constant, then the remaining one or two
@@ -649,8 +708,8 @@ __device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const unsigned c
 constexpr int kFbRows = 16;
 constexpr int kFbPitch = kLatent + 4;  // floats per staged row
 
-template <int HG, bool FP8>
-__device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<HG>& sm, const unsigned char* kv,
+template <int HG, bool FP8, bool FETCH>
+__device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<HG>& sm, const RowSource& rs,
                                                float kvs, size_t head0, int pair, int split, int hg, int n_rows,
                                                int tid) {
   static_assert(HG * kLatent * 2 + kFbRows * kFbPitch * 4 <= kNBuf * kTileBytes, "fallback staging fits the tiles");
@@ -676,13 +735,17 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
         const int rid = c0 + j < n_rows ? sm.rowid[c0 + j] : -1;
         float x0 = 0.f, x1 = 0.f;
         if (rid >= 0) {
+          // a row this step fills is read where the fast path read it
+          const int pos = FETCH ? sm.rowpos[c0 + j] : -1;
+          const unsigned char* row = pos >= 0 ? rs.host + (size_t)pos * (FP8 ? kRowBytesFp8 : kRowBytes)
+                                              : rs.kv + (size_t)rid * (FP8 ? kRowBytesFp8 : kRowBytes);
           if constexpr (FP8) {
-            const uint32_t w = *reinterpret_cast<const uint16_t*>(kv + (size_t)rid * kRowBytesFp8 + 2 * d2);
+            const uint32_t w = *(gu16*)(row + 2 * d2);
             const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
             x0 = v[0];
             x1 = v[1];
           } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(kv + (size_t)rid * kRowBytes + 4 * d2);
+            const uint32_t w = *(gu32*)(row + 4 * d2);
             x0 = __uint_as_float(w << 16);
             x1 = __uint_as_float(w & 0xFFFF0000u);
           }
@@ -760,21 +823,42 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
   for (int c = 0; c < 64; ++c) o.dst[c] = acc[c] * o.scale;
 }
 
+// Host pool position of entry k of query set `pair` (request r) when this
+// step fills its row (its fill-mask bit), else -1.  A position the host pool
+// does not hold is an error; the row is then read where it is (as the
+// separate miss fetch leaves such a row unwritten).
+__device__ __forceinline__ int fetch_pos(const DecodeArgs& a, int pair, int r, int k, int k1, int rid, int held) {
+  if (k >= k1 || rid < 0) return -1;
+  const uint64_t bits = a.fill_mask[(size_t)pair * a.mask_words + (k >> 6)];
+  if (!((bits >> (k & 63)) & 1ull)) return -1;
+  const int p = a.sel[(size_t)r * a.top_k + k];
+  if (p < 0 || p >= held) {
+    atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
+    return -1;
+  }
+  return p;
+}
+
 // Every role passes the same barriers: per pass one before the loop and one
 // per iteration (n_tiles + 1), one between passes, and the final
 // __syncthreads().
-template <int HG, bool FP8>
+// FETCH: the decode reads the rows this step fills from the host pool (and
+// head group 0 writes them to their hot rows): the miss fetch and the
+// decode in one pass over the rows.
+template <int HG, bool FP8, bool FETCH>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   __shared__ __align__(16) DecodeSmem<HG> sm;
   const int H = a.num_heads, R = a.num_requests, K = a.top_k;
-  // XCD-aware order: consecutive logical blocks (the head groups and splits
-  // of one request) share blockIdx % 8, i.e. one XCD and its L2.
+  // XCD-aware order: consecutive logical blocks share blockIdx % 8, i.e.
+  // one XCD and its L2, and the head groups of one key range are
+  // consecutive: they read the same rows (from HBM, or from the host pool
+  // when the decode fetches), which the second one finds in that L2.
   int li = blockIdx.x;
   if (gridDim.x % 8 == 0) li = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-  const int split = li % a.splits;
-  li /= a.splits;
   const int hg = li % nhg;
-  const int pair = li / nhg;
+  li /= nhg;
+  const int split = li % a.splits;
+  const int pair = li / a.splits;
   const int l = a.layer_begin + pair / R;
   const unsigned char* kv = a.kv[l];
   const float kvs = FP8 ? a.kv_scale[l] : 1.f;  // x = decode(code) * kvs for FP8 rows
@@ -796,10 +880,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
     sm.nonfinite = 0;
     sm.vbad = 0;
   }
+  constexpr int RB = FP8 ? kRowBytesFp8 : kRowBytes;
+  RowSource rs;
+  rs.kv = kv;
+  rs.host = nullptr;
+  rs.hot_base = 0;
+  rs.writer = false;
+  int held = 0;
+  if constexpr (FETCH) {
+    const int r = pair % R;
+    held = a.hv[(size_t)l * a.total_requests + r];
+    rs.host = reinterpret_cast<const unsigned char*>(a.host_rows[(size_t)l * a.total_requests + r]);
+    rs.hot_base = a.resident_rows + (int64_t)r * a.hot_slots;
+    rs.hot = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kv) + rs.hot_base * RB, 0,
+                                               a.hot_slots * RB, 0x00020000);
+    rs.writer = hg == 0;
+  } else {
+    rs.hot = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+  }
   int n_rows = k1 > k0 ? k1 - k0 : 0;
   if (a.part == 0) {
     const int n_pad = (n_rows + kT - 1) / kT * kT;
-    for (int k = tid; k < n_pad; k += kThreads) sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
+    for (int k = tid; k < n_pad; k += kThreads) {
+      const int rid = load_row_id(a, rows, k0 + k, k1);
+      sm.rowid[k] = rid;
+      if constexpr (FETCH) sm.rowpos[k] = fetch_pos(a, pair, pair % R, k0 + k, k1, rid, held);
+    }
   } else {
     const uint64_t* mask = a.fill_mask + (size_t)pair * a.mask_words;
     const bool want_filled = a.part == 2;
@@ -833,10 +939,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   else if (w < 8)
     value_role<HG, FP8>(a, sm, kvs, head0, pair, split, hg, n_tiles, w - 4, g, i16);
   else
-    loader_role<HG, FP8>(sm, kv, n_tiles, tid - 512);
+    loader_role<HG, FP8, FETCH>(sm, rs, n_tiles, tid - 512);
   // nonfinite is final after every role's last barrier.
   if (sm.nonfinite || sm.vbad) {
-    exact_fallback<HG, FP8>(a, sm, kv, kvs, head0, pair, split, hg, n_rows, tid);
+    exact_fallback<HG, FP8, FETCH>(a, sm, rs, kvs, head0, pair, split, hg, n_rows, tid);
     if (tid == 0) atomicAdd(a.fallback_count, 1u);
   }
 }
@@ -986,19 +1092,25 @@ hipError_t launch_decode(hisparse_pool* p, const DecodeArgs& a, hipStream_t s, b
   const int hgs = a.head_group > 0 ? a.head_group : head_group(a.num_heads);
   const int nhg = a.num_heads / hgs;
   const int grid = a.n_layers * a.num_requests * nhg * a.splits;
-  prof_begin(p, kKDecode, s);
+  prof_begin(p, a.fetch ? kKDecodeFetch : kKDecode, s);
   const bool fp8 = a.kv_dtype == HISPARSE_KV_FP8_E4M3;
   const dim3 gd(grid), bd(kThreads);
+#define HS_DECODE(HG_, FP8_)                                                          \
+  do {                                                                                \
+    if (a.fetch) hipLaunchKernelGGL((decode_ws<HG_, FP8_, true>), gd, bd, 0, s, a, nhg); \
+    else hipLaunchKernelGGL((decode_ws<HG_, FP8_, false>), gd, bd, 0, s, a, nhg);      \
+  } while (0)
   if (hgs == 64) {
-    if (fp8) hipLaunchKernelGGL((decode_ws<64, true>), gd, bd, 0, s, a, nhg);
-    else hipLaunchKernelGGL((decode_ws<64, false>), gd, bd, 0, s, a, nhg);
+    if (fp8) HS_DECODE(64, true);
+    else HS_DECODE(64, false);
   } else if (hgs == 32) {
-    if (fp8) hipLaunchKernelGGL((decode_ws<32, true>), gd, bd, 0, s, a, nhg);
-    else hipLaunchKernelGGL((decode_ws<32, false>), gd, bd, 0, s, a, nhg);
+    if (fp8) HS_DECODE(32, true);
+    else HS_DECODE(32, false);
   } else {
-    if (fp8) hipLaunchKernelGGL((decode_ws<16, true>), gd, bd, 0, s, a, nhg);
-    else hipLaunchKernelGGL((decode_ws<16, false>), gd, bd, 0, s, a, nhg);
+    if (fp8) HS_DECODE(16, true);
+    else HS_DECODE(16, false);
   }
+#undef HS_DECODE
   hipError_t e = hipGetLastError();
   prof_end(p, s);
   if (e != hipSuccess || a.split_total == 1 || !combine) return e;

@@ -145,6 +145,16 @@ struct DecodeArgs {
   const uint64_t* fill_mask;  // [n_layers][R][mask_words] (part != 0)
   int32_t mask_words;
   int32_t head_group;      // heads per workgroup (16, 32 or 64); 0: the default for num_heads
+  // Fetch in the decode: the entries this step fills (fill_mask) are read
+  // from the host pool, and the workgroups of head group 0 write them to
+  // their hot rows (rows holds those rows' ids).
+  int32_t fetch;
+  const int32_t* sel;          // [R][top_k] positions of the launch's selection (its layers share it)
+  const uint64_t* host_rows;   // [L * total_requests] device-visible addresses of the host pool rows
+  const int32_t* hv;           // [L][total_requests] positions below hv[l][r] are held by the host pool
+  int32_t total_requests;
+  int32_t hot_slots;
+  int64_t resident_rows;       // rows of the KV tensor before the hot buffers
   int32_t merge_from;      // > 0: partial slots [0, merge_from) of every (query set, head), written by an
                            // earlier launch over other entries, are merged into this launch's O and lse
                            // (which then has one split and split_total 1)
@@ -166,7 +176,7 @@ struct Layout {
 }  // namespace hs
 
 namespace hs {
-enum KernelId { kKMeta = 0, kKFetch = 1, kKDecode = 2, kKCombine = 3, kKCount = 4 };
+enum KernelId { kKMeta = 0, kKFetch = 1, kKDecode = 2, kKCombine = 3, kKDecodeFetch = 4, kKCount = 5 };
 constexpr int kProfCap = 8192;
 struct Profiler {
   bool on = false;
@@ -230,6 +240,9 @@ struct hisparse_pool {
   // fetch (beside the fetches), then the fetched rows.  -1 never, 0 where
   // the part after the fetch fills enough workgroups, 1 always.
   int resident_first = 0;
+  // hisparse_step reads the rows a step fills from the host pool inside the
+  // decode (-1: separate fetches; 0, 1: where it applies).
+  int fetch_in_decode = 0;
 };
 
 namespace hs {

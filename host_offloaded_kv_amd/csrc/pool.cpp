@@ -575,9 +575,12 @@ hisparse_status enqueue_fetch(hisparse_pool* p, int32_t layer, int32_t n_layers,
 // slots [split_base, split_base + splits) of split_total, merged by
 // combine_splits after the launch of part 2; or, with merge_from > 0, part
 // 2 in one launch that merges part 1's slots [0, merge_from) itself.
+// fetch_sel: non-null when the decode fetches the rows this step fills
+// from the host pool (the launch's selection, [R][K]).
 struct PartSpec {
   int part = 0, split_base = 0, split_total = 0, merge_from = 0, head_group = 0;
   bool combine = true;
+  const int32_t* fetch_sel = nullptr;
 };
 
 hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_layers, int32_t nreq,
@@ -606,10 +609,18 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.part = ps.part;
   a.merge_from = ps.merge_from;
   a.head_group = ps.head_group;
+  a.fetch = ps.fetch_sel != nullptr ? 1 : 0;
+  a.sel = ps.fetch_sel;
+  a.host_rows = p->host_rows_d;
+  a.hv = p->hv_d;
+  a.total_requests = p->cfg.num_requests;
+  a.hot_slots = p->cfg.hot_slots;
+  a.resident_rows = p->cfg.resident_rows_per_layer;
   a.mask_words = p->mask_words;
   a.fill_mask = p->fill_mask + ((size_t)layer_begin * p->cfg.num_requests) * p->mask_words;
   if ((ps.part != 0 && (n_layers != 1 || nreq != p->cfg.num_requests || p->T != 1)) ||
-      (ps.merge_from > 0 && (a.splits != 1 || a.split_total != 1 || ps.merge_from > kMaxMergeSlots))) {
+      (ps.merge_from > 0 && (a.splits != 1 || a.split_total != 1 || ps.merge_from > kMaxMergeSlots)) ||
+      (a.fetch && (ps.part != 0 || nreq != p->cfg.num_requests || p->T != 1))) {
     set_error("bad two-part decode launch");
     return HISPARSE_EINVAL;
   }
@@ -775,9 +786,27 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
                   (p->resident_first > 0 || (p->resident_first == 0 && resident_first_pays((int)R, (int)H)));
   int rf_before = 1, rf_after = 0;
   if (rf) resident_first_splits((int)R, (int)H, (int)K, &rf_before, &rf_after);
+  // The fetch in the decode: one decode launch over a group's layers reads
+  // the rows the step fills straight from the host pool (and writes them
+  // to their hot rows), so the step is the metadata kernel and that launch,
+  // on `stream` alone.  One verify token, no tail chunks; a step with a
+  // prefetch keeps the separate fetches, behind which the prefetch queues.
+  const bool fused = T == 1 && C == 1 && !pf && p->fetch_in_decode >= 0;
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
+    if (fused) {
+      hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
+                                           d_counts + (size_t)l0 * R * 3, s);
+      if (st) return st;
+      PartSpec ps;
+      ps.fetch_sel = d_topk + (size_t)g * R * W;
+      const size_t pr = (size_t)l0 * R;  // first query set of the group
+      st = enqueue_decode(p, l0, G, (int)R, d_q + pr * H * kLatent, d_rows + pr * K, scale, d_out + pr * H * kVDim,
+                          d_lse + pr * H, s, 0, false, ps);
+      if (st) return st;
+      continue;
+    }
     // One metadata launch for the whole group (its layers share the
     // selection).  Then a pipeline of units on two streams: the side stream
     // fetches unit after unit, the caller's stream decodes unit u as soon
@@ -1037,10 +1066,11 @@ hisparse_status hisparse_set_replacement(hisparse_pool* p, int32_t policy, uint6
 }
 
 hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_workgroups,
-                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first) {
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first,
+                                      int32_t fetch_in_decode) {
   if (!p || group_fetch_workgroups < 0 || group_fetch_workgroups > 65536 || unit_fetch_workgroups < 0 ||
       unit_fetch_workgroups > 65536 || tail_chunks < 0 || tail_chunks > kMaxTailChunks || resident_first < -1 ||
-      resident_first > 1) {
+      resident_first > 1 || fetch_in_decode < -1 || fetch_in_decode > 1) {
     set_error("hisparse_set_pipeline: bad argument");
     return HISPARSE_EINVAL;
   }
@@ -1048,6 +1078,7 @@ hisparse_status hisparse_set_pipeline(hisparse_pool* p, int32_t group_fetch_work
   p->fetch_wg_unit = unit_fetch_workgroups > 0 ? unit_fetch_workgroups : kDefaultUnitFetchWorkgroups;
   p->tail_chunks = tail_chunks > 0 ? tail_chunks : kDefaultTailChunks;
   p->resident_first = resident_first;
+  p->fetch_in_decode = fetch_in_decode;
   return HISPARSE_OK;
 }
 
@@ -1117,14 +1148,15 @@ hisparse_status hisparse_profile_enable(hisparse_pool* p, int32_t enable) {
 }
 
 hisparse_status hisparse_profile_read(hisparse_pool* p, hisparse_kernel_time* out, int32_t max, int32_t* n) {
-  static const char* names[kKCount] = {"resolve_meta", "fetch_rows", "sparse_mla_decode", "combine_splits"};
+  static const char* names[kKCount] = {"resolve_meta", "fetch_rows", "sparse_mla_decode", "combine_splits",
+                                       "sparse_mla_decode_fetch"};
   if (!p || !out || !n || max < 0) {
     set_error("hisparse_profile_read: bad argument");
     return HISPARSE_EINVAL;
   }
   Profiler& pr = p->prof;
-  double total[kKCount] = {0, 0, 0, 0};
-  int cnt[kKCount] = {0, 0, 0, 0};
+  double total[kKCount] = {};
+  int cnt[kKCount] = {};
   for (int i = 0; i < pr.n; ++i) {
     hipError_t e = hipEventSynchronize(pr.ev[2 * i + 1]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");

@@ -129,7 +129,7 @@ def load() -> ctypes.CDLL:
         "hisparse_step_prefetch": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP]),
         "hisparse_prefetch": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP]),
         "hisparse_reset_state": (_I32, [_VP, _VP]),
-        "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32, _I32]),
+        "hisparse_set_pipeline": (_I32, [_VP, _I32, _I32, _I32, _I32, _I32]),
         "hisparse_append": (_I32, [_VP, _VP, _VP]),
         "hisparse_set_replacement": (_I32, [_VP, _I32, ctypes.c_uint64, _VP]),
         "hisparse_writeback": (_I32, [_VP, _VP]),
@@ -264,9 +264,9 @@ def hisparse_reset_state(pool: int, stream: int) -> None:
 
 
 def hisparse_set_pipeline(pool: int, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
-                          tail_chunks: int = 0, resident_first: int = 0) -> None:
+                          tail_chunks: int = 0, resident_first: int = 0, fetch_in_decode: int = 0) -> None:
     _check(load().hisparse_set_pipeline(pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks,
-                                        resident_first))
+                                        resident_first, fetch_in_decode))
 
 
 def hisparse_set_replacement(pool: int, policy: int, seed: int, stream: int) -> None:
@@ -424,8 +424,9 @@ class HiSparse:
         hisparse_reset_state(self.pool, self.stream)
 
     def set_pipeline(self, group_fetch_workgroups: int = 0, unit_fetch_workgroups: int = 0,
-                     tail_chunks: int = 0, resident_first: int = 0) -> None:
-        hisparse_set_pipeline(self.pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks, resident_first)
+                     tail_chunks: int = 0, resident_first: int = 0, fetch_in_decode: int = 0) -> None:
+        hisparse_set_pipeline(self.pool, group_fetch_workgroups, unit_fetch_workgroups, tail_chunks, resident_first,
+                              fetch_in_decode)
 
     def set_replacement(self, policy: str, seed: int = 0) -> None:
         hisparse_set_replacement(self.pool, POLICIES[policy], seed, self.stream)

@@ -260,6 +260,9 @@ hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* pool, in
 
 /* One decode step over every layer: for each index-share group, RESOLVE all
  * of its layers with the group's selection, then decode each layer.
+ * By default (fetch_in_decode of hisparse_set_pipeline) the decode itself
+ * reads the rows the step fills from the host pool, one launch per group;
+ * the rest of this comment describes the pipeline of separate fetches. 
  *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],
  *   d_counts [L][R][3], d_out [L][R][H][512], d_lse [L][R][H].
  * Layer-ahead fetch (the shared selection of an index-share group is known
@@ -416,11 +419,19 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *     without key splits that merges the first; with fewer, both parts are
  *     split and combine_splits merges them.  1: always; -1: never (one
  *     launch after the fetch); 0 (default): where the merging launch
- *     applies, i.e. with at least 32 such workgroups.
+ *     applies, i.e. with at least 32 such workgroups;
+ *   fetch_in_decode: 0 or 1 (default): with one verify token, one tail
+ *     chunk and no prefetch, hisparse_step has no separate miss fetch: one
+ *     decode launch per index-share group reads the rows the step fills
+ *     straight from the pinned host pool into its tiles (the workgroups of
+ *     head group 0 also write them to their hot rows), so the step is the
+ *     metadata kernel and that launch on `stream`; -1: separate fetches
+ *     (the layer pipeline above), as a step with a prefetch always uses.
  * Results do not depend on these settings, except the rounding of O and
  * lse of the chunked or two-part layer.  Errors: EINVAL. */
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,
-                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first);
+                                      int32_t unit_fetch_workgroups, int32_t tail_chunks, int32_t resident_first,
+                                      int32_t fetch_in_decode);
 
 /* Copy the LRU state of (request r, layer l) -- the slot owners and LRU
  * stamps that the HiSparse summary article, section 02, keeps per device
@@ -453,8 +464,10 @@ hisparse_status hisparse_decode_fallback_count(hisparse_pool* pool, void* stream
 /* ---- measurement helpers (not on the decode path) ---- */
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
- * every kernel the pool enqueues (resolve metadata, miss fetch, decode,
- * split combine).  Off by default; while on, each launch adds two event
+ * every kernel the pool enqueues (resolve metadata "resolve_meta", miss
+ * fetch "fetch_rows", decode "sparse_mla_decode", the decode that also
+ * fetches "sparse_mla_decode_fetch", split merge "combine_splits").  Off
+ * by default; while on, each launch adds two event
  * records.  Up to 8192 launches are kept between reads; switching the
  * profiler on or off keeps them.  Launches enqueued under HIP graph capture
  * record their events when the graph is replayed. */

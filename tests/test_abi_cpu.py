@@ -92,7 +92,7 @@ def test_null_arguments_rejected():
     assert lib.hisparse_reset_state(None, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_set_replacement(None, 0, 0, None) == H.HISPARSE_EINVAL
     assert lib.hisparse_sparse_mla_decode_layers(None, 0, 1, None, None, 1.0, None, None, None) == H.HISPARSE_EINVAL
-    assert lib.hisparse_set_pipeline(None, 0, 0, 0, 0) == H.HISPARSE_EINVAL
+    assert lib.hisparse_set_pipeline(None, 0, 0, 0, 0, 0) == H.HISPARSE_EINVAL
     assert lib.hisparse_decode_fallback_count(None, None, None) == H.HISPARSE_EINVAL
     c, keep = _cfg()
     out = ctypes.c_void_p()

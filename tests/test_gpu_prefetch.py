@@ -194,17 +194,18 @@ def test_step_prefetch_full_size_exact_path():
     """r32_ctx128k_l4 with the exact next selection prefetched in every step:
     from step 1 on no miss, and row ids and LRU state bit-identical to the
     plain step path (the same victims, fetched one step earlier); O and lse
-    too, since the decode sees the same rows.  Both runs decode each group's
-    last layer in one launch: decoded resident rows first, its keys would be
-    split by hit or miss, which the prefetch changes (the results would then
-    agree to rounding only)."""
+    too, since the decode sees the same rows.  Both runs use separate
+    fetches and decode each group's last layer in one launch (the step with
+    a prefetch always fetches separately; decoded resident rows first, the
+    last layer's keys would be split by hit or miss, which the prefetch
+    changes, and the results would then agree to rounding only)."""
     import torch
 
     w = named_workload("r32_ctx128k_l4")
     steps = 5
     tr = w.trace(steps + 1)
     hs = make_pool(w)
-    hs.set_pipeline(resident_first=-1)
+    hs.set_pipeline(resident_first=-1, fetch_in_decode=-1)
     buf = _Buffers(w, hs.device)
     plain = []
     for t in range(steps):

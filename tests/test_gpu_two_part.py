@@ -1,5 +1,6 @@
 """GPU parity of the two-part decode of an index-share group's last layer
-(resident_first of hisparse_set_pipeline): the entries whose rows were in
+(resident_first of hisparse_set_pipeline, with separate fetches; the
+fetch in the decode is switched off here): the entries whose rows were in
 place before the layer's fetch are decoded beside the fetches, the entries
 the fetch fills after it, and the two parts' partial softmax sums are
 merged.  Attention over a set of keys is the same for any partition of the
@@ -43,7 +44,7 @@ def _gpu():
 
 
 def _force_two_part(hs):
-    hs.set_pipeline(resident_first=1)
+    hs.set_pipeline(resident_first=1, fetch_in_decode=-1)
 
 
 @pytest.mark.parametrize("variant", ["split_and_combine", "merge_in_second_part"])
@@ -68,7 +69,7 @@ def test_two_part_off_matches_on():
     snaps = {}
     for mode in (1, -1):
         hs = make_pool(w)
-        hs.set_pipeline(resident_first=mode)
+        hs.set_pipeline(resident_first=mode, fetch_in_decode=-1)
         run = GpuRun(w, hs)
         snaps[mode] = []
         for t in range(w.steps):
@@ -103,7 +104,7 @@ def test_two_part_fallback_merges(n_requests):
     sel0[0] = pos  # (the lists may lose their ascending order: any order is accepted)
     sel1[0] = pos
     hs = make_pool(w)
-    hs.set_pipeline(resident_first=1)
+    hs.set_pipeline(resident_first=1, fetch_in_decode=-1)
     dim = 5
     host = hs.host_rows_ptr(0, 0) + pos * 576 * 2 + dim * 2
     ctypes.c_uint16.from_address(host).value = int(f32_to_bf16_bits(np.array([70000.0], np.float32))[0])
