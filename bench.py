@@ -41,8 +41,8 @@ def pmc_ratio(workload: str, kernel: str, host_link: bool):
         return None
     with open(path) as f:
         ks = json.load(f).get("kernels", {})
-    names = {"sparse_mla_decode": ["decode_ws_unsplit", "decode_ws_split", "decode_ws_part1",
-                                   "decode_ws_part2"]}.get(kernel, [kernel])
+    names = {"sparse_mla_decode": ["decode_ws_unsplit", "decode_ws_split", "decode_ws_part1", "decode_ws_part2"],
+             "sparse_mla_decode_fetch": ["decode_ws_fetch"]}.get(kernel, [kernel])
     es = [ks[n] for n in names if n in ks and "alg_bytes_per_launch" in ks[n]]
     if not es:
         return None
@@ -50,7 +50,9 @@ def pmc_ratio(workload: str, kernel: str, host_link: bool):
         with open(os.path.join(ROOT, e["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest()[:16] != e["source_sha256_16"]:
                 return None
-    key = "read_per_alg_byte" if host_link else "traffic_per_alg_byte"
+    # the fetching decode's counters cover HBM and host-link bytes together:
+    # its ratio is to all its algorithmic bytes
+    key = "read_per_alg_byte" if host_link and kernel != "sparse_mla_decode_fetch" else "traffic_per_alg_byte"
     n = sum(e["launches"] for e in es)
     ratio = sum(e[key] * e["launches"] for e in es) / n
     rd = sum(e["read_bytes_per_launch"] * e["launches"] for e in es) / n
@@ -632,15 +634,20 @@ def main() -> int:
     d = kern[dom]
     pmc = pmc_ratio(w.name, dom, d["bound"] == "host_link") if T == 1 and args.kv_dtype == "bf16" else None
     traffic = None
-    if pmc is not None and d["alg_bytes_per_launch"]:
+    alg_for_traffic = d["alg_bytes_per_launch"]
+    if dom == "sparse_mla_decode_fetch":
+        # host reads and hot-row writes of the filled rows, and the decode's own bytes
+        alg_for_traffic = int(2 * d["alg_bytes_per_launch"] + d["decode_alg_bytes_per_launch"])
+    if pmc is not None and alg_for_traffic:
         # counted bytes of the timed launches: the counters' ratio to the
         # algorithmic bytes (host-link side: reads) times the timed launches'
         # algorithmic bytes
-        traffic = int(pmc[0] * d["alg_bytes_per_launch"])
+        traffic = int(pmc[0] * alg_for_traffic)
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
                 "frac": d["frac"], "traffic": traffic, "kernel": dom, "avg_us": d["avg_us"],
                 "alg_bytes_per_launch": d["alg_bytes_per_launch"],
                 "traffic_per_alg_byte": round(pmc[0], 4) if pmc else None,
+                "traffic_alg_bytes_per_launch": alg_for_traffic,
                 "counted_read_write_per_launch_pmc_steps": [int(pmc[1]), int(pmc[2])] if pmc else None}
 
     residency = None

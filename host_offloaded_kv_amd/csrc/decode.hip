@@ -1060,6 +1060,17 @@ int decode_splits(int n_layers, int num_requests, int num_heads, int top_k) {
   return splits;
 }
 
+// A decode that fetches is bound by the host link, not by the workgroup
+// count: at least 8 tiles per key split keep each workgroup's loads
+// streaming and halve the partials to merge (r8_ctx32k: 117 against 128 us
+// per step with the 2-tile minimum; miss_1m 88 against 90).
+constexpr int kMinTilesPerFetchSplit = 8;
+
+int fetch_decode_splits(int n_layers, int num_requests, int num_heads, int top_k) {
+  const int s = decode_splits(n_layers, num_requests, num_heads, top_k);
+  return std::max(1, std::min(s, top_k / (kMinTilesPerFetchSplit * kT)));
+}
+
 // With at least 32 (request, head group) workgroups, the part beside the
 // fetches runs without key splits (a whole fetch to hide under) and the
 // part after the fetch is one launch without key splits that merges it, on

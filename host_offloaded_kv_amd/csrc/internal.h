@@ -269,6 +269,9 @@ hipError_t launch_writeback(hisparse_pool* p, const WritebackArgs& a, hipStream_
 
 // decode.hip
 int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
+// Key splits of a decode that fetches the rows it fills (at most
+// decode_splits, so the workspace's partials cover it).
+int fetch_decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
 // A layer decoded resident rows first: `before` key splits for the part
 // beside the fetches; after the fetch either one launch without key splits
 // that also merges the first part's partials (*after = 0), or `after` key

@@ -803,7 +803,7 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       ps.fetch_sel = d_topk + (size_t)g * R * W;
       const size_t pr = (size_t)l0 * R;  // first query set of the group
       st = enqueue_decode(p, l0, G, (int)R, d_q + pr * H * kLatent, d_rows + pr * K, scale, d_out + pr * H * kVDim,
-                          d_lse + pr * H, s, 0, false, ps);
+                          d_lse + pr * H, s, fetch_decode_splits(G, (int)R, (int)H, (int)K), false, ps);
       if (st) return st;
       continue;
     }
