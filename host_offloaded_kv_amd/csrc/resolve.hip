@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   int32_t* stamp_g = a.stamp + pair * B;
   int32_t* lru_g = a.lru + pair * B;
   int16_t* map = a.posmap + (size_t)l * a.map_layer_stride + a.map_off[r];
+  const int32_t* bt = a.bt + a.bt_off[r];  // read here, not at first use: one dependent round trip less
 
   // Wave ranges: selection entries [jb, je), order-array entries [ib, ie).
   const int Kq = (K + kMetaThreads - 1) / kMetaThreads * 64;
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   }
 
   // Classify every entry: resident page, hot hit (stamp refresh + pin), miss.
-  const int32_t* bt = a.bt + a.bt_off[r];
+  // All gathers are consumed before the first store: a store issued between
+  // two loads would make the wait for the later load wait for the store too.
   int pv[SC], bv[SC], sv[SC];
 #pragma unroll
   for (int c = 0; c < SC; ++c) {
@@ -355,37 +357,38 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     bv[c] = p >= 0 ? bt[p >> page_shift] : -1;
     sv[c] = p >= 0 ? (int)map[p] : -1;
   }
-  int n_res = 0, n_hit = 0, mloc = 0;
-  uint64_t mb[SC];
+  int n_res = 0, n_hit = 0, mloc = 0;  // wave totals (uniform)
+  uint64_t mb[SC], hb[SC];              // ballots: misses, hot hits
+  int rowv[SC];                         // row id of a resident or hit entry, -1 for padding
 #pragma unroll
   for (int c = 0; c < SC; ++c) {
     const int j = jb + 64 * c + lane;
     const int p = pv[c];
-    bool miss = false;
-    if (c < njc && j < je) {
-      int row = -1;
-      if (p >= 0) {
-        if (bv[c] >= 0) {
-          row = (bv[c] << page_shift) + (p & page_mask);
-          ++n_res;
-        } else if (sv[c] >= 0) {
-          const int s = sv[c];
-          if (pf || a.policy == HISPARSE_POLICY_FIFO) {
-            tflag_s[s] |= 1;  // pinned; the stamp stays (FIFO: fill step; prefetch: a guess refreshes nothing)
-          } else {
-            tflag_s[s] |= 5;
-            stamp_g[s] = t;
-          }
-          row = (int)(hot_base + s);
-          ++n_hit;
-        } else {
-          miss = true;
-        }
-      }
-      if (!miss && !pf) rows_out[j] = row;
-    }
+    const bool in = c < njc && j < je && p >= 0;
+    const bool res = in && bv[c] >= 0;
+    const bool hit = in && !res && sv[c] >= 0;
+    const bool miss = in && !res && !hit;
+    rowv[c] = res ? (bv[c] << page_shift) + (p & page_mask) : hit ? (int)(hot_base + sv[c]) : -1;
     mb[c] = __ballot(miss);
+    hb[c] = __ballot(hit);
     mloc += __popcll(mb[c]);
+    n_hit += __popcll(hb[c]);
+    n_res += __popcll(__ballot(res));
+  }
+  // Pin and stamp the hits (LRU: refreshed to t; FIFO keeps the fill step
+  // and a prefetch, a guess, refreshes nothing); write the rows of every
+  // entry that is not a miss.  Before this call of the step no slot holds
+  // a flag unless an earlier call of the same step stamped it.
+  const unsigned char hit_flag = (pf || a.policy == HISPARSE_POLICY_FIFO) ? 1 : 5;
+#pragma unroll
+  for (int c = 0; c < SC; ++c) {
+    const int j = jb + 64 * c + lane;
+    if ((hb[c] >> lane) & 1) {
+      const int s = sv[c];
+      tflag_s[s] = same_step ? (unsigned char)(tflag_s[s] | hit_flag) : hit_flag;
+      if (hit_flag == 5) stamp_g[s] = t;
+    }
+    if (c < njc && j < je && !((mb[c] >> lane) & 1) && !pf) rows_out[j] = rowv[c];
   }
   // The entries this call fills, one bit each (wave ranges start on 64).
   if (a.fill_mask && !pf && lane == 0) {
@@ -394,7 +397,11 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     for (int c = 0; c < SC; ++c)
       if (c < njc && jb + 64 * c < je) fm[(jb >> 6) + c] = mb[c];
   }
-  if (lane == 0) cnt_s[0][wid] = mloc;
+  if (lane == 0) {
+    cnt_s[0][wid] = mloc;
+    red_s[0][wid] = n_res;
+    red_s[1][wid] = n_hit;
+  }
   __syncthreads();
   int m;
   {
@@ -485,18 +492,31 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   // Fill: i-th smallest missing position -> i-th victim.  The evicted
   // position cannot be in this selection (its slot would be pinned), so the
   // map entries cleared and set here are all distinct.
+  // The victims' owners are all read before the first store (as in the
+  // classification); m <= W <= SC * kMetaThreads.
   int2* fetch = a.fetch + cpair * K;
-  for (int i = tid; i < m; i += kMetaThreads) {
-    const unsigned long long x = key_s[i];
-    const int v = vic_s[i], p = (int)(x >> 32), j = (int)(uint32_t)x;
-    const int old = owner_g[v];
-    if (old >= 0) map[old] = -1;
-    map[p] = (int16_t)v;
-    owner_g[v] = p;
-    stamp_g[v] = t;
-    tflag_s[v] |= 5;
-    if (!pf) rows_out[j] = (int)(hot_base + v);
-    fetch[i] = make_int2(p, v);
+  int fv[SC], fold[SC];
+#pragma unroll
+  for (int c = 0; c < SC; ++c) {
+    const int i = tid + c * kMetaThreads;
+    fv[c] = i < m ? vic_s[i] : 0;
+    fold[c] = i < m ? owner_g[fv[c]] : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < SC; ++c) {
+    const int i = tid + c * kMetaThreads;
+    if (i < m) {
+      const unsigned long long x = key_s[i];
+      const int v = fv[c], p = (int)(x >> 32), j = (int)(uint32_t)x;
+      if (fold[c] >= 0) map[fold[c]] = -1;
+      map[p] = (int16_t)v;
+      owner_g[v] = p;
+      stamp_g[v] = t;
+      // a victim is unpinned: no flag but "stamped earlier this step"
+      tflag_s[v] = same_step ? (unsigned char)(tflag_s[v] | 5) : 5;
+      if (!pf) rows_out[j] = (int)(hot_base + v);
+      fetch[i] = make_int2(p, v);
+    }
   }
   __syncthreads();  // also makes every row id written above visible to the workgroup
   if (!fast && !pf) {
@@ -540,15 +560,8 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     }
   }
 
-  n_res = wave_sum(n_res);
-  n_hit = wave_sum(n_hit);
   if (errbits) atomicOr(a.err, errbits);
-  if (lane == 0) {
-    red_s[0][wid] = n_res;
-    red_s[1][wid] = n_hit;
-  }
-  __syncthreads();
-  if (tid == 0) {
+  if (tid == 0) {  // red_s was written before the classification barrier
     int tr = 0, th = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kMetaWaves; ++w2) {
