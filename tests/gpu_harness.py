@@ -138,13 +138,15 @@ def check_attention(run, dec, t, sel_t, pairs):
 
 
 def run_and_compare(w, steps=None, attend_every=1, attend_pairs=None, state_pairs=None,
-                    bytes_pairs=None, requests_for_oracle=None, label="", trace=None, setup=None):
+                    bytes_pairs=None, requests_for_oracle=None, label="", trace=None, setup=None,
+                    host_coherent=0):
     """Run ``steps`` decode steps on the GPU and check each one (``trace``:
     the selections to use instead of the workload's own sorted trace;
-    ``setup``: called with the pool before the first step)."""
+    ``setup``: called with the pool before the first step; ``host_coherent``:
+    the host pool's memory type)."""
     steps = w.steps if steps is None else steps
     tr = w.trace(steps) if trace is None else trace
-    hs = make_pool(w)
+    hs = make_pool(w, host_coherent=host_coherent)
     if setup is not None:
         setup(hs)
     run = GpuRun(w, hs)

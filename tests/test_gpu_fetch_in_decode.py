@@ -10,7 +10,8 @@ with separate miss fetches, including a request with two head groups (both
 read the row from the host pool, one writes it) and FP8 rows.  A value
 beyond fp16 planted in a host row sends the workgroup that reads it to the
 exact fp32 path, which reads the row from the host pool as well; a step
-later the row is a hit and is read from the hot row the decode wrote.
+later the row is a hit and is read from the hot row the decode wrote.  Both
+pipelines also run on a host pool in coherent pinned memory.
 """
 
 import ctypes
@@ -76,6 +77,19 @@ def test_fetch_in_decode_matches_oracle_and_separate_fetches(kind):
             assert np.abs(fused[2][l, r] - sep[2][l, r]).max() / den <= O_TOL
             assert np.abs(fused[3][l, r] - sep[3][l, r]).max() <= LSE_TOL
     assert hs.check_errors() == 0
+    hs.close()
+
+
+@pytest.mark.parametrize("pipeline", ["fetch_in_decode", "separate_fetches"])
+def test_coherent_host_pool(pipeline):
+    """The host pool in coherent pinned memory (host_coherent = 1): reads
+    of it are not cached on the device, so both head groups of a request
+    read a filled row over the link; the results are the same."""
+    w = _workload("two_head_groups")
+    setup = None if pipeline == "fetch_in_decode" else (lambda hs: hs.set_pipeline(fetch_in_decode=-1))
+    pairs = [(l, r) for l in range(w.num_layers) for r in range(w.num_requests)]
+    hs, _, _ = run_and_compare(w, label=f"coherent host pool, {pipeline}", bytes_pairs=pairs, setup=setup,
+                               host_coherent=1)
     hs.close()
 
 
