@@ -358,6 +358,10 @@ __device__ __forceinline__ void score_tiles(DecodeSmem<HG>& sm, const f32x4 (&q)
 // row sets m, and P = 2^(s*scale*log2e - m) accumulates unnormalised, so
 // the O accumulators are never rescaled inside the loop.  Both passes give
 // the exact softmax.
+template <int HG>
+__device__ __forceinline__ void merge_prepare(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, int pair, int hg,
+                                              int h, float mo, float lo);
+
 template <int HG, bool FP8>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, DecodeSmem<HG>& sm, float kvs, size_t head0,
                                            int pair, int hg, int n_tiles, int w, int g, int i16) {
@@ -823,22 +827,6 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
   for (int c = 0; c < 64; ++c) o.dst[c] = acc[c] * o.scale;
 }
 
-// Host pool position of entry k of query set `pair` (request r) when this
-// step fills its row (its fill-mask bit), else -1.  A position the host pool
-// does not hold is an error; the row is then read where it is (as the
-// separate miss fetch leaves such a row unwritten).
-__device__ __forceinline__ int fetch_pos(const DecodeArgs& a, int pair, int r, int k, int k1, int rid, int held) {
-  if (k >= k1 || rid < 0) return -1;
-  const uint64_t bits = a.fill_mask[(size_t)pair * a.mask_words + (k >> 6)];
-  if (!((bits >> (k & 63)) & 1ull)) return -1;
-  const int p = a.sel[(size_t)r * a.top_k + k];
-  if (p < 0 || p >= held) {
-    atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
-    return -1;
-  }
-  return p;
-}
-
 // Every role passes the same barriers: per pass one before the loop and one
 // per iteration (n_tiles + 1), one between passes, and the final
 // __syncthreads().
@@ -902,9 +890,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   if (a.part == 0) {
     const int n_pad = (n_rows + kT - 1) / kT * kT;
     for (int k = tid; k < n_pad; k += kThreads) {
-      const int rid = load_row_id(a, rows, k0 + k, k1);
-      sm.rowid[k] = rid;
-      if constexpr (FETCH) sm.rowpos[k] = fetch_pos(a, pair, pair % R, k0 + k, k1, rid, held);
+      if constexpr (FETCH) {
+        // The row id, its fill-mask word and its position are independent
+        // loads: issued together and unconditionally (entries past the range
+        // read entry k0 and are dropped), so that none waits for another.
+        const int kk = k0 + k;
+        const bool in = kk < k1;
+        const int kc = in ? kk : k0;
+        const int r_in = rows[kc];
+        const uint64_t word = a.fill_mask[(size_t)pair * a.mask_words + (kc >> 6)];
+        const int p_in = a.sel[(size_t)(pair % R) * a.top_k + kc];
+        const bool rbad = in & ((r_in < -1) | (r_in >= a.kv_rows));
+        const int rid = (in & !rbad) ? r_in : -1;
+        const bool filled = (rid >= 0) & (((word >> (kc & 63)) & 1ull) != 0);
+        const bool pbad = filled & ((p_in < 0) | (p_in >= held));
+        sm.rowid[k] = rid;
+        sm.rowpos[k] = (filled & !pbad) ? p_in : -1;
+        if (rbad) atomicOr(a.err, HISPARSE_ERR_ROW);
+        if (pbad) atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
+      } else {
+        sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
+      }
     }
   } else {
     const uint64_t* mask = a.fill_mask + (size_t)pair * a.mask_words;
