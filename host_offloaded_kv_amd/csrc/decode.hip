@@ -875,8 +875,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   rs.hot_base = 0;
   rs.writer = false;
   int held = 0;
+  int q = 0;             // query set within its layer: token q % tokens of request q / tokens
+  size_t mask_bit0 = 0;  // fill-mask bit of this query set's entry 0
   if constexpr (FETCH) {
-    const int r = pair % R;
+    q = pair % R;
+    const int r = q / a.tokens;
+    mask_bit0 = ((size_t)(pair / R) * (R / a.tokens) + r) * a.mask_words * 64 + (size_t)(q - r * a.tokens) * K;
     held = a.hv[(size_t)l * a.total_requests + r];
     rs.host = reinterpret_cast<const unsigned char*>(a.host_rows[(size_t)l * a.total_requests + r]);
     rs.hot_base = a.resident_rows + (int64_t)r * a.hot_slots;
@@ -897,12 +901,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
         const int kk = k0 + k;
         const bool in = kk < k1;
         const int kc = in ? kk : k0;
+        const size_t bit = mask_bit0 + kc;
         const int r_in = rows[kc];
-        const uint64_t word = a.fill_mask[(size_t)pair * a.mask_words + (kc >> 6)];
-        const int p_in = a.sel[(size_t)(pair % R) * a.top_k + kc];
+        const uint64_t word = a.fill_mask[bit >> 6];
+        const int p_in = a.sel[(size_t)q * K + kc];
         const bool rbad = in & ((r_in < -1) | (r_in >= a.kv_rows));
         const int rid = (in & !rbad) ? r_in : -1;
-        const bool filled = (rid >= 0) & (((word >> (kc & 63)) & 1ull) != 0);
+        const bool filled = (rid >= 0) & (((word >> (bit & 63)) & 1ull) != 0);
         const bool pbad = filled & ((p_in < 0) | (p_in >= held));
         sm.rowid[k] = rid;
         sm.rowpos[k] = (filled & !pbad) ? p_in : -1;

@@ -142,14 +142,16 @@ struct DecodeArgs {
   int32_t out_partial;     // 1: the launch writes partial slots (merged later); 0: O and lse
   int32_t part;            // entries attended: 0 all; 1 those whose row was in place before this step's
                            // fetch (fill_mask bit clear); 2 those filled by it (bit set)
-  const uint64_t* fill_mask;  // [n_layers][R][mask_words] (part != 0)
+  const uint64_t* fill_mask;  // [n_layers][total_requests][mask_words], one bit per selection entry
+                              // of a (layer, request), all verify tokens (part != 0, fetch)
   int32_t mask_words;
   int32_t head_group;      // heads per workgroup (16, 32 or 64); 0: the default for num_heads
   // Fetch in the decode: the entries this step fills (fill_mask) are read
   // from the host pool, and the workgroups of head group 0 write them to
   // their hot rows (rows holds those rows' ids).
   int32_t fetch;
-  const int32_t* sel;          // [R][top_k] positions of the launch's selection (its layers share it)
+  int32_t tokens;              // verify tokens: query set q is token q % tokens of request q / tokens
+  const int32_t* sel;          // [R][top_k] positions of each query set (its layers share them)
   const uint64_t* host_rows;   // [L * total_requests] device-visible addresses of the host pool rows
   const int32_t* hv;           // [L][total_requests] positions below hv[l][r] are held by the host pool
   int32_t total_requests;

@@ -152,7 +152,7 @@ Layout make_layout(const hisparse_config* c) {
   L.fetch = off; off = align256(off + NL * R * W * 8);
   L.pf_miss_count = off; off = align256(off + NL * R * 4);
   L.pf_fetch = off; off = align256(off + NL * R * W * 8);
-  L.fill_mask = off; off = align256(off + NL * R * ((c->top_k + 63) / 64) * 8);
+  L.fill_mask = off; off = align256(off + NL * R * ((W + 63) / 64) * 8);
   L.bt = off; off = align256(off + (size_t)bt_entries * 4);
   L.bt_off = off; off = align256(off + R * 4);
   L.ctx = off; off = align256(off + R * 4);
@@ -378,7 +378,7 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
   p->pf_miss_count = (int32_t*)(w + lay.pf_miss_count);
   p->pf_fetch = (int2*)(w + lay.pf_fetch);
   p->fill_mask = (uint64_t*)(w + lay.fill_mask);
-  p->mask_words = (cfg->top_k + 63) / 64;
+  p->mask_words = (p->W + 63) / 64;
   p->bt = (int32_t*)(w + lay.bt);
   p->bt_off = (int32_t*)(w + lay.bt_off);
   p->ctx_d = (int32_t*)(w + lay.ctx);
@@ -527,9 +527,8 @@ hisparse_status enqueue_resolve(hisparse_pool* p, int32_t layer_begin, int32_t n
   a.resident_rows = p->cfg.resident_rows_per_layer;
   a.policy = p->policy;
   a.policy_seed = p->policy_seed;
-  // The fill mask serves the two-part decode of a one-token selection.
-  a.fill_mask = (!prefetch && p->T == 1) ? p->fill_mask + (size_t)layer_begin * p->cfg.num_requests * p->mask_words
-                                         : nullptr;
+  // The fill mask serves the decode that fetches and the two-part decode.
+  a.fill_mask = !prefetch ? p->fill_mask + (size_t)layer_begin * p->cfg.num_requests * p->mask_words : nullptr;
   a.posmap = p->posmap;
   a.map_off = p->map_off;
   a.map_layer_stride = p->lay.posmap_entries / p->cfg.num_layers;
@@ -610,6 +609,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.merge_from = ps.merge_from;
   a.head_group = ps.head_group;
   a.fetch = ps.fetch_sel != nullptr ? 1 : 0;
+  a.tokens = (int32_t)p->T;
   a.sel = ps.fetch_sel;
   a.host_rows = p->host_rows_d;
   a.hv = p->hv_d;
@@ -620,7 +620,7 @@ hisparse_status enqueue_decode(hisparse_pool* p, int32_t layer_begin, int32_t n_
   a.fill_mask = p->fill_mask + ((size_t)layer_begin * p->cfg.num_requests) * p->mask_words;
   if ((ps.part != 0 && (n_layers != 1 || nreq != p->cfg.num_requests || p->T != 1)) ||
       (ps.merge_from > 0 && (a.splits != 1 || a.split_total != 1 || ps.merge_from > kMaxMergeSlots)) ||
-      (a.fetch && (ps.part != 0 || nreq != p->cfg.num_requests || p->T != 1))) {
+      (a.fetch && (ps.part != 0 || (size_t)nreq != (size_t)p->cfg.num_requests * p->T))) {
     set_error("bad two-part decode launch");
     return HISPARSE_EINVAL;
   }
@@ -789,9 +789,9 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
   // The fetch in the decode: one decode launch over a group's layers reads
   // the rows the step fills straight from the host pool (and writes them
   // to their hot rows), so the step is the metadata kernel and that launch,
-  // on `stream` alone.  One verify token, no tail chunks; a step with a
-  // prefetch keeps the separate fetches, behind which the prefetch queues.
-  const bool fused = T == 1 && C == 1 && !pf && p->fetch_in_decode >= 0;
+  // on `stream` alone.  No tail chunks; a step with a prefetch keeps the
+  // separate fetches, behind which the prefetch queues.
+  const bool fused = C == 1 && !pf && p->fetch_in_decode >= 0;
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
@@ -801,9 +801,10 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       if (st) return st;
       PartSpec ps;
       ps.fetch_sel = d_topk + (size_t)g * R * W;
-      const size_t pr = (size_t)l0 * R;  // first query set of the group
-      st = enqueue_decode(p, l0, G, (int)R, d_q + pr * H * kLatent, d_rows + pr * K, scale, d_out + pr * H * kVDim,
-                          d_lse + pr * H, s, fetch_decode_splits(G, (int)R, (int)H, (int)K), false, ps);
+      const size_t pr = (size_t)l0 * R * T;  // first query set of the group
+      st = enqueue_decode(p, l0, G, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                          d_out + pr * H * kVDim, d_lse + pr * H, s, fetch_decode_splits(G, (int)(R * T), (int)H, (int)K),
+                          false, ps);
       if (st) return st;
       continue;
     }

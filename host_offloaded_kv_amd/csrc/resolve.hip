@@ -71,9 +71,10 @@ constexpr int kSelChunksMax = kMaxTopK / kMetaThreads;  // entries per thread of
 // selection in input order (2 W' int32 positions and 2 W' int32 earliest
 // entries, W' = W rounded up to a power of two), and, for random
 // replacement, B 64-bit keys (the misses stay in the key region while the
-// victims are sorted).
+// victims are sorted).  Several tokens add the fill mask (W bits), which
+// their cross-token copies extend before it is written out.
 struct LdsMap {
-  size_t sel, key, vic, tflag, aux, total;
+  size_t sel, key, vic, tflag, aux, fm, total;
 };
 
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -95,7 +96,8 @@ __host__ __device__ inline LdsMap lds_map(int W, int B, bool random, bool one_to
   m.aux = round16(m.tflag + (size_t)B);
   const size_t hash = one_token ? 8 * hash_entries(W) : 0;
   const size_t rkey = random ? 8 * (size_t)next_pow2(B) : 0;
-  m.total = m.aux + (hash > rkey ? hash : rkey);
+  m.fm = round16(m.aux + (hash > rkey ? hash : rkey));
+  m.total = m.fm + (one_token ? 0 : 8 * (size_t)((W + 63) / 64));
   return m;
 }
 
@@ -390,9 +392,12 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     }
     if (c < njc && j < je && !((mb[c] >> lane) & 1) && !pf) rows_out[j] = rowv[c];
   }
-  // The entries this call fills, one bit each (wave ranges start on 64).
-  if (a.fill_mask && !pf && lane == 0) {
-    uint64_t* fm = a.fill_mask + cpair * ((K + 63) / 64);
+  // The entries this call fills, one bit each (wave ranges start on 64);
+  // with several tokens the mask goes through LDS first (see below).
+  const bool fill_mask = a.fill_mask && !pf;
+  uint64_t* fm_s = (uint64_t*)(smem + M.fm);
+  if (fill_mask && lane == 0) {
+    uint64_t* fm = one_token ? a.fill_mask + cpair * ((K + 63) / 64) : fm_s;
 #pragma unroll
     for (int c = 0; c < SC; ++c)
       if (c < njc && jb + 64 * c < je) fm[(jb >> 6) + c] = mb[c];
@@ -415,7 +420,21 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
       run += __popcll(mb[c]);
     }
   }
+  if (fill_mask && !one_token) {
+    // An entry of a later token that repeats a filled position reads the
+    // same row, which is being written in this step: it is marked as
+    // filled too (the decode then reads it from the host pool as well).
+    for (int j = tid; j < K; j += kMetaThreads) {
+      const int p = sel_s[j];
+      if (p <= -2) {
+        const int e = -2 - p;
+        if ((fm_s[e >> 6] >> (e & 63)) & 1ull) atomicOr((unsigned long long*)&fm_s[j >> 6], 1ull << (j & 63));
+      }
+    }
+  }
   __syncthreads();
+  if (fill_mask && !one_token)
+    for (int i = tid; i < (K + 63) / 64; i += kMetaThreads) a.fill_mask[cpair * ((K + 63) / 64) + i] = fm_s[i];
 
   if (!fast && m > 1 && m <= kMetaThreads) {
     // Ascending position order of the misses: thread i counts the keys

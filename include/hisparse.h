@@ -262,7 +262,7 @@ hisparse_status hisparse_sparse_mla_decode_layers_static(hisparse_pool* pool, in
  * of its layers with the group's selection, then decode each layer.
  * By default (fetch_in_decode of hisparse_set_pipeline) the decode itself
  * reads the rows the step fills from the host pool, one launch per group;
- * the rest of this comment describes the pipeline of separate fetches. 
+ * the rest of this comment describes the pipeline of separate fetches.
  *   d_topk [L/g][R][K], d_q [L][R][H][576], d_rows [L][R][K],
  *   d_counts [L][R][3], d_out [L][R][H][512], d_lse [L][R][H].
  * Layer-ahead fetch (the shared selection of an index-share group is known
@@ -420,13 +420,15 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *     split and combine_splits merges them.  1: always; -1: never (one
  *     launch after the fetch); 0 (default): where the merging launch
  *     applies, i.e. with at least 32 such workgroups;
- *   fetch_in_decode: 0 or 1 (default): with one verify token, one tail
- *     chunk and no prefetch, hisparse_step has no separate miss fetch: one
- *     decode launch per index-share group reads the rows the step fills
- *     straight from the pinned host pool into its tiles (the workgroups of
- *     head group 0 also write them to their hot rows), so the step is the
- *     metadata kernel and that launch on `stream`; -1: separate fetches
- *     (the layer pipeline above), as a step with a prefetch always uses.
+ *   fetch_in_decode: 0 or 1 (default): with one tail chunk and no
+ *     prefetch, hisparse_step has no separate miss fetch: one decode launch
+ *     per index-share group reads the rows the step fills straight from the
+ *     pinned host pool into its tiles (the workgroups of head group 0 also
+ *     write them to their hot rows; with several verify tokens an entry
+ *     that shares a filled row with an earlier token's entry reads it from
+ *     the host pool too), so the step is the metadata kernel and that launch
+ *     on `stream`; -1: separate fetches (the layer pipeline above), as a
+ *     step with a prefetch always uses.
  * Results do not depend on these settings, except the rounding of O and
  * lse of the chunked or two-part layer.  Errors: EINVAL. */
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,

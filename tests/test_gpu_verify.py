@@ -4,7 +4,10 @@ every (request, token) with its own query.
 
 Bit-exact: row ids of every entry (copies across tokens share a row),
 counts over distinct positions, LRU state and hot-row bytes; attention per
-token within the usual bound.
+token within the usual bound.  The small configurations run both step
+pipelines: the decode that reads the filled rows from the host pool (an
+entry of a later token that shares a filled row reads it there too) and
+separate miss fetches.
 """
 
 import numpy as np
@@ -29,7 +32,7 @@ def _gpu():
     fill.build(force=False)
 
 
-def _run(w, steps, attend_every=1, attend_pairs=None, dup_step=None):
+def _run(w, steps, attend_every=1, attend_pairs=None, dup_step=None, fetch_in_decode=1):
     import torch
 
     T, L, R, K, H = w.num_verify, w.num_layers, w.num_requests, w.top_k, w.num_heads
@@ -37,6 +40,7 @@ def _run(w, steps, attend_every=1, attend_pairs=None, dup_step=None):
     if dup_step is not None:
         tr[dup_step, 0, 0, T - 1, 1] = tr[dup_step, 0, 0, T - 1, 0]  # a repeat inside one token's list
     hs = make_pool(w)
+    hs.set_pipeline(fetch_in_decode=fetch_in_decode)
     dev = hs.device
     rows = torch.empty((L, R, T, K), dtype=torch.int32, device=dev)
     counts = torch.empty((L, R, 3), dtype=torch.int32, device=dev)
@@ -76,8 +80,9 @@ def _run(w, steps, attend_every=1, attend_pairs=None, dup_step=None):
     return flags
 
 
+@pytest.mark.parametrize("pipeline", [1, -1], ids=["fetch_in_decode", "separate_fetches"])
 @pytest.mark.parametrize("case", range(4))
-def test_verify_small_configs(case):
+def test_verify_small_configs(case, pipeline):
     rng = np.random.default_rng(900 + case)
     T = int(rng.choice([2, 3, 4]))
     K = int(rng.choice([16, 50, 128]))
@@ -92,7 +97,7 @@ def test_verify_small_configs(case):
     if case == 3:
         w = with_fp8(w)
     log(f"verify config {case}: T={T} R={R} L={L} g={share} K={K} B={B} ctx={ctx} res={w.residency} {w.kv_dtype}")
-    flags = _run(w, w.steps, dup_step=3 if case == 1 else None)
+    flags = _run(w, w.steps, dup_step=3 if case == 1 else None, fetch_in_decode=pipeline)
     from host_offloaded_kv_amd.hisparse import HISPARSE_ERR_DUP
 
     assert flags == (HISPARSE_ERR_DUP if case == 1 else 0)
