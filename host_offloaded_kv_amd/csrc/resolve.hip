@@ -54,7 +54,7 @@ __device__ __forceinline__ void wait_vmem_and_sync() {
   __syncthreads();
 }
 
-int ceil_log2(int64_t v) {
+[[maybe_unused]] int ceil_log2(int64_t v) {
   int b = 0;
   while ((int64_t{1} << b) < v) ++b;
   return b;
@@ -63,6 +63,7 @@ int ceil_log2(int64_t v) {
 constexpr int kMetaThreads = 1024;  // 16 wavefronts per (request, layer)
 constexpr int kMetaWaves = kMetaThreads / 64;
 constexpr int kSelChunksMax = kMaxTopK / kMetaThreads;  // entries per thread of a one-token selection
+constexpr int kHashTokensMax = 8;  // several tokens: repeats found by a hash up to this many tokens, else a sort
 
 // LDS of one metadata workgroup: the selection (W int32), the sort and
 // miss-list region (W 64-bit keys, a power of two), the victims (W int32),
@@ -319,12 +320,72 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
       }
     }
     __syncthreads();
+  } else if (!fast && K / a.tok_k <= kHashTokensMax) {
+    // Repeated positions of several tokens' selections: the earliest entry
+    // of each position is the one resolved; a later entry of the same
+    // token's list is an error (padding); an entry of a later token shares
+    // the row of the earliest entry, which it names as sel = -2 - index
+    // (padding to the classification below).  An LDS hash keyed by
+    // position (linear probing over HN >= W slots in the key and victim
+    // regions, unused until the classification) holds per position the
+    // earliest entry overall (atomic minimum) and, one token after the
+    // other, the earliest entry of the current token (atomic maximum of
+    // (token << 16) | (65535 - entry), larger than every earlier token's).
+    const int T = K / a.tok_k;
+    const int HN = (int)((M.tflag - M.key) / 12);
+    int* hpos = (int*)key_s;
+    int* hfirst = hpos + HN;
+    int* hcur = hfirst + HN;
+    for (int i = tid; i < HN; i += kMetaThreads) {
+      hpos[i] = -1;
+      hfirst[i] = INT_MAX;
+      hcur[i] = -1;
+    }
+    __syncthreads();
+    for (int tk = 0; tk < T; ++tk) {
+      int hs[kSelChunksMax];
+#pragma unroll
+      for (int c = 0; c < kSelChunksMax; ++c) {
+        const int jt = tid + c * kMetaThreads;
+        const int j = tk * a.tok_k + jt;
+        hs[c] = -1;
+        const int p = jt < a.tok_k ? sel_s[j] : -1;
+        if (p >= 0) {
+          int h = (int)(((uint64_t)((uint32_t)p * 0x9E3779B1u) * (uint32_t)HN) >> 32);
+          int probe = 0;
+          for (; probe < HN; ++probe) {  // HN >= W >= distinct positions: always ends on a break
+            const int old = atomicCAS(&hpos[h], -1, p);
+            if (old == -1 || old == p) break;
+            if (++h == HN) h = 0;
+          }
+          if (probe < HN) {
+            atomicMin(&hfirst[h], j);
+            atomicMax(&hcur[h], (tk << 16) | (65535 - j));
+            hs[c] = h;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < kSelChunksMax; ++c) {
+        const int j = tk * a.tok_k + tid + c * kMetaThreads;
+        if (hs[c] >= 0 && hcur[hs[c]] != ((tk << 16) | (65535 - j))) {
+          sel_s[j] = -1;
+          errbits |= HISPARSE_ERR_DUP;
+          hs[c] = -1;
+        }
+      }
+      __syncthreads();  // the token's checks read hcur before the next token raises it
+#pragma unroll
+      for (int c = 0; c < kSelChunksMax; ++c) {
+        const int j = tk * a.tok_k + tid + c * kMetaThreads;
+        if (hs[c] >= 0 && hfirst[hs[c]] != j) sel_s[j] = -2 - hfirst[hs[c]];
+      }
+    }
+    __syncthreads();  // the key region is free again
   } else if (!fast) {
-    // Repeated positions: sort (position, index); the earliest index of
-    // each position is the one resolved.  A later entry in the same
-    // verify token's list as the entry before it is an error (padding); an
-    // entry of a later token shares the row of the earliest entry, which it
-    // names as sel = -2 - index (padding to the classification below).
+    // Repeated positions, many tokens: sort (position, index), with the
+    // rules above.
     for (int i = tid; i < KP; i += kMetaThreads) {
       const int p = i < K ? sel_s[i] : -1;
       key_s[i] = p >= 0 ? (((unsigned long long)(uint32_t)p << 32) | (uint32_t)i) : ~0ull;
