@@ -1056,6 +1056,8 @@ hipError_t static_scratch_address(int device, float** out) {
 
 int head_group(int num_heads) { return num_heads % 64 == 0 ? 64 : (num_heads % 32 == 0 ? 32 : 16); }
 
+int layer_workgroups(int num_requests, int num_heads) { return num_requests * (num_heads / head_group(num_heads)); }
+
 // Key splits per (layer, query set, head group): enough workgroups to fill
 // the 256 CUs, but at least two tiles each, since a workgroup's fixed costs
 // (row ids, Q, the loader's first tiles, the partial write) outweigh a

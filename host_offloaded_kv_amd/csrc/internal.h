@@ -209,6 +209,7 @@ struct hisparse_pool {
   int32_t row_bytes = hs::kRowBytes;    // bytes per KV row (1152 bf16, 576 FP8)
   size_t resolve_lds = 0;
   int max_lds = 0;                      // LDS bytes per workgroup the device allows
+  int num_cus = 0;                      // compute units of the device
   int32_t policy = HISPARSE_POLICY_LRU;
   uint64_t policy_seed = 0;
   int32_t T = 1;                        // verify tokens per request per step
@@ -274,6 +275,8 @@ int decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
 // Key splits of a decode that fetches the rows it fills (at most
 // decode_splits, so the workspace's partials cover it).
 int fetch_decode_splits(int n_layers, int num_requests, int num_heads, int top_k);
+// (query set, head group) workgroups of one layer's unsplit decode.
+int layer_workgroups(int num_requests, int num_heads);
 // A layer decoded resident rows first: `before` key splits for the part
 // beside the fetches; after the fetch either one launch without key splits
 // that also merges the first part's partials (*after = 0), or `after` key

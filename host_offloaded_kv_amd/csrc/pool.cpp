@@ -321,6 +321,11 @@ hisparse_status hisparse_create_pool(const hisparse_config* cfg, void* d_workspa
     return hip_fail(e, "hipDeviceGetAttribute");
   }
   p->max_lds = max_lds;
+  e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
   if ((size_t)max_lds < p->resolve_lds) {
     set_error("resolve needs " + std::to_string(p->resolve_lds) + " bytes of LDS, device allows " +
               std::to_string(max_lds));
@@ -753,13 +758,20 @@ hisparse_status enqueue_step_prefetch(hisparse_pool* p, const int32_t* d_step, c
 // fetches and beside its decodes (hisparse_step_prefetch).
 //
 // The prefetch is enqueued on the side stream right after the last group's
-// own fetches and before that group's decodes.  It writes only the hot rows
-// of slots this step did not touch and its own miss lists, so it races with
-// nothing the step reads.  Enqueued in that order, a captured graph keeps
-// the prefetch on the fetches' chain (one queue) and the decodes on their
-// own: enqueued after the decodes, the prefetch became a third chain that a
-// graph launch queued ahead of the decodes, serialising them behind its
-// fetch.
+// own fetches (with the fetch in the decode: its metadata kernel) and before
+// that group's decodes.  It writes only the hot rows of slots this step did
+// not touch and its own miss lists, so it races with nothing the step reads.
+// Enqueued in that order, a captured graph keeps the prefetch on the
+// fetches' chain (one queue) and the decodes on their own: enqueued after
+// the decodes, the prefetch became a third chain that a graph launch queued
+// ahead of the decodes, serialising them behind its fetch.
+// A step with a prefetch decodes its last group in unsplit launches that
+// leave the prefetch's copy kPrefetchCopyCUs compute units (its 32
+// workgroups fill the host link), where a layer has at least
+// kPrefetchLayerWorkgroups (query set, head group) workgroups.
+constexpr int kPrefetchLayerWorkgroups = 32;
+constexpr int kPrefetchCopyCUs = 32;
+
 hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk,
                           const int32_t* d_next, const uint16_t* d_q, float scale, int32_t* d_rows,
                           int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts, void* stream) {
@@ -789,9 +801,10 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
   // The fetch in the decode: one decode launch over a group's layers reads
   // the rows the step fills straight from the host pool (and writes them
   // to their hot rows), so the step is the metadata kernel and that launch,
-  // on `stream` alone.  No tail chunks; a step with a prefetch keeps the
-  // separate fetches, behind which the prefetch queues.
-  const bool fused = C == 1 && !pf && p->fetch_in_decode >= 0;
+  // on `stream` alone (no tail chunks).  A prefetch of the next selections
+  // forks onto the side stream after the last group's metadata kernel and
+  // runs beside that group's decode.
+  const bool fused = C == 1 && p->fetch_in_decode >= 0;
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
@@ -799,8 +812,30 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
       hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
                                            d_counts + (size_t)l0 * R * 3, s);
       if (st) return st;
+      if (pf && g + 1 == c.num_layers / G) {
+        if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
+          return hip_fail(e, (f + ": fork").c_str());
+        if ((st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, fs))) return st;
+      }
       PartSpec ps;
       ps.fetch_sel = d_topk + (size_t)g * R * W;
+      const int lw = layer_workgroups((int)(R * T), (int)H);
+      if (pf && g + 1 == c.num_layers / G && G > 1 && lw >= kPrefetchLayerWorkgroups &&
+          G * lw > p->num_cus - kPrefetchCopyCUs) {
+        // Beside a prefetch, the group's layers are decoded in unsplit
+        // launches of as many layers as leave the prefetch's copy its CUs:
+        // a launch over the whole group would hold every CU, and the copy,
+        // which needs few, would wait for it.
+        const int per = std::max(1, (p->num_cus - kPrefetchCopyCUs) / lw);
+        for (int i = 0; i < G; i += per) {
+          const int n = std::min(per, G - i);
+          const size_t pr = (size_t)(l0 + i) * R * T;
+          if ((st = enqueue_decode(p, l0 + i, n, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                                   d_out + pr * H * kVDim, d_lse + pr * H, s, 1, false, ps)))
+            return st;
+        }
+        continue;
+      }
       const size_t pr = (size_t)l0 * R * T;  // first query set of the group
       st = enqueue_decode(p, l0, G, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
                           d_out + pr * H * kVDim, d_lse + pr * H, s, fetch_decode_splits(G, (int)(R * T), (int)H, (int)K),

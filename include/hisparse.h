@@ -325,9 +325,10 @@ hisparse_status hisparse_prefetch(hisparse_pool* pool, int32_t layer_begin, int3
 
 /* hisparse_step, followed by the prefetch of d_topk_next ([L/g][R][T*K],
  * the predicted selections of the next step) into every layer: the prefetch
- * runs on the pool's side stream after all of this step's miss fetches and
- * beside its decodes, and `stream` waits for it before the call's work
- * ends (graph-capturable like hisparse_step).  d_pf_counts: device int32
+ * runs on the pool's side stream after all of this step's metadata kernels
+ * (with separate fetches: after its miss fetches) and beside the last
+ * group's decode, and `stream` waits for it before the call's work ends
+ * (graph-capturable like hisparse_step).  d_pf_counts: device int32
  * [L][R][4] out, or NULL (as hisparse_prefetch's d_counts).  Row ids,
  * counts, O and lse of this step are those of hisparse_step.
  * Errors: EINVAL. */
@@ -420,15 +421,15 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *     split and combine_splits merges them.  1: always; -1: never (one
  *     launch after the fetch); 0 (default): where the merging launch
  *     applies, i.e. with at least 32 such workgroups;
- *   fetch_in_decode: 0 or 1 (default): with one tail chunk and no
- *     prefetch, hisparse_step has no separate miss fetch: one decode launch
- *     per index-share group reads the rows the step fills straight from the
- *     pinned host pool into its tiles (the workgroups of head group 0 also
- *     write them to their hot rows; with several verify tokens an entry
- *     that shares a filled row with an earlier token's entry reads it from
- *     the host pool too), so the step is the metadata kernel and that launch
- *     on `stream`; -1: separate fetches (the layer pipeline above), as a
- *     step with a prefetch always uses.
+ *   fetch_in_decode: 0 or 1 (default): with one tail chunk,
+ *     hisparse_step and hisparse_step_prefetch have no separate miss fetch:
+ *     one decode launch per index-share group reads the rows the step fills
+ *     straight from the pinned host pool into its tiles (the workgroups of
+ *     head group 0 also write them to their hot rows; with several verify
+ *     tokens an entry that shares a filled row with an earlier token's
+ *     entry reads it from the host pool too), so the step is the metadata
+ *     kernel and that launch on `stream`; -1: separate fetches (the layer
+ *     pipeline above).
  * Results do not depend on these settings, except the rounding of O and
  * lse of the chunked or two-part layer.  Errors: EINVAL. */
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,

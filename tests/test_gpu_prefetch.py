@@ -144,15 +144,17 @@ def _grouped():
 
 
 @pytest.mark.parametrize("shape,two_part", [("grouped", 0), ("grouped", 1), ("single_layer", 0), ("single_layer", 1),
-                                            ("full_size", 1)])
+                                            ("full_size", 0), ("full_size", 1)])
 def test_step_prefetch_matches_oracle(shape, two_part):
     """hisparse_step_prefetch with the exact next selection: the step's own
     outputs as in the oracle, the in-step prefetch as oracle.prefetch, and
-    (room permitting) no miss in the next step.  two_part = 1 decodes each
-    group's last layer in two parts (resident_first) where the default would
-    not (small shapes: both parts split, merged by combine_splits); the full
-    size r32_ctx128k_l4 case (requests 0 and 17 checked) merges in the
-    second part."""
+    (room permitting) no miss in the next step.  two_part = 0 runs the
+    default pipeline (the decode reads the filled rows from the host pool,
+    the prefetch beside it); two_part = 1 runs separate fetches and decodes
+    each group's last layer in two parts (resident_first) where that
+    pipeline's default would not (small shapes: both parts split, merged by
+    combine_splits); the full size r32_ctx128k_l4 case (requests 0 and 17
+    checked) merges in the second part."""
     import torch
 
     w = {"grouped": _grouped, "single_layer": lambda: named_workload("r8_ctx32k"),
@@ -161,7 +163,7 @@ def test_step_prefetch_matches_oracle(shape, two_part):
     tr = w.trace(steps + 1)
     hs = make_pool(w)
     if two_part:
-        hs.set_pipeline(resident_first=1)
+        hs.set_pipeline(resident_first=1, fetch_in_decode=-1)
     buf = _Buffers(w, hs.device)
     reqs = list(range(w.num_requests)) if shape != "full_size" else [0, 17]
     dec = OracleDecoder(w, requests=reqs)
@@ -190,14 +192,16 @@ def test_step_prefetch_matches_oracle(shape, two_part):
     hs.close()
 
 
-def test_step_prefetch_full_size_exact_path():
+@pytest.mark.parametrize("fetch_in_decode", [1, -1], ids=["fetch_in_decode", "separate_fetches"])
+def test_step_prefetch_full_size_exact_path(fetch_in_decode):
     """r32_ctx128k_l4 with the exact next selection prefetched in every step:
     from step 1 on no miss, and row ids and LRU state bit-identical to the
     plain step path (the same victims, fetched one step earlier); O and lse
-    too, since the decode sees the same rows.  Both runs use separate
-    fetches and decode each group's last layer in one launch (the step with
-    a prefetch always fetches separately; decoded resident rows first, the
-    last layer's keys would be split by hit or miss, which the prefetch
+    too, since the decode sees the same rows in the same order: whether a
+    row is read from the host pool (a fill) or from its hot row (a hit once
+    prefetched) changes no arithmetic.  With separate fetches both runs
+    decode each group's last layer in one launch (decoded resident rows
+    first, its keys would be split by hit or miss, which the prefetch
     changes, and the results would then agree to rounding only)."""
     import torch
 
@@ -205,7 +209,7 @@ def test_step_prefetch_full_size_exact_path():
     steps = 5
     tr = w.trace(steps + 1)
     hs = make_pool(w)
-    hs.set_pipeline(resident_first=-1, fetch_in_decode=-1)
+    hs.set_pipeline(resident_first=-1, fetch_in_decode=fetch_in_decode)
     buf = _Buffers(w, hs.device)
     plain = []
     for t in range(steps):
