@@ -63,6 +63,7 @@ __device__ __forceinline__ void wait_vmem_and_sync() {
 constexpr int kMetaThreads = 1024;  // 16 wavefronts per (request, layer)
 constexpr int kMetaWaves = kMetaThreads / 64;
 constexpr int kSelChunksMax = kMaxTopK / kMetaThreads;  // entries per thread of a one-token selection
+constexpr int kRankSortMax = 128;  // misses ordered by a rank count up to this many, else by buckets
 constexpr int kHashTokensMax = 8;  // several tokens: repeats found by a hash up to this many tokens, else a sort
 
 // LDS of one metadata workgroup: the selection (W int32), the sort and
@@ -178,6 +179,7 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int cnt_s[2][kMetaWaves];
   __shared__ int red_s[2][kMetaWaves];
+  __shared__ int scan_s[kMetaWaves];
   const int B = a.hot_slots, K = a.top_k, R = a.num_requests;
   const bool one_token = a.tok_k == K;
   const LdsMap M = lds_map(K, B, a.policy == HISPARSE_POLICY_RANDOM, one_token);
@@ -288,7 +290,12 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
     const int HN = (int)hash_entries(K);
     int* hpos = (int*)(smem + M.aux);
     int* hidx = hpos + HN;
-    for (int i = tid; i < HN; i += kMetaThreads) {
+    // cleared 16 bytes at a time (HN is a power of two, the region starts on 16 bytes)
+    for (int i = tid; i < HN / 4; i += kMetaThreads) {
+      ((int4*)hpos)[i] = make_int4(-1, -1, -1, -1);
+      ((int4*)hidx)[i] = make_int4(INT_MAX, INT_MAX, INT_MAX, INT_MAX);
+    }
+    for (int i = HN / 4 * 4 + tid; i < HN; i += kMetaThreads) {
       hpos[i] = -1;
       hidx[i] = INT_MAX;
     }
@@ -497,23 +504,77 @@ __global__ __launch_bounds__(kMetaThreads) void resolve_meta(ResolveArgs a) {
   if (fill_mask && !one_token)
     for (int i = tid; i < (K + 63) / 64; i += kMetaThreads) a.fill_mask[cpair * ((K + 63) / 64) + i] = fm_s[i];
 
-  if (!fast && m > 1 && m <= kMetaThreads) {
-    // Ascending position order of the misses: thread i counts the keys
-    // below miss i (the keys are distinct; every thread reads the same key
-    // at a time, an LDS broadcast), then writes it at that rank.
+  if (!fast && m > 1 && m <= kRankSortMax) {
+    // Ascending position order of a few misses (their positions are
+    // distinct: a repeat is padding or a copy by now): thread i counts the
+    // misses at smaller positions than miss i (every thread reads the same
+    // key at a time, an LDS broadcast), then writes it at that rank.
     const unsigned long long x = tid < m ? key_s[tid] : 0ull;
+    const uint32_t xp = (uint32_t)(x >> 32);
     int rank = 0;
     if (tid < m)
-      for (int i = 0; i < m; ++i) rank += key_s[i] < x ? 1 : 0;
+      for (int i = 0; i < m; ++i) rank += (uint32_t)(key_s[i] >> 32) < xp ? 1 : 0;
     __syncthreads();
     if (tid < m) key_s[rank] = x;
     __syncthreads();
   } else if (!fast && m > 1) {
-    // more misses than threads: bitonic sort
-    const int mp = next_pow2(m);
-    for (int i = m + tid; i < mp; i += kMetaThreads) key_s[i] = ~0ull;
+    // More misses: ascending position order by buckets of positions:
+    // bucket b holds positions [b ctx / NB, (b + 1) ctx / NB).
+    // Count the misses per bucket, take the exclusive prefix of the counts,
+    // scatter the misses in bucket order, and place each miss by its rank
+    // within its bucket (each thread counts the smaller positions there).
+    const int NB = min(kMetaThreads, K / 2);
+    int* bcnt = vic_s;  // the victims' region, unused until the victims are chosen
+    int* bbase = vic_s + NB;
+    for (int i = tid; i < NB; i += kMetaThreads) bcnt[i] = 0;
     __syncthreads();
-    bitonic_sort(key_s, mp, tid);
+    unsigned long long xk[SC];
+    int bk[SC], lo[SC];
+#pragma unroll
+    for (int c = 0; c < SC; ++c) {
+      const int i = tid + c * kMetaThreads;
+      xk[c] = 0ull;
+      bk[c] = 0;
+      lo[c] = -1;
+      if (i < m) {
+        xk[c] = key_s[i];
+        bk[c] = (int)(((uint64_t)(uint32_t)(xk[c] >> 32) * (uint32_t)NB) / (uint32_t)ctx);
+        lo[c] = atomicAdd(&bcnt[bk[c]], 1);
+      }
+    }
+    __syncthreads();
+    const int v = tid < NB ? bcnt[tid] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) scan_s[wid] = incl;
+    __syncthreads();
+    int wb = 0;
+    for (int w2 = 0; w2 < wid; ++w2) wb += scan_s[w2];
+    if (tid < NB) bbase[tid] = wb + incl - v;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SC; ++c)
+      if (lo[c] >= 0) key_s[bbase[bk[c]] + lo[c]] = xk[c];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SC; ++c) {
+      if (lo[c] >= 0) {
+        const int s0 = bbase[bk[c]], n = bcnt[bk[c]];
+        const uint32_t xp = (uint32_t)(xk[c] >> 32);
+        int rk = 0;
+        for (int q = 0; q < n; ++q) rk += (uint32_t)(key_s[s0 + q] >> 32) < xp ? 1 : 0;
+        lo[c] = s0 + rk;  // from here on: the miss's place
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SC; ++c)
+      if (lo[c] >= 0) key_s[lo[c]] = xk[c];
+    __syncthreads();
   }
 
   int unpinned = 0;  // slots a fill may take
