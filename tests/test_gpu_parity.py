@@ -183,6 +183,24 @@ def test_r32_ctx128k_l4():
     hs.close()
 
 
+def test_indexer_order_misses_in_few_position_buckets():
+    """Misses concentrated in a narrow range of a 1M-token context, in
+    indexer order: each step's selection of request 0 is a contiguous block
+    of 2048 positions (shuffled) that moves on by 1024 per step, so about
+    1024 misses per step fall into one or two of the metadata kernel's
+    position buckets (1024 positions wide here), whose rank counts are then
+    as long as the misses; request 1 draws the usual trace.  Bit-exact
+    against the oracle."""
+    w = make_workload("few_buckets", 61, 2, 1, 1, [1 << 20, 300000], 16, 2048, 4096, 5, 0.7, 0.8, "none")
+    tr = w.trace(w.steps).copy()
+    rng = np.random.default_rng(61)
+    for t in range(tr.shape[0]):
+        tr[t, 0, 0] = rng.permutation(np.arange(500000 + 1024 * t, 500000 + 1024 * t + 2048, dtype=np.int32))
+        tr[t, 0, 1] = rng.permutation(tr[t, 0, 1])
+    hs, _, _ = run_and_compare(w, bytes_pairs=[(0, 0), (0, 1)], label="misses in few position buckets", trace=tr)
+    hs.close()
+
+
 def test_r8_ctx32k_indexer_order():
     """The r8_ctx32k workload with every selection in a shuffled (indexer)
     order instead of ascending: the metadata kernel's unsorted path at full
