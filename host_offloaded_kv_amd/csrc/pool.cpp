@@ -772,6 +772,50 @@ hisparse_status enqueue_step_prefetch(hisparse_pool* p, const int32_t* d_step, c
 constexpr int kPrefetchLayerWorkgroups = 32;
 constexpr int kPrefetchCopyCUs = 32;
 
+// One index-share group of a step with the fetch in the decode: the
+// metadata kernel, then one decode launch over the group's layers that
+// reads the rows the step fills straight from the host pool (and writes
+// them to their hot rows), on `s` alone.  With a prefetch (d_next), the
+// last group forks it onto the side stream after its metadata kernel, and
+// decodes in unsplit launches of as many layers as leave the prefetch's
+// copy its CUs: a launch over the whole group would hold every CU, and the
+// copy, which needs few, would wait for it.
+hisparse_status fetching_group(hisparse_pool* p, int g, const int32_t* d_step, const int32_t* d_topk,
+                               const int32_t* d_next, const uint16_t* d_q, float scale, int32_t* d_rows,
+                               int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts, hipStream_t s,
+                               const std::string& f) {
+  const auto& c = p->cfg;
+  const size_t R = c.num_requests, K = c.top_k, H = c.num_heads, T = p->T, W = p->W;
+  const int G = c.index_share, l0 = g * G;
+  const bool last = g + 1 == c.num_layers / G;
+  hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
+                                       d_counts + (size_t)l0 * R * 3, s);
+  if (st) return st;
+  if (d_next && last) {
+    hipError_t e;
+    if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess ||
+        (e = hipStreamWaitEvent(p->fetch_stream, p->ev_meta, 0)) != hipSuccess)
+      return hip_fail(e, (f + ": fork").c_str());
+    if ((st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, p->fetch_stream))) return st;
+  }
+  PartSpec ps;
+  ps.fetch_sel = d_topk + (size_t)g * R * W;
+  const int lw = layer_workgroups((int)(R * T), (int)H);
+  int per = G, splits = fetch_decode_splits(G, (int)(R * T), (int)H, (int)K);
+  if (d_next && last && G > 1 && lw >= kPrefetchLayerWorkgroups && G * lw > p->num_cus - kPrefetchCopyCUs) {
+    per = std::max(1, (p->num_cus - kPrefetchCopyCUs) / lw);
+    splits = 1;
+  }
+  for (int i = 0; i < G; i += per) {
+    const int n = std::min(per, G - i);
+    const size_t pr = (size_t)(l0 + i) * R * T;  // first query set of the launch
+    if ((st = enqueue_decode(p, l0 + i, n, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
+                             d_out + pr * H * kVDim, d_lse + pr * H, s, splits, false, ps)))
+      return st;
+  }
+  return HISPARSE_OK;
+}
+
 hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_step, const int32_t* d_topk,
                           const int32_t* d_next, const uint16_t* d_q, float scale, int32_t* d_rows,
                           int32_t* d_counts, float* d_out, float* d_lse, int32_t* d_pf_counts, void* stream) {
@@ -798,48 +842,15 @@ hisparse_status step_impl(const char* fn, hisparse_pool* p, const int32_t* d_ste
                   (p->resident_first > 0 || (p->resident_first == 0 && resident_first_pays((int)R, (int)H)));
   int rf_before = 1, rf_after = 0;
   if (rf) resident_first_splits((int)R, (int)H, (int)K, &rf_before, &rf_after);
-  // The fetch in the decode: one decode launch over a group's layers reads
-  // the rows the step fills straight from the host pool (and writes them
-  // to their hot rows), so the step is the metadata kernel and that launch,
-  // on `stream` alone (no tail chunks).  A prefetch of the next selections
-  // forks onto the side stream after the last group's metadata kernel and
-  // runs beside that group's decode.
+  // The fetch in the decode (fetching_group) takes every step without
+  // tail chunks unless hisparse_set_pipeline switched it off.
   const bool fused = C == 1 && p->fetch_in_decode >= 0;
   hipError_t e;
   for (int g = 0; g < c.num_layers / G; ++g) {
     const int l0 = g * G;
     if (fused) {
-      hisparse_status st = enqueue_resolve(p, l0, G, d_step, d_topk + (size_t)g * R * W, d_rows + (size_t)l0 * R * W,
-                                           d_counts + (size_t)l0 * R * 3, s);
-      if (st) return st;
-      if (pf && g + 1 == c.num_layers / G) {
-        if ((e = hipEventRecord(p->ev_meta, s)) != hipSuccess || (e = hipStreamWaitEvent(fs, p->ev_meta, 0)) != hipSuccess)
-          return hip_fail(e, (f + ": fork").c_str());
-        if ((st = enqueue_step_prefetch(p, d_step, d_next, d_pf_counts, fs))) return st;
-      }
-      PartSpec ps;
-      ps.fetch_sel = d_topk + (size_t)g * R * W;
-      const int lw = layer_workgroups((int)(R * T), (int)H);
-      if (pf && g + 1 == c.num_layers / G && G > 1 && lw >= kPrefetchLayerWorkgroups &&
-          G * lw > p->num_cus - kPrefetchCopyCUs) {
-        // Beside a prefetch, the group's layers are decoded in unsplit
-        // launches of as many layers as leave the prefetch's copy its CUs:
-        // a launch over the whole group would hold every CU, and the copy,
-        // which needs few, would wait for it.
-        const int per = std::max(1, (p->num_cus - kPrefetchCopyCUs) / lw);
-        for (int i = 0; i < G; i += per) {
-          const int n = std::min(per, G - i);
-          const size_t pr = (size_t)(l0 + i) * R * T;
-          if ((st = enqueue_decode(p, l0 + i, n, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
-                                   d_out + pr * H * kVDim, d_lse + pr * H, s, 1, false, ps)))
-            return st;
-        }
-        continue;
-      }
-      const size_t pr = (size_t)l0 * R * T;  // first query set of the group
-      st = enqueue_decode(p, l0, G, (int)(R * T), d_q + pr * H * kLatent, d_rows + pr * K, scale,
-                          d_out + pr * H * kVDim, d_lse + pr * H, s, fetch_decode_splits(G, (int)(R * T), (int)H, (int)K),
-                          false, ps);
+      hisparse_status st = fetching_group(p, g, d_step, d_topk, d_next, d_q, scale, d_rows, d_counts, d_out, d_lse,
+                                          d_pf_counts, s, f);
       if (st) return st;
       continue;
     }
