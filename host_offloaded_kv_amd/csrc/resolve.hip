@@ -171,7 +171,8 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 //    and write at base + ballot prefix.  The order array is read once into
 //    registers and rewritten at the end.
 //  * The misses are kept as 64-bit keys (position << 32 | entry index), so
-//    the unsorted path sorts them in place.
+//    the unsorted path orders them in place (a rank count, or buckets of
+//    positions).
 // SC / BC: 64-entry chunks of the selection / of the order array per wave
 // (the selection width W is at most 1024 SC, the slot count B at most 1024 BC).
 template <int SC, int BC>
