@@ -103,6 +103,16 @@ def test_verify_small_configs(case, pipeline):
     assert flags == (HISPARSE_ERR_DUP if case == 1 else 0)
 
 
+@pytest.mark.parametrize("pipeline", [1, -1], ids=["fetch_in_decode", "separate_fetches"])
+def test_verify_tokens_off_word_boundaries(pipeline):
+    """K = 50 with 3 tokens: each token's entries start inside a 64-bit word
+    of the fill mask; index sharing over 2 layers, 16 heads, contexts a few
+    times the width, resident tail pages."""
+    w = make_workload("verify_k50", 977, 2, 2, 2, [700, 1300], 16, 50, 200, 6, 0.6, 0.8, "tail", page_size=16)
+    w.num_verify = 3
+    assert _run(w, w.steps, fetch_in_decode=pipeline) == 0
+
+
 def test_verify_mtp1_r8_ctx32k():
     """One speculative token on the 8 x 32K workload: T*K = 4096 = B."""
     w = named_workload("r8_ctx32k")
