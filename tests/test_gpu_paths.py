@@ -155,38 +155,60 @@ def test_overlapped_step_matches_oracle_and_sync_path():
     hs.close()
 
 
-@pytest.mark.parametrize("variant", ["bf16", "fp8_verify2"])
+@pytest.mark.parametrize("variant", ["bf16", "fp8_verify2", "separate_fetches", "prefetch"])
 def test_captured_step_graph_replays(variant):
     """A captured hisparse_step, replayed once per step with fresh inputs
     copied in between, matches eager steps of a second pool bit for bit
-    (bf16 rows, and FP8 rows with two verify tokens per request)."""
+    (bf16 rows; FP8 rows with two verify tokens per request; the pipeline
+    of separate fetches on two streams; hisparse_step_prefetch of the next
+    step's selection, forked onto the side stream and joined)."""
     import torch
 
     w = _grouped_workload()
     if variant == "fp8_verify2":
         w = with_fp8(w)
         w.num_verify = 2
-    tr = w.trace(w.steps)
+    tr = w.trace(w.steps + 1)
+    pipeline = -1 if variant == "separate_fetches" else 1
+    prefetch = variant == "prefetch"
+
+    def run_step(hs, buf, nxt):
+        if prefetch:
+            hs.step_prefetch(buf.d_step, buf.topk, nxt, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse, None)
+        else:
+            hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+
     eager = make_pool(w)
+    eager.set_pipeline(fetch_in_decode=pipeline)
     ebuf = _Buffers(w, eager.device)
-    want = _run_step_path(eager, w, tr, ebuf)
+    enext = torch.empty_like(ebuf.topk)
+    want = []
+    for t in range(w.steps):
+        ebuf.load(w, t, tr[t])
+        enext.copy_(torch.from_numpy(np.ascontiguousarray(tr[t + 1], dtype=np.int32)).reshape(enext.shape))
+        run_step(eager, ebuf, enext)
+        torch.cuda.synchronize(eager.device)
+        want.append(ebuf.snapshot())
     eager.close()
 
     hs = make_pool(w)
+    hs.set_pipeline(fetch_in_decode=pipeline)
     buf = _Buffers(w, hs.device)
+    nxt = torch.empty_like(buf.topk)
     side = torch.cuda.Stream(device=hs.device)
     side.wait_stream(torch.cuda.current_stream(hs.device))
     graph = torch.cuda.CUDAGraph()
     buf.load(w, 0, tr[0])
     torch.cuda.synchronize(hs.device)
     with torch.cuda.graph(graph, stream=side):
-        hs.step(buf.d_step, buf.topk, buf.q, w.scale, buf.rows, buf.counts, buf.out, buf.lse)
+        run_step(hs, buf, nxt)
     torch.cuda.synchronize(hs.device)
     # capture enqueues nothing: the state is still empty
     owner, stamp = hs.export_state(0, 0)
     assert np.all(owner == -1) and np.all(stamp == -1)
     for t in range(w.steps):
         buf.load(w, t, tr[t])
+        nxt.copy_(torch.from_numpy(np.ascontiguousarray(tr[t + 1], dtype=np.int32)).reshape(nxt.shape))
         torch.cuda.synchronize(hs.device)
         graph.replay()
         torch.cuda.synchronize(hs.device)
