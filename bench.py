@@ -400,19 +400,29 @@ def main() -> int:
                 H.hisparse_sparse_mla_decode(hs.pool, l, d_q[t, l].data_ptr(), d_rows[t, l].data_ptr(), w.scale,
                                              d_out[l].data_ptr(), d_lse[l].data_ptr(), stream.cuda_stream)
 
-    def time_steps(fn):
-        """Replays steps 0..n_steps from the empty state; returns ms of the timed ones."""
+    def time_steps(fn, per_step=None):
+        """Replays steps 0..n_steps from the empty state; returns ms of the timed ones.
+        per_step (a dict) receives each step's own time in us: the warm-up steps
+        (step 0 from the empty state, i.e. cold) and the timed ones, from events
+        recorded between the steps on the same stream."""
         hs.reset_state()
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        warm = [ev() for _ in range(args.warmup + 1)]
+        warm[0].record(stream)
         for t in range(args.warmup):
             fn(t)
+            warm[t + 1].record(stream)
         torch.cuda.synchronize(dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for t in range(args.warmup, n_steps):
+        evs = [ev() for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i, t in enumerate(range(args.warmup, n_steps)):
             fn(t)
-        e1.record(stream)
+            evs[i + 1].record(stream)
         torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1)
+        if per_step is not None:
+            per_step["warmup_us"] = [round(warm[i].elapsed_time(warm[i + 1]) * 1e3, 2) for i in range(args.warmup)]
+            per_step["timed_us"] = [round(evs[i].elapsed_time(evs[i + 1]) * 1e3, 2) for i in range(args.steps)]
+        return evs[0].elapsed_time(evs[-1])
 
     # 1) eager steps; every kernel is bracketed by HIP events on its stream
     for t in range(args.warmup):
@@ -442,7 +452,7 @@ def main() -> int:
 
     # 2) the same steps as captured-graph replays (the timed region of the
     #    headline), with the kernel events captured into the timed graphs
-    graph_ms, prof_graph = None, None
+    graph_ms, prof_graph, graph_steps = None, None, {}
     if not args.no_graph:
         log("captured-graph replay of the same steps")
         side = torch.cuda.Stream(device=dev)
@@ -457,7 +467,7 @@ def main() -> int:
             graphs.append(g)
         H.hisparse_profile_enable(hs.pool, False)
         torch.cuda.synchronize(dev)
-        graph_ms = time_steps(lambda t: graphs[t].replay())
+        graph_ms = time_steps(lambda t: graphs[t].replay(), graph_steps)
         try:
             prof_graph = H.hisparse_profile_read(hs.pool)
             if not prof_graph or any(not (ms > 0) for _, ms in prof_graph.values()):
@@ -723,7 +733,13 @@ def main() -> int:
         "timing": {"timed_region": "graph replays" if use_graph else "eager steps",
                    "kernel_times_from": "graph replays" if use_graph else "eager steps",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 2),
-                   "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None},
+                   "graph_replay_us_per_step": round(graph_ms / args.steps * 1e3, 2) if graph_ms else None,
+                   # graph replays from the empty state: step 0 (cold: every entry misses) and the
+                   # median of the timed steps, each from events between the replays
+                   "cold_step0_us": graph_steps["warmup_us"][0] if graph_steps.get("warmup_us") else None,
+                   "median_us_per_step": (round(float(np.median(graph_steps["timed_us"])), 2)
+                                          if graph_steps.get("timed_us") else None),
+                   "graph_replay_us_each_step": graph_steps.get("timed_us")},
         "layer_ahead": {"unit_fetch_workgroups": args.fetch_wg or None, "tail_chunks": args.tail_chunks or None,
                         "resident_first": not args.no_resident_first,
                         "fetch_in_decode": not args.no_fetch_in_decode,
