@@ -617,14 +617,18 @@ constexpr int kLoadSets = 3;
 
 // Where the loader reads the rows of a workgroup's tiles: the layer's KV
 // tensor, or, for rows this step fills when the decode fetches them, the
-// request's host pool rows; the workgroups of head group 0 then also write
-// those rows to their hot rows.
+// request's host pool rows; each such row is also written to its hot row,
+// by one of the head groups that read it: row i of the key range by head
+// group i mod (head groups).  Sharing the writes keeps the head groups of
+// a key range at the same pace, so the later one still finds the host rows
+// in their XCD's L2 (with all the writes in head group 0 it fell behind,
+// and a step of nothing but misses moved every row over the link twice).
 struct RowSource {
   const unsigned char* kv;
   const unsigned char* host;       // the request's host pool rows (fetch in the decode)
   __amdgpu_buffer_rsrc_t hot;      // the request's hot rows
   int64_t hot_base;                // row id of the request's first hot row
-  bool writer;
+  int hg, nhg;                     // this workgroup's head group, and the request's head groups
 };
 
 template <int HG, bool FP8, bool FETCH>
@@ -654,7 +658,7 @@ __device__ __forceinline__ void loader_role(DecodeSmem<HG>& sm, const RowSource&
       const int pr = sm.rowpos[in ? i : 0];
       const int pos = in ? pr : -1;
       x.src = pos >= 0 ? rs.host + (size_t)pos * RB : x.src;
-      x.hoff = pos >= 0 && rs.writer ? (int)((rid - rs.hot_base) * RB) : kNoHotWrite;
+      x.hoff = pos >= 0 && i % rs.nhg == rs.hg ? (int)((rid - rs.hot_base) * RB) : kNoHotWrite;
     }
     return x;
   };
@@ -831,8 +835,8 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
 // per iteration (n_tiles + 1), one between passes, and the final
 // __syncthreads().
 // FETCH: the decode reads the rows this step fills from the host pool (and
-// head group 0 writes them to their hot rows): the miss fetch and the
-// decode in one pass over the rows.
+// the head groups share writing them to their hot rows): the miss fetch and
+// the decode in one pass over the rows.
 template <int HG, bool FP8, bool FETCH>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   __shared__ __align__(16) DecodeSmem<HG> sm;
@@ -873,7 +877,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   rs.kv = kv;
   rs.host = nullptr;
   rs.hot_base = 0;
-  rs.writer = false;
+  rs.hg = hg;
+  rs.nhg = nhg;
   int held = 0;
   int q = 0;             // query set within its layer: token q % tokens of request q / tokens
   size_t mask_bit0 = 0;  // fill-mask bit of this query set's entry 0
@@ -886,7 +891,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
     rs.hot_base = a.resident_rows + (int64_t)r * a.hot_slots;
     rs.hot = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kv) + rs.hot_base * RB, 0,
                                                a.hot_slots * RB, 0x00020000);
-    rs.writer = hg == 0;
   } else {
     rs.hot = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
   }

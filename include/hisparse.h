@@ -424,12 +424,12 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *   fetch_in_decode: 0 or 1 (default): with one tail chunk,
  *     hisparse_step and hisparse_step_prefetch have no separate miss fetch:
  *     one decode launch per index-share group reads the rows the step fills
- *     straight from the pinned host pool into its tiles (the workgroups of
- *     head group 0 also write them to their hot rows; with several verify
- *     tokens an entry that shares a filled row with an earlier token's
- *     entry reads it from the host pool too), so the step is the metadata
- *     kernel and that launch on `stream`; -1: separate fetches (the layer
- *     pipeline above).
+ *     straight from the pinned host pool into its tiles and writes them to
+ *     their hot rows, each row once, the head groups sharing the writes
+ *     (with several verify tokens an entry that shares a filled row with an
+ *     earlier token's entry reads it from the host pool too), so the step
+ *     is the metadata kernel and that launch on `stream`; -1: separate
+ *     fetches (the layer pipeline above).
  * Results do not depend on these settings, except the rounding of O and
  * lse of the chunked or two-part layer.  Errors: EINVAL. */
 hisparse_status hisparse_set_pipeline(hisparse_pool* pool, int32_t group_fetch_workgroups,
