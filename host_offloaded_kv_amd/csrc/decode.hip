@@ -618,11 +618,14 @@ constexpr int kLoadSets = 3;
 // Where the loader reads the rows of a workgroup's tiles: the layer's KV
 // tensor, or, for rows this step fills when the decode fetches them, the
 // request's host pool rows; each such row is also written to its hot row,
-// by one of the head groups that read it: row i of the key range by head
-// group i mod (head groups).  Sharing the writes keeps the head groups of
-// a key range at the same pace, so the later one still finds the host rows
-// in their XCD's L2 (with all the writes in head group 0 it fell behind,
-// and a step of nothing but misses moved every row over the link twice).
+// by one of the head groups that read it (row i of the key range by head
+// group hg when i mod nhg == hg).  Where most rows are filled, sharing the
+// writes keeps the head groups of a key range at the same pace, so the
+// later one still finds the host rows in their XCD's L2: with all the
+// writes in head group 0 it fell behind, and a step of nothing but misses
+// moved every row over the link twice.  Where few are, head group 0 writes
+// them all (sharing measured up to 1% slower per step there, and 1-4% with
+// several verify tokens).
 struct RowSource {
   const unsigned char* kv;
   const unsigned char* host;       // the request's host pool rows (fetch in the decode)
@@ -835,8 +838,8 @@ __device__ __forceinline__ void exact_fallback(const DecodeArgs& a, DecodeSmem<H
 // per iteration (n_tiles + 1), one between passes, and the final
 // __syncthreads().
 // FETCH: the decode reads the rows this step fills from the host pool (and
-// the head groups share writing them to their hot rows): the miss fetch and
-// the decode in one pass over the rows.
+// writes them to their hot rows): the miss fetch and the decode in one pass
+// over the rows.
 template <int HG, bool FP8, bool FETCH>
 __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) {
   __shared__ __align__(16) DecodeSmem<HG> sm;
@@ -877,8 +880,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   rs.kv = kv;
   rs.host = nullptr;
   rs.hot_base = 0;
-  rs.hg = hg;
-  rs.nhg = nhg;
   int held = 0;
   int q = 0;             // query set within its layer: token q % tokens of request q / tokens
   size_t mask_bit0 = 0;  // fill-mask bit of this query set's entry 0
@@ -897,6 +898,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   int n_rows = k1 > k0 ? k1 - k0 : 0;
   if (a.part == 0) {
     const int n_pad = (n_rows + kT - 1) / kT * kT;
+    int nf = 0;  // filled rows this wave saw
     for (int k = tid; k < n_pad; k += kThreads) {
       if constexpr (FETCH) {
         // The row id, its fill-mask word and its position are independent
@@ -915,12 +917,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
         const bool pbad = filled & ((p_in < 0) | (p_in >= held));
         sm.rowid[k] = rid;
         sm.rowpos[k] = (filled & !pbad) ? p_in : -1;
+        nf += __popcll(__ballot(filled & !pbad));
         if (rbad) atomicOr(a.err, HISPARSE_ERR_ROW);
         if (pbad) atomicOr(a.err, HISPARSE_ERR_UNMATERIALIZED);
       } else {
         sm.rowid[k] = load_row_id(a, rows, k0 + k, k1);
       }
     }
+    if (FETCH && lane == 0) sm.cnt[w] = nf;
   } else {
     const uint64_t* mask = a.fill_mask + (size_t)pair * a.mask_words;
     const bool want_filled = a.part == 2;
@@ -947,6 +951,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws(DecodeArgs a, int nhg) 
   }
   const int n_tiles = (n_rows + kT - 1) / kT;
   __syncthreads();
+  if constexpr (FETCH) {
+    // Who writes the filled rows to their hot rows.  With one verify token
+    // and more than half of the key range filled (a step of misses), row i
+    // by head group i mod nhg; otherwise head group 0 writes them all.  The
+    // head groups of a key range count the same rows, so each row is
+    // written once either way.
+    int nfilled = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) nfilled += sm.cnt[i];
+    const bool share = a.tokens == 1 && 2 * nfilled > n_rows;
+    rs.hg = share ? hg : (hg == 0 ? 0 : -1);
+    rs.nhg = share ? nhg : 1;
+  }
 
   const size_t head0 = (size_t)pair * H + hg * HG;
   if (w < 4)

@@ -148,7 +148,7 @@ struct DecodeArgs {
   int32_t head_group;      // heads per workgroup (16, 32 or 64); 0: the default for num_heads
   // Fetch in the decode: the entries this step fills (fill_mask) are read
   // from the host pool and written to their hot rows (rows holds those
-  // rows' ids), each by one of the head groups that read it.
+  // rows' ids) by the head groups that read them.
   int32_t fetch;
   int32_t tokens;              // verify tokens: query set q is token q % tokens of request q / tokens
   const int32_t* sel;          // [R][top_k] positions of each query set (its layers share them)

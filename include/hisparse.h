@@ -425,8 +425,8 @@ hisparse_status hisparse_set_replacement(hisparse_pool* pool, int32_t policy, ui
  *     hisparse_step and hisparse_step_prefetch have no separate miss fetch:
  *     one decode launch per index-share group reads the rows the step fills
  *     straight from the pinned host pool into its tiles and writes them to
- *     their hot rows, each row once, the head groups sharing the writes
- *     (with several verify tokens an entry that shares a filled row with an
+ *     their hot rows (with one verify token the head groups share the
+ *     writes; with several, an entry that shares a filled row with an
  *     earlier token's entry reads it from the host pool too), so the step
  *     is the metadata kernel and that launch on `stream`; -1: separate
  *     fetches (the layer pipeline above).
